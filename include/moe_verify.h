@@ -1,0 +1,190 @@
+/*
+ * moe_verify.h — C ABI of the MoE expert operation inside a speculative-decoding
+ * verification pass, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one MoE layer, one verify pass of n drafted tokens):
+ *   1. route:   each token's K largest router logits and their softmax gates
+ *               ("Making Every Verified Token Count: Adaptive Verification for
+ *               MoE Speculative Decoding", Sec. 2.2, Eq. (4));
+ *   2. union:   the distinct experts over all n*K token-slots, with the slots
+ *               grouped by expert ("Less Experts, Faster Decoding", Sec. 3,
+ *               Eq. (1); adaptive-verification page, Eq. (5));
+ *   3. experts: SwiGLU y = (silu(x W_gate) * (x W_up)) W_down for every slot,
+ *               either deduplicating (each union expert streamed from HBM once
+ *               per pass) or per-slot (each expert read once per token-slot)
+ *               ("Speculative Decoding for Mixture-of-Experts Models: Expert
+ *               Bytes, Kernel Bandwidth and the Best Draft Length", abstract and
+ *               Table 5 / Table 6);
+ *   4. combine: gate-weighted sum of the K slot outputs plus the shared experts
+ *               (adaptive-verification page, Sec. 2.2).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are device pointers; the caller allocates and
+ *     owns all memory.  The library allocates nothing and keeps no state
+ *     between calls; calls on different streams with disjoint buffers may run
+ *     concurrently.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Outputs are valid once the stream has reached the call.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns an error code and enqueues nothing.
+ *   - Faults only the device can see (an expert id outside [0, E) in ids given
+ *     by the caller) are recorded: moe_build_union writes U = -1, and the FFN
+ *     entry points set a bit in the error word at the start of their
+ *     workspace, which moe_get_error reads back.  Outputs of a call that
+ *     recorded a fault are unspecified.
+ *   - Token-slot s = t*K + k names the k-th expert of token t.
+ *
+ * Storage layouts (row-major, one row per output feature, as in a Linear
+ * weight):
+ *   x         [n][d]          f32 or bf16
+ *   w_gate    [E][f][d]       row j holds column j of the d x f matrix W_gate
+ *   w_up      [E][f][d]
+ *   w_down    [E][d][f]       row c holds column c of the f x d matrix W_down
+ *   fp8 scales (w_dtype = MOE_FP8_E4M3, OCP E4M3FN codes): one fp32 per
+ *             128 x 128 block of each stored matrix, indexed
+ *             [E][rows/128][cols/128]; weight = decode(code) * scale.
+ *   shared experts use the same layouts with S in place of E.
+ * Supported (w_dtype, x_dtype): (F32, F32), (BF16, BF16), (FP8_E4M3, BF16).
+ * Limits: 1 <= n <= 32, 1 <= K <= 8, K <= E <= 256, 0 <= S <= 4;
+ *         d and f multiples of 8 (bf16), 4 (f32) or 128 (fp8), at most 65536.
+ * Every device pointer must be 16-byte aligned; workspaces 256-byte aligned.
+ */
+#ifndef MOE_VERIFY_H
+#define MOE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* null/misaligned pointer or size out of range */
+  MOE_ERR_UNSUPPORTED = 2,  /* dtype combination or shape not supported */
+  MOE_ERR_WORKSPACE = 3,    /* workspace too small or misaligned */
+  MOE_ERR_HIP = 4,          /* the HIP runtime refused a launch or copy */
+  MOE_ERR_BAD_IDS = 5,      /* (device) an expert id outside [0, E) was seen */
+  MOE_ERR_TIMEOUT = 6       /* (device) a bounded wait gave up */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_MODE_DEDUP = 0, MOE_MODE_PERSLOT = 1 } moe_mode;
+
+/* Layer geometry: routed experts E, experts per token K, hidden d, expert
+ * intermediate f, shared experts S, storage types of weights and tokens. */
+typedef struct {
+  int32_t E, K, d, f, S;
+  int32_t w_dtype, x_dtype; /* moe_dtype */
+} moe_shape;
+
+/* Expert weights (device).  s_* / sh_s_* are read only for fp8 weights;
+ * sh_* are read only when S > 0. */
+typedef struct {
+  const void *w_gate, *w_up, *w_down;
+  const float *s_gate, *s_up, *s_down;
+  const void *sh_gate, *sh_up, *sh_down;
+  const float *sh_s_gate, *sh_s_up, *sh_s_down;
+} moe_weights;
+
+/* Router top-K (adaptive-verification page, Sec. 2.2, Eq. (4)).
+ *   logits (device) f32 [n][E]
+ *   ids    (device) int32 [n][K]: the K experts with the largest logits, in
+ *          descending-logit order; equal logits go to the lower id, NaN ranks
+ *          below every number, -0.0 equals +0.0.
+ *   gates  (device) f32 [n][K]: softmax over the K selected logits.
+ * Errors: MOE_ERR_ARG for n, E or K out of range or null pointers. */
+moe_status moe_route_topk(const float* logits, int32_t n, int32_t E, int32_t K,
+                          int32_t* ids, float* gates, moe_stream_t stream);
+
+/* Expert union of a verify pass ("Less Experts, Faster Decoding", Sec. 3,
+ * Eq. (1)) and the slots grouped by expert (the expert-bytes page, Table 6:
+ * rows sorted by expert before the tiled product).  cap = min(n*K, E).
+ *   ids        (device) int32 [n*K]
+ *   U          (device) int32 [1]: distinct ids, or -1 if an id is outside [0, E)
+ *   union_ids  (device) int32 [cap]: ascending distinct ids; -1 beyond U
+ *   offsets    (device) int32 [cap+1]: slots of union_ids[u] are
+ *              perm[offsets[u] .. offsets[u+1]); entries from U on equal n*K
+ *   perm       (device) int32 [n*K]: slots ordered by (id, slot)
+ *   slot_rank  (device) int32 [n*K]: position of ids[s] in union_ids
+ * Bit-exact and deterministic.  Errors: MOE_ERR_ARG. */
+moe_status moe_build_union(const int32_t* ids, int32_t n, int32_t K, int32_t E,
+                           int32_t* U, int32_t* union_ids, int32_t* offsets,
+                           int32_t* perm, int32_t* slot_rank, moe_stream_t stream);
+
+/* Deduplicating expert FFN: each expert of the union (and each shared expert)
+ * is streamed from HBM once and applied to every slot routed to it (the
+ * expert-bytes page, abstract).  The union arrays are those of
+ * moe_build_union for the same ids.
+ *   x         (device) [n][d] in shape->x_dtype
+ *   y_slots   (device) f32 [n][K][d]: SwiGLU output of slot (t, k)
+ *   y_shared  (device) f32 [n][S][d] (may be NULL when S == 0)
+ *   bytes     (device) uint64 [2] or NULL: [0] = (U + S) * b, the bytes this
+ *             call streams; [1] = n * (K + S) * b, what per-slot requests;
+ *             b = bytes of one expert (3*d*f*elem, plus fp8 scales)
+ *   ws        (device) workspace of at least moe_workspace_size(shape, n, DEDUP)
+ *             bytes, zero-filled before its first use (moe_workspace_init).
+ * Errors: MOE_ERR_ARG / _UNSUPPORTED / _WORKSPACE on the host; a device-side
+ * U < 0 records MOE_ERR_BAD_IDS in the workspace. */
+moe_status moe_expert_ffn_dedup(const moe_shape* shape, const moe_weights* w,
+                                const void* x, int32_t n, const int32_t* U,
+                                const int32_t* union_ids, const int32_t* offsets,
+                                const int32_t* perm, float* y_slots, float* y_shared,
+                                uint64_t* bytes, void* ws, size_t ws_bytes,
+                                moe_stream_t stream);
+
+/* Per-slot expert FFN: the expert of every slot (t, k), and every shared
+ * expert for every token, is read once for that slot (the expert-bytes page,
+ * abstract; Table 5, one grid slice per token-slot pair).  Same outputs as the
+ * deduplicating call.
+ *   ids    (device) int32 [n][K]; a slot with an id outside [0, E) gets a zero
+ *          output row and records MOE_ERR_BAD_IDS in the workspace.
+ *   bytes  (device) uint64 [2] or NULL: both entries n * (K + S) * b. */
+moe_status moe_expert_ffn_perslot(const moe_shape* shape, const moe_weights* w,
+                                  const void* x, int32_t n, const int32_t* ids,
+                                  float* y_slots, float* y_shared, uint64_t* bytes,
+                                  void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Combine (adaptive-verification page, Sec. 2.2: the layer output is the
+ * weighted sum of the selected experts):
+ *   out[t] = sum_{k ascending} gates[t][k] * y_slots[t][k] + sum_s y_shared[t][s]
+ * out (device) [n][d] of out_dtype (MOE_F32 or MOE_BF16, round to nearest even).
+ * y_shared may be NULL when S == 0.  Errors: MOE_ERR_ARG / _UNSUPPORTED. */
+moe_status moe_combine(const float* y_slots, const float* gates, const float* y_shared,
+                       int32_t n, int32_t K, int32_t S, int32_t d, void* out,
+                       int32_t out_dtype, moe_stream_t stream);
+
+/* Bytes of workspace the FFN calls need for passes of up to n_max tokens
+ * (0 for an invalid shape). */
+size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode);
+
+/* Zero-fill a workspace on `stream` (with a kernel, never a memset node). */
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Host-only: b = bytes of one expert; union = (U + S) * b, requested =
+ * n * (K + S) * b (the expert-bytes page, Fig. 2 and Table 1).  Either output
+ * pointer (host) may be NULL.  Errors: MOE_ERR_ARG / _UNSUPPORTED. */
+moe_status moe_byte_counts(const moe_shape* shape, int32_t n, int32_t U,
+                           uint64_t* union_bytes, uint64_t* requested_bytes);
+
+/* Synchronizes `stream`, then returns and clears the device error word kept
+ * at the start of `ws`: MOE_OK, MOE_ERR_BAD_IDS or MOE_ERR_TIMEOUT. */
+moe_status moe_get_error(void* ws, moe_stream_t stream);
+
+/* Diagnostic: decode `count` E4M3FN codes (device) to f32 (device) with the
+ * same conversion the fp8 FFN kernels use. */
+moe_status moe_decode_fp8(const uint8_t* codes, float* out, int64_t count,
+                          moe_stream_t stream);
+
+const char* moe_status_str(int32_t status);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_VERIFY_H */

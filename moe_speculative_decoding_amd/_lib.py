@@ -1,0 +1,169 @@
+"""ctypes binding of ``libmoe_verify.so`` — argument marshalling only.
+
+Every function here has the name and the parameter order of its C entry
+point in ``include/moe_verify.h``; device buffers are passed as torch tensors
+(their ``data_ptr()``) or raw integer addresses, and the stream defaults to
+torch's current stream.  A non-OK status raises ``MoeError``.  Nothing is
+computed in Python, and there is no fallback: without the built library,
+importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_verify.so")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, 1, 2, 3
+MOE_ERR_HIP, MOE_ERR_BAD_IDS, MOE_ERR_TIMEOUT = 4, 5, 6
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_MODE_DEDUP, MOE_MODE_PERSLOT = 0, 1
+
+DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
+
+
+class moe_shape(C.Structure):
+    _fields_ = [("E", C.c_int32), ("K", C.c_int32), ("d", C.c_int32), ("f", C.c_int32),
+                ("S", C.c_int32), ("w_dtype", C.c_int32), ("x_dtype", C.c_int32)]
+
+
+class moe_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+        "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down")]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmoe_verify.so is not built (run __graft_entry__.build() or "
+                          "python -m moe_speculative_decoding_amd.build): %s" % LIB_PATH)
+    return C.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_P = C.c_void_p
+_I = C.c_int32
+_SIG = {
+    "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_build_union": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_dedup": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _I, _P, _P,
+                                  _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_expert_ffn_perslot": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _I, _P, _P,
+                                    _P, _P, _P, C.c_size_t, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]),
+    "moe_workspace_size": (C.c_size_t, [C.POINTER(moe_shape), _I, _I]),
+    "moe_workspace_init": (_I, [_P, C.c_size_t, _P]),
+    "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
+                             C.POINTER(C.c_uint64)]),
+    "moe_get_error": (_I, [_P, _P]),
+    "moe_decode_fp8": (_I, [_P, _P, C.c_int64, _P]),
+    "moe_status_str": (C.c_char_p, [_I]),
+    "moe_abi_version": (_I, []),
+}
+for _name, (_res, _args) in _SIG.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def status_str(status: int) -> str:
+    return lib.moe_status_str(int(status)).decode()
+
+
+def ptr(t) -> Optional[int]:
+    """Device address of a tensor (None/0 stays null; ints pass through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t or None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def make_shape(E: int, K: int, d: int, f: int, S: int, w_dtype: str, x_dtype: str) -> moe_shape:
+    return moe_shape(E, K, d, f, S, DTYPE_CODES[w_dtype], DTYPE_CODES[x_dtype])
+
+
+def make_weights(**tensors) -> moe_weights:
+    w = moe_weights()
+    for k, v in tensors.items():
+        setattr(w, k, ptr(v))
+    return w
+
+
+# ---------------------------------------------------------------- entry points
+def moe_route_topk(logits, n, E, K, ids, gates, stream=None) -> None:
+    _check(lib.moe_route_topk(ptr(logits), n, E, K, ptr(ids), ptr(gates), _stream(stream)),
+           "moe_route_topk")
+
+
+def moe_build_union(ids, n, K, E, U, union_ids, offsets, perm, slot_rank, stream=None) -> None:
+    _check(lib.moe_build_union(ptr(ids), n, K, E, ptr(U), ptr(union_ids), ptr(offsets), ptr(perm),
+                               ptr(slot_rank), _stream(stream)), "moe_build_union")
+
+
+def moe_expert_ffn_dedup(shape: moe_shape, w: moe_weights, x, n, U, union_ids, offsets, perm,
+                         y_slots, y_shared, bytes_, ws, ws_bytes, stream=None) -> None:
+    _check(lib.moe_expert_ffn_dedup(C.byref(shape), C.byref(w), ptr(x), n, ptr(U), ptr(union_ids),
+                                    ptr(offsets), ptr(perm), ptr(y_slots), ptr(y_shared),
+                                    ptr(bytes_), ptr(ws), ws_bytes, _stream(stream)),
+           "moe_expert_ffn_dedup")
+
+
+def moe_expert_ffn_perslot(shape: moe_shape, w: moe_weights, x, n, ids, y_slots, y_shared, bytes_,
+                           ws, ws_bytes, stream=None) -> None:
+    _check(lib.moe_expert_ffn_perslot(C.byref(shape), C.byref(w), ptr(x), n, ptr(ids),
+                                      ptr(y_slots), ptr(y_shared), ptr(bytes_), ptr(ws), ws_bytes,
+                                      _stream(stream)), "moe_expert_ffn_perslot")
+
+
+def moe_combine(y_slots, gates, y_shared, n, K, S, d, out, out_dtype, stream=None) -> None:
+    _check(lib.moe_combine(ptr(y_slots), ptr(gates), ptr(y_shared), n, K, S, d, ptr(out),
+                           out_dtype, _stream(stream)), "moe_combine")
+
+
+def moe_workspace_size(shape: moe_shape, n_max: int, mode: int) -> int:
+    return int(lib.moe_workspace_size(C.byref(shape), n_max, mode))
+
+
+def moe_workspace_init(ws, ws_bytes, stream=None) -> None:
+    _check(lib.moe_workspace_init(ptr(ws), ws_bytes, _stream(stream)), "moe_workspace_init")
+
+
+def moe_byte_counts(shape: moe_shape, n: int, U: int):
+    ub, rb = C.c_uint64(0), C.c_uint64(0)
+    _check(lib.moe_byte_counts(C.byref(shape), n, U, C.byref(ub), C.byref(rb)), "moe_byte_counts")
+    return int(ub.value), int(rb.value)
+
+
+def moe_get_error(ws, stream=None) -> int:
+    """Status of the device error word (also returned, not raised)."""
+    return int(lib.moe_get_error(ptr(ws), _stream(stream)))
+
+
+def moe_decode_fp8(codes, out, count, stream=None) -> None:
+    _check(lib.moe_decode_fp8(ptr(codes), ptr(out), count, _stream(stream)), "moe_decode_fp8")
+
+
+def moe_abi_version() -> int:
+    return int(lib.moe_abi_version())

@@ -1,0 +1,275 @@
+// C ABI of the MoE verify-pass library: host-side validation, workspace
+// sizing, byte accounting and the launches (the operations themselves are
+// described in include/moe_verify.h).  Every argument is checked before any
+// work is enqueued, so an invalid call enqueues nothing.
+#include "moe_verify.h"
+
+#include "common.h"
+
+namespace {
+
+using moe::kCtrlBytes;
+
+constexpr int kMaxN = 32, kMaxK = 8, kMaxE = 256, kMaxS = 4, kMaxDim = 65536;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case MOE_F32: return 4;
+    case MOE_BF16: return 2;
+    case MOE_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+// token storage type of a weight type (f32 for f32 weights, bf16 otherwise)
+int token_bytes(int w_dtype) { return w_dtype == MOE_F32 ? 4 : 2; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (s == nullptr) return MOE_ERR_ARG;
+  if (s->K < 1 || s->K > kMaxK || s->E < s->K || s->E > kMaxE) return MOE_ERR_ARG;
+  if (s->S < 0 || s->S > kMaxS) return MOE_ERR_ARG;
+  if (s->d < 1 || s->f < 1 || s->d > kMaxDim || s->f > kMaxDim) return MOE_ERR_ARG;
+  const bool ok_combo = (s->w_dtype == MOE_F32 && s->x_dtype == MOE_F32) ||
+                        (s->w_dtype == MOE_BF16 && s->x_dtype == MOE_BF16) ||
+                        (s->w_dtype == MOE_FP8_E4M3 && s->x_dtype == MOE_BF16);
+  if (!ok_combo) return MOE_ERR_UNSUPPORTED;
+  const int mult = s->w_dtype == MOE_F32 ? 4 : (s->w_dtype == MOE_BF16 ? 8 : 128);
+  if (s->d % mult != 0 || s->f % mult != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+uint64_t expert_bytes(const moe_shape* s) {
+  uint64_t b = 3ull * static_cast<uint64_t>(s->d) * static_cast<uint64_t>(s->f) *
+               static_cast<uint64_t>(elem_bytes(s->w_dtype));
+  if (s->w_dtype == MOE_FP8_E4M3) b += 3ull * (s->d / 128) * (s->f / 128) * 4ull;
+  return b;
+}
+
+size_t h_bytes(const moe_shape* s, int n) {
+  return static_cast<size_t>(n) * (s->K + s->S) * s->f * token_bytes(s->w_dtype);
+}
+
+moe_status check_weights(const moe_shape* s, const moe_weights* w) {
+  if (w == nullptr) return MOE_ERR_ARG;
+  const void* need[3] = {w->w_gate, w->w_up, w->w_down};
+  for (const void* p : need)
+    if (p == nullptr || !aligned(p, 16)) return MOE_ERR_ARG;
+  if (s->w_dtype == MOE_FP8_E4M3) {
+    const void* sc[3] = {w->s_gate, w->s_up, w->s_down};
+    for (const void* p : sc)
+      if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+  }
+  if (s->S > 0) {
+    const void* sh[3] = {w->sh_gate, w->sh_up, w->sh_down};
+    for (const void* p : sh)
+      if (p == nullptr || !aligned(p, 16)) return MOE_ERR_ARG;
+    if (s->w_dtype == MOE_FP8_E4M3) {
+      const void* ss[3] = {w->sh_s_gate, w->sh_s_up, w->sh_s_down};
+      for (const void* p : ss)
+        if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status check_ffn_common(const moe_shape* s, const moe_weights* w, const void* x, int n,
+                            float* y_slots, float* y_shared, const void* ws, size_t ws_bytes) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (n < 1 || n > kMaxN) return MOE_ERR_ARG;
+  st = check_weights(s, w);
+  if (st != MOE_OK) return st;
+  if (x == nullptr || !aligned(x, 16) || y_slots == nullptr || !aligned(y_slots, 4))
+    return MOE_ERR_ARG;
+  if (s->S > 0 && (y_shared == nullptr || !aligned(y_shared, 4))) return MOE_ERR_ARG;
+  if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < kCtrlBytes + h_bytes(s, n)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe::FfnParams make_params(const moe_shape* s, const moe_weights* w, const void* x, int n,
+                           float* y_slots, float* y_shared, uint64_t* bytes, void* ws) {
+  moe::FfnParams p{};
+  p.w[0] = static_cast<const uint8_t*>(w->w_gate);
+  p.w[1] = static_cast<const uint8_t*>(w->w_up);
+  p.w[2] = static_cast<const uint8_t*>(w->w_down);
+  p.s[0] = w->s_gate;
+  p.s[1] = w->s_up;
+  p.s[2] = w->s_down;
+  p.shw[0] = static_cast<const uint8_t*>(w->sh_gate);
+  p.shw[1] = static_cast<const uint8_t*>(w->sh_up);
+  p.shw[2] = static_cast<const uint8_t*>(w->sh_down);
+  p.shs[0] = w->sh_s_gate;
+  p.shs[1] = w->sh_s_up;
+  p.shs[2] = w->sh_s_down;
+  p.x = static_cast<const uint8_t*>(x);
+  p.err = static_cast<uint32_t*>(ws);
+  p.H = static_cast<uint8_t*>(ws) + kCtrlBytes;
+  p.y_slots = y_slots;
+  p.y_shared = y_shared;
+  p.bytes = bytes;
+  p.expert_bytes = expert_bytes(s);
+  p.n = n;
+  p.K = s->K;
+  p.S = s->S;
+  p.E = s->E;
+  p.d = s->d;
+  p.f = s->f;
+  p.ucap = n * s->K < s->E ? n * s->K : s->E;
+  return p;
+}
+
+int wt_of(int w_dtype) {
+  return w_dtype == MOE_F32 ? moe::WT_F32 : (w_dtype == MOE_BF16 ? moe::WT_BF16 : moe::WT_FP8);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_BAD_IDS: return "expert id outside [0, E)";
+    case MOE_ERR_TIMEOUT: return "bounded device wait gave up";
+    default: return "unknown status";
+  }
+}
+
+moe_status moe_route_topk(const float* logits, int32_t n, int32_t E, int32_t K, int32_t* ids,
+                          float* gates, moe_stream_t stream) {
+  if (n < 1 || n > kMaxN || K < 1 || K > kMaxK || E < K || E > kMaxE) return MOE_ERR_ARG;
+  if (logits == nullptr || ids == nullptr || gates == nullptr) return MOE_ERR_ARG;
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4)) return MOE_ERR_ARG;
+  return moe::launch_route_topk(logits, n, E, K, ids, gates, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status moe_build_union(const int32_t* ids, int32_t n, int32_t K, int32_t E, int32_t* U,
+                           int32_t* union_ids, int32_t* offsets, int32_t* perm,
+                           int32_t* slot_rank, moe_stream_t stream) {
+  if (n < 1 || n > kMaxN || K < 1 || K > kMaxK || E < K || E > kMaxE) return MOE_ERR_ARG;
+  const void* ptrs[6] = {ids, U, union_ids, offsets, perm, slot_rank};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+  return moe::launch_build_union(ids, n, K, E, U, union_ids, offsets, perm, slot_rank,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status moe_expert_ffn_dedup(const moe_shape* shape, const moe_weights* w, const void* x,
+                                int32_t n, const int32_t* U, const int32_t* union_ids,
+                                const int32_t* offsets, const int32_t* perm, float* y_slots,
+                                float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
+                                moe_stream_t stream) {
+  moe_status st = check_ffn_common(shape, w, x, n, y_slots, y_shared, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const void* ptrs[4] = {U, union_ids, offsets, perm};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+  if (bytes != nullptr && !aligned(bytes, 8)) return MOE_ERR_ARG;
+  moe::FfnParams p = make_params(shape, w, x, n, y_slots, y_shared, bytes, ws);
+  p.mode = moe::MODE_DEDUP;
+  p.U = U;
+  p.union_ids = union_ids;
+  p.offsets = offsets;
+  p.perm = perm;
+  return moe::launch_expert_ffn(p, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status moe_expert_ffn_perslot(const moe_shape* shape, const moe_weights* w, const void* x,
+                                  int32_t n, const int32_t* ids, float* y_slots, float* y_shared,
+                                  uint64_t* bytes, void* ws, size_t ws_bytes,
+                                  moe_stream_t stream) {
+  moe_status st = check_ffn_common(shape, w, x, n, y_slots, y_shared, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (ids == nullptr || !aligned(ids, 4)) return MOE_ERR_ARG;
+  if (bytes != nullptr && !aligned(bytes, 8)) return MOE_ERR_ARG;
+  moe::FfnParams p = make_params(shape, w, x, n, y_slots, y_shared, bytes, ws);
+  p.mode = moe::MODE_PERSLOT;
+  p.ids = ids;
+  return moe::launch_expert_ffn(p, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status moe_combine(const float* y_slots, const float* gates, const float* y_shared,
+                       int32_t n, int32_t K, int32_t S, int32_t d, void* out, int32_t out_dtype,
+                       moe_stream_t stream) {
+  if (n < 1 || n > kMaxN || K < 1 || K > kMaxK || S < 0 || S > kMaxS || d < 1 || d > kMaxDim)
+    return MOE_ERR_ARG;
+  if (y_slots == nullptr || gates == nullptr || out == nullptr) return MOE_ERR_ARG;
+  if (S > 0 && y_shared == nullptr) return MOE_ERR_ARG;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(y_slots, 4) || !aligned(gates, 4) || !aligned(out, 2)) return MOE_ERR_ARG;
+  if (out_dtype == MOE_F32 && !aligned(out, 4)) return MOE_ERR_ARG;
+  return moe::launch_combine(y_slots, gates, y_shared, n, K, S, d, out, out_dtype == MOE_BF16,
+                             static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode) {
+  if (check_shape(shape) != MOE_OK || n_max < 1 || n_max > kMaxN) return 0;
+  if (mode != MOE_MODE_DEDUP && mode != MOE_MODE_PERSLOT) return 0;
+  const size_t h = h_bytes(shape, n_max);
+  return kCtrlBytes + ((h + 255) / 256) * 256;
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
+  return moe::launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status moe_byte_counts(const moe_shape* shape, int32_t n, int32_t U, uint64_t* union_bytes,
+                           uint64_t* requested_bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (n < 1 || n > kMaxN) return MOE_ERR_ARG;
+  const int cap = n * shape->K < shape->E ? n * shape->K : shape->E;
+  if (U < shape->K || U > cap) return MOE_ERR_ARG;
+  const uint64_t b = expert_bytes(shape);
+  if (union_bytes) *union_bytes = static_cast<uint64_t>(U + shape->S) * b;
+  if (requested_bytes) *requested_bytes = static_cast<uint64_t>(n) * (shape->K + shape->S) * b;
+  return MOE_OK;
+}
+
+moe_status moe_get_error(void* ws, moe_stream_t stream) {
+  if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  if (word == 0) return MOE_OK;
+  const uint32_t zero = 0;
+  if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return MOE_ERR_HIP;
+  if (word & moe::ERRBIT_BAD_IDS) return MOE_ERR_BAD_IDS;
+  return MOE_ERR_TIMEOUT;
+}
+
+moe_status moe_decode_fp8(const uint8_t* codes, float* out, int64_t count, moe_stream_t stream) {
+  if (count < 0 || (count > 0 && (codes == nullptr || out == nullptr))) return MOE_ERR_ARG;
+  if (out != nullptr && !aligned(out, 4)) return MOE_ERR_ARG;
+  return moe::launch_decode_fp8(codes, out, count, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations of the MoE verify-pass library (gfx950 / CDNA4).
+// Device helpers shared by the kernels and the launch functions the C ABI
+// layer calls.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // 4 waves
+
+enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
+enum { MODE_DEDUP = 0, MODE_PERSLOT = 1 };
+enum : uint32_t { ERRBIT_BAD_IDS = 1u, ERRBIT_TIMEOUT = 2u };
+
+// Workspace: [0, kCtrlBytes) control words (error word first), then the
+// intermediate activations H [n*(K+S)][f] in the token storage type.
+constexpr size_t kCtrlBytes = 256;
+
+// ----------------------------------------------------------------- loads
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned v) {
+  return __builtin_bit_cast(bf16x2, v);
+}
+
+// Two E4M3FN codes (bytes 0,1 of the dword when hi == false, bytes 2,3
+// otherwise) -> two bf16 values, exactly (every E4M3FN value is a bf16 value).
+template <bool hi>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, hi);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<unsigned>(b) << 16);
+}
+
+// Round-to-nearest-even f32 -> bf16 bits (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  unsigned u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------- FFN launch parameters
+struct FfnParams {
+  const uint8_t* w[3];    // routed gate [E][f][d], up [E][f][d], down [E][d][f]
+  const float* s[3];      // fp8 block scales of the same three matrices
+  const uint8_t* shw[3];  // shared experts, same layouts with S for E
+  const float* shs[3];
+  const uint8_t* x;       // [n][d] tokens
+  uint8_t* H;             // [n*(K+S)][f] intermediate activations
+  float* y_slots;         // [n][K][d]
+  float* y_shared;        // [n][S][d]
+  const int32_t* U;       // dedup: union size (device)
+  const int32_t* union_ids;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* ids;     // per-slot: [n][K]
+  uint32_t* err;          // error word (workspace)
+  uint64_t* bytes;        // [2] or null
+  unsigned long long expert_bytes;
+  int n, K, S, E, d, f;
+  int ucap;               // dedup: upper bound of U = min(n*K, E)
+  int mode;
+};
+
+hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* ids,
+                             float* gates, hipStream_t s);
+hipError_t launch_build_union(const int32_t* ids, int n, int K, int E, int32_t* U,
+                              int32_t* union_ids, int32_t* offsets, int32_t* perm,
+                              int32_t* slot_rank, hipStream_t s);
+hipError_t launch_expert_ffn(const FfnParams& p, int w_dtype, hipStream_t s);
+hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
+                          int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_decode_fp8(const uint8_t* codes, float* out, long long count, hipStream_t s);
+
+}  // namespace moe

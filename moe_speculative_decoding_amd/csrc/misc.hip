@@ -1,0 +1,87 @@
+// Combine of the slot outputs, workspace fill and the fp8 decode diagnostic (gfx950).
+//
+// Combine: the layer output of a MoE layer is the gate-weighted sum of its
+// selected experts' outputs ("Making Every Verified Token Count: Adaptive
+// Verification for MoE Speculative Decoding", Sec. 2.2), plus the shared
+// experts, which every token uses with weight 1.
+#include "common.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(kBlock) void combine_kernel(const float* __restrict__ y_slots,
+                                                         const float* __restrict__ gates,
+                                                         const float* __restrict__ y_shared,
+                                                         int n, int K, int S, int d,
+                                                         void* __restrict__ out, int out_bf16) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= n || c >= d) return;
+  float acc = 0.0f;
+  const float* g = gates + static_cast<size_t>(t) * K;
+  const float* y = y_slots + static_cast<size_t>(t) * K * d + c;
+  for (int k = 0; k < K; ++k) acc = fmaf(g[k], y[static_cast<size_t>(k) * d], acc);
+  if (S > 0) {
+    const float* ys = y_shared + static_cast<size_t>(t) * S * d + c;
+    for (int s = 0; s < S; ++s) acc += ys[static_cast<size_t>(s) * d];
+  }
+  const size_t o = static_cast<size_t>(t) * d + c;
+  if (out_bf16) {
+    reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(acc);
+  } else {
+    reinterpret_cast<float*>(out)[o] = acc;
+  }
+}
+
+hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
+                          int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s) {
+  dim3 grid((d + kBlock - 1) / kBlock, n);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kBlock), 0, s, y_slots, gates, y_shared, n, K,
+                     S, d, out, out_bf16);
+  return hipGetLastError();
+}
+
+// Zero fill with a kernel (no memset node, so it is safe inside captured graphs).
+__global__ __launch_bounds__(kBlock) void fill_zero_kernel(uint32_t* __restrict__ p, size_t words) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kBlock;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; i < words; i += stride)
+    p[i] = 0u;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + kBlock - 1) / kBlock;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
+                     static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+// Each lane decodes one code with the conversion the fp8 FFN kernels use,
+// picking its byte position inside the aligned dword that holds it.
+__global__ __launch_bounds__(kBlock) void decode_fp8_kernel(const uint8_t* __restrict__ codes,
+                                                            float* __restrict__ out,
+                                                            long long count) {
+  const long long i = static_cast<long long>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= count) return;
+  const int pos = static_cast<int>(i & 3);
+  unsigned word = 0;
+  // assemble the dword from bytes that exist (the buffer may end mid-dword)
+  const long long base = i - pos;
+  for (int b = 0; b < 4; ++b)
+    if (base + b < count) word |= static_cast<unsigned>(codes[base + b]) << (8 * b);
+  const bf16x2 v = (pos < 2) ? fp8x2_to_bf16x2<false>(word) : fp8x2_to_bf16x2<true>(word);
+  const unsigned pair = __builtin_bit_cast(unsigned, v);
+  const uint16_t bits = (pos & 1) ? static_cast<uint16_t>(pair >> 16) : static_cast<uint16_t>(pair);
+  out[i] = bf16_bits_to_f32(bits);
+}
+
+hipError_t launch_decode_fp8(const uint8_t* codes, float* out, long long count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const long long blocks = (count + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(decode_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
+                     codes, out, count);
+  return hipGetLastError();
+}
+
+}  // namespace moe

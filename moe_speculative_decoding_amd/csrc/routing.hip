@@ -1,0 +1,197 @@
+// Router top-K and expert union for one verify pass (gfx950).
+//
+// Top-K: "Making Every Verified Token Count: Adaptive Verification for MoE
+// Speculative Decoding", Sec. 2.2, Eq. (4) — the indices of the K largest
+// router scores, normalised (softmax over the K here).
+// Union: "Less Experts, Faster Decoding", Sec. 3, Eq. (1), and the same page
+// family's Eq. (5) / (A2): the distinct experts of all verified tokens; the
+// slot permutation sorts rows by expert as the MLX-LM deduplicating engine
+// does (expert-bytes page, Table 6).
+//
+// Both are integer-exact: top-K compares 64-bit keys built from the fp32
+// bit pattern (no float arithmetic decides a selection), and the union uses
+// an LDS histogram per wavefront, ballot scans and a ballot-based match of
+// equal ids, so every output is deterministic.
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ top-K
+// Key order = (logit descending, id ascending); NaN below every number,
+// -0.0 equal to +0.0.  Larger key wins; every real entry has a non-zero key.
+__device__ __forceinline__ unsigned long long topk_key(float v, int e) {
+  unsigned b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;  // -0.0 -> +0.0
+  unsigned k32;
+  if ((b & 0x7fffffffu) > 0x7f800000u) {
+    k32 = 0u;  // NaN
+  } else {
+    k32 = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+  return (static_cast<unsigned long long>(k32) << 32) | static_cast<unsigned>(~static_cast<unsigned>(e));
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
+  unsigned lo = __shfl_xor(static_cast<unsigned>(v), o);
+  unsigned hi = __shfl_xor(static_cast<unsigned>(v >> 32), o);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// One wavefront per token; each lane holds up to 4 of the E <= 256 logits.
+__global__ __launch_bounds__(kBlock) void route_topk_kernel(const float* __restrict__ logits,
+                                                            int n, int E, int K,
+                                                            int32_t* __restrict__ ids,
+                                                            float* __restrict__ gates) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kBlock / kWave) + wave;
+  if (t >= n) return;  // wave-uniform
+  const float* row = logits + static_cast<size_t>(t) * E;
+  unsigned long long key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    key[j] = (e < E) ? topk_key(row[e], e) : 0ull;
+  }
+  int my_id = 0;
+  for (int k = 0; k < K; ++k) {
+    unsigned long long best = key[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const unsigned long long other = shfl_xor_u64(best, o);
+      best = other > best ? other : best;
+    }
+    const int e = static_cast<int>(~static_cast<unsigned>(best));
+    if (lane == (e & 63)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == (e >> 6)) key[j] = 0ull;
+    }
+    if (lane == k) my_id = e;
+  }
+  // softmax over the selected logits; the first selection holds the maximum
+  float l = (lane < K) ? row[my_id] : 0.0f;
+  const float top = __shfl(l, 0);
+  float ex = (lane < K) ? expf(l - top) : 0.0f;
+  float sum = ex;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  if (lane < K) {
+    ids[static_cast<size_t>(t) * K + lane] = my_id;
+    gates[static_cast<size_t>(t) * K + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* ids,
+                             float* gates, hipStream_t s) {
+  const int per_block = kBlock / kWave;
+  dim3 grid((n + per_block - 1) / per_block);
+  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kBlock), 0, s, logits, n, E, K, ids, gates);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ union
+// One workgroup of 256 lanes; lane s owns slot s (n*K <= 256) and expert e = s
+// (E <= 256).
+__global__ __launch_bounds__(kBlock) void build_union_kernel(
+    const int32_t* __restrict__ ids, int n, int K, int E, int32_t* __restrict__ U_out,
+    int32_t* __restrict__ union_ids, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ slot_rank) {
+  __shared__ int wcnt[kBlock / kWave][256];  // per-wave histogram of ids
+  __shared__ int rank_of[256];               // expert -> union position
+  __shared__ int start_of[256];              // expert -> first position in perm
+  __shared__ int wtot_present[kBlock / kWave];
+  __shared__ int wtot_count[kBlock / kWave];
+  __shared__ int bad;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nk = n * K;
+  const int cap = nk < E ? nk : E;
+  for (int i = tid; i < (kBlock / kWave) * 256; i += kBlock) (&wcnt[0][0])[i] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+
+  const bool act = tid < nk;
+  int id = act ? ids[tid] : 0;
+  if (act) {
+    if (id < 0 || id >= E) {
+      atomicOr(&bad, 1);
+    } else {
+      atomicAdd(&wcnt[wave][id], 1);
+    }
+  }
+  __syncthreads();
+  if (bad) {
+    if (tid == 0) *U_out = -1;
+    return;
+  }
+
+  // exclusive scans over experts e = tid of "present" and of the slot count
+  const int e = tid;
+  int c = 0;
+  if (e < E) c = wcnt[0][e] + wcnt[1][e] + wcnt[2][e] + wcnt[3][e];
+  const int pres = (e < E && c > 0) ? 1 : 0;
+  const unsigned long long pmask = __ballot(pres);
+  const int pre_present = __popcll(pmask & ((1ull << lane) - 1ull));
+  int inc = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int up = __shfl_up(inc, o);
+    if (lane >= o) inc += up;
+  }
+  if (lane == kWave - 1) {
+    wtot_present[wave] = __popcll(pmask);
+    wtot_count[wave] = inc;
+  }
+  __syncthreads();
+  int base_p = 0, base_c = 0, Utot = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) {
+    if (w < wave) {
+      base_p += wtot_present[w];
+      base_c += wtot_count[w];
+    }
+    Utot += wtot_present[w];
+  }
+  const int rank = base_p + pre_present;
+  const int start = base_c + inc - c;
+  rank_of[e] = rank;
+  start_of[e] = start;
+  if (pres) {
+    union_ids[rank] = e;
+    offsets[rank] = start;
+  }
+  for (int i = Utot + tid; i < cap; i += kBlock) union_ids[i] = -1;
+  for (int i = Utot + tid; i <= cap; i += kBlock) offsets[i] = nk;
+  if (tid == 0) *U_out = Utot;
+  __syncthreads();
+
+  // stable position of slot tid among the slots of its expert:
+  // slots of earlier waves (histograms) + earlier lanes of this wave with the
+  // same id (8 ballots over the id bits, ids < 256)
+  unsigned long long same = __ballot(act);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int bit = (id >> b) & 1;
+    const unsigned long long ones = __ballot(act && bit);
+    same &= bit ? ones : ~ones;
+  }
+  if (act) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wcnt[w][id];
+    const int pos = start_of[id] + before + __popcll(same & ((1ull << lane) - 1ull));
+    perm[pos] = tid;
+    slot_rank[tid] = rank_of[id];
+  }
+}
+
+hipError_t launch_build_union(const int32_t* ids, int n, int K, int E, int32_t* U,
+                              int32_t* union_ids, int32_t* offsets, int32_t* perm,
+                              int32_t* slot_rank, hipStream_t s) {
+  hipLaunchKernelGGL(build_union_kernel, dim3(1), dim3(kBlock), 0, s, ids, n, K, E, U, union_ids,
+                     offsets, perm, slot_rank);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -238,3 +238,37 @@ def make_case(cfg: LayerConfig, n: int, routing: Optional[str] = None, seed: int
                                 gen_sets, cfg.E)
     return Case(cfg=cfg, n=n, routing=routing, seed=seed, layer=layer, window=window,
                 x=x, logits=logits, parents=parents, gen_sets=gen_sets)
+
+
+# ------------------------------------------------- device-resident layer weights
+def device_layer_weights(cfg: LayerConfig, seed: int, layer: int, device, count: Optional[int] = None,
+                         shared: bool = False) -> Dict[str, "torch.Tensor"]:
+    """Weights of a whole layer drawn directly on the device (large benchmark layers).
+
+    Same recipe as ``expert_weights`` (N(0, 1/d) per element; fp8 codes with one
+    scale per 128x128 block), drawn from torch's device generator seeded with
+    (seed, cfg_id, layer, shared); the values therefore differ from the host
+    generator's, and a check against the oracle copies the experts it needs back.
+    """
+    count = count if count is not None else (cfg.S if shared else cfg.E)
+    g = torch.Generator(device=device)
+    g.manual_seed(((seed * 1000003 + cfg.cfg_id) * 10007 + layer) * 2 + int(shared))
+    std = 1.0 / float(np.sqrt(cfg.d))
+    out: Dict[str, torch.Tensor] = {}
+    shapes = {"w_gate": (cfg.f, cfg.d), "w_up": (cfg.f, cfg.d), "w_down": (cfg.d, cfg.f)}
+    for name, (r, c) in shapes.items():
+        w = torch.randn((count, r, c), generator=g, device=device, dtype=torch.float32)
+        w.mul_(std)
+        if cfg.w_dtype == FP8:
+            blocks = w.view(count, r // FP8_BLOCK, FP8_BLOCK, c // FP8_BLOCK, FP8_BLOCK)
+            amax = blocks.abs().amax(dim=(2, 4))
+            scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+            blocks.div_(scale[:, :, None, :, None]).clamp_(-FP8_MAX, FP8_MAX)
+            out[name] = w.to(torch.float8_e4m3fn).view(torch.uint8)
+            out["s" + name[1:]] = scale.contiguous()
+        elif cfg.w_dtype == BF16:
+            out[name] = w.to(torch.bfloat16).view(torch.int16)
+        else:
+            out[name] = w
+        del w
+    return out

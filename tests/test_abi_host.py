@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/moe_verify.h
+declares, reject invalid calls before touching the device, and size
+workspaces / count bytes as documented.  No call here reaches a launch.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle
+from synth.configs import ALL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+L = pytest.importorskip("moe_speculative_decoding_amd._lib",
+                        reason="libmoe_verify.so not built")
+
+FAKE = 0x10000  # an aligned non-null address; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = C.CDLL(L.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert L.moe_abi_version() == 1
+    for s in range(7):
+        assert L.status_str(s) and L.status_str(s) != "unknown status"
+    assert L.status_str(99) == "unknown status"
+
+
+def shape(**kw):
+    base = dict(E=64, K=8, d=2048, f=1024, S=0, w_dtype="bf16", x_dtype="bf16")
+    base.update(kw)
+    return L.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(K=0), L.MOE_ERR_ARG), (dict(K=9), L.MOE_ERR_ARG), (dict(E=7), L.MOE_ERR_ARG),
+    (dict(E=257), L.MOE_ERR_ARG), (dict(S=5), L.MOE_ERR_ARG), (dict(S=-1), L.MOE_ERR_ARG),
+    (dict(d=0), L.MOE_ERR_ARG), (dict(f=70000), L.MOE_ERR_ARG),
+    (dict(w_dtype="bf16", x_dtype="f32"), L.MOE_ERR_UNSUPPORTED),
+    (dict(w_dtype="f32", x_dtype="bf16"), L.MOE_ERR_UNSUPPORTED),
+    (dict(w_dtype="fp8_e4m3", x_dtype="fp8_e4m3"), L.MOE_ERR_UNSUPPORTED),
+    (dict(d=2044), L.MOE_ERR_UNSUPPORTED),                       # bf16 needs d % 8 == 0
+    (dict(w_dtype="fp8_e4m3", d=2048, f=1000), L.MOE_ERR_UNSUPPORTED),  # fp8 needs % 128
+])
+def test_shape_validation(kw, expect):
+    s = shape(**kw)
+    ub, rb = C.c_uint64(), C.c_uint64()
+    assert L.lib.moe_byte_counts(C.byref(s), 1, s.K, C.byref(ub), C.byref(rb)) == expect
+    assert L.moe_workspace_size(s, 4, L.MOE_MODE_DEDUP) == 0
+
+
+def _weights():
+    return L.make_weights(w_gate=FAKE, w_up=FAKE, w_down=FAKE)
+
+
+def test_ffn_validation_before_launch():
+    s = shape()
+    w = _weights()
+    ws_need = L.moe_workspace_size(s, 8, L.MOE_MODE_DEDUP)
+    dd = L.lib.moe_expert_ffn_dedup
+    args = [C.byref(s), C.byref(w), FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+            ws_need, None]
+    bad = list(args); bad[3] = 0          # n = 0
+    assert dd(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[3] = 33         # n > 32
+    assert dd(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[2] = FAKE + 4   # misaligned x
+    assert dd(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[12] = ws_need - 1
+    assert dd(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(args); bad[11] = FAKE + 64  # workspace not 256-aligned
+    assert dd(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(args); bad[4] = None       # U missing
+    assert dd(*bad) == L.MOE_ERR_ARG
+    w2 = L.make_weights(w_gate=FAKE, w_up=None, w_down=FAKE)
+    bad = list(args); bad[1] = C.byref(w2)
+    assert dd(*bad) == L.MOE_ERR_ARG
+    s_sh = shape(S=2)
+    bad = list(args); bad[0] = C.byref(s_sh)   # shared experts but no shared weights
+    bad[12] = L.moe_workspace_size(s_sh, 8, L.MOE_MODE_DEDUP)
+    assert dd(*bad) == L.MOE_ERR_ARG
+    s8 = shape(w_dtype="fp8_e4m3", d=2048, f=1024)
+    bad = list(args); bad[0] = C.byref(s8)     # fp8 without scales
+    bad[12] = L.moe_workspace_size(s8, 8, L.MOE_MODE_DEDUP)
+    assert dd(*bad) == L.MOE_ERR_ARG
+
+    ps = L.lib.moe_expert_ffn_perslot
+    assert ps(C.byref(s), C.byref(w), FAKE, 8, None, FAKE, None, None, FAKE, ws_need, None) \
+        == L.MOE_ERR_ARG                                           # ids missing
+
+
+def test_routing_and_combine_validation():
+    rt = L.lib.moe_route_topk
+    assert rt(FAKE, 0, 8, 2, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert rt(FAKE, 4, 8, 9, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert rt(FAKE, 4, 300, 2, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert rt(None, 4, 8, 2, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    bu = L.lib.moe_build_union
+    assert bu(FAKE, 33, 8, 256, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert bu(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, FAKE, None) == L.MOE_ERR_ARG
+    cb = L.lib.moe_combine
+    assert cb(FAKE, FAKE, None, 4, 2, 1, 256, FAKE, L.MOE_F32, None) == L.MOE_ERR_ARG
+    assert cb(FAKE, FAKE, None, 4, 2, 0, 256, FAKE, L.MOE_FP8_E4M3, None) == L.MOE_ERR_UNSUPPORTED
+    assert L.lib.moe_decode_fp8(None, FAKE, 5, None) == L.MOE_ERR_ARG
+    assert L.lib.moe_workspace_init(FAKE + 8, 1024, None) == L.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("cfg", ALL, ids=lambda c: c.name)
+def test_byte_counts_match_oracle(cfg):
+    s = L.make_shape(cfg.E, cfg.K, cfg.d, cfg.f, cfg.S, cfg.w_dtype, cfg.x_dtype)
+    for n in (1, 2, 8, 32):
+        cap = min(n * cfg.K, cfg.E)
+        for U in sorted({cfg.K, (cfg.K + cap) // 2, cap}):
+            assert L.moe_byte_counts(s, n, U) == oracle.byte_counts(
+                cfg.d, cfg.f, cfg.w_dtype, cfg.K, cfg.S, n, U)
+        with pytest.raises(L.MoeError):
+            L.moe_byte_counts(s, n, cap + 1)
+    tb = 4 if cfg.w_dtype == "f32" else 2
+    need = 256 + 32 * (cfg.K + cfg.S) * cfg.f * tb
+    got = L.moe_workspace_size(s, 32, L.MOE_MODE_DEDUP)
+    assert need <= got < need + 256 and got % 256 == 0

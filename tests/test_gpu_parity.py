@@ -1,0 +1,208 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Routing, union and permutation are compared bit for bit; expert outputs and
+the combined layer output within the tolerances of ``gpu_harness``.  Cases:
+the five layer shapes at their real sizes (the DeepSeek-V3 shape at its
+smallest pass sizes), plus small shapes with ragged tails (d, f not
+multiples of a load step or of a workgroup's row block), groups of more
+tokens than one LDS tile holds, K = E, ties and NaN logits, and invalid ids.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_case
+from synth.configs import DSV2LITE, DSV3, LayerConfig, OLMOE, QWEN3, TINY
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU machines, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+from moe_speculative_decoding_amd import _lib as L  # noqa: E402
+from gpu_harness import DEV, run_case  # noqa: E402
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+# ------------------------------------------------------------ fp8 decoding
+def test_decode_fp8_every_code_every_byte_position():
+    codes = np.concatenate([np.arange(256, dtype=np.uint8)] * 4 + [np.arange(3, dtype=np.uint8)])
+    # shift so each code lands in every position of its dword
+    codes = np.concatenate([codes[1:], codes[:1]])
+    out = torch.empty(len(codes), dtype=torch.float32, device=DEV)
+    L.moe_decode_fp8(dev(codes), out, len(codes))
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.decode_fp8_e4m3fn(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+# --------------------------------------------------------------- top-K
+def _route(logits, K):
+    n, E = logits.shape
+    ids = torch.full((n, K), -7, dtype=torch.int32, device=DEV)
+    gates = torch.zeros(n, K, dtype=torch.float32, device=DEV)
+    L.moe_route_topk(dev(logits), n, E, K, ids, gates)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), gates.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("cfg,n,routing,tree", [
+    (TINY, 4, None, False), (QWEN3, 8, None, False), (OLMOE, 8, "markov:0.5", False),
+    (DSV3, 8, "iid", False), (DSV3, 32, "markov:0.5", True), (DSV2LITE, 16, "markov:0.5", True),
+])
+def test_route_topk_matches_oracle(cfg, n, routing, tree):
+    case = make_case(cfg, n, routing, seed=0, tree=tree)
+    ids, gates = _route(case.logits, cfg.K)
+    rid, rg = oracle.route_topk(case.logits, cfg.K)
+    assert np.array_equal(ids, rid)
+    assert np.all(np.abs(gates - rg) <= 1e-6 + 1e-5 * np.abs(rg))
+
+
+@pytest.mark.parametrize("n,E,K", [(32, 256, 8), (5, 8, 8), (7, 13, 3), (1, 64, 1)])
+def test_route_topk_ties_nan_signed_zero(n, E, K):
+    g = np.random.default_rng(E * 7 + K)
+    vals = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0, np.nan, -np.inf], dtype=np.float32)
+    logits = vals[g.integers(0, len(vals), (n, E))]
+    ids, _ = _route(logits, K)
+    rid, _ = oracle.route_topk(logits, K)
+    assert np.array_equal(ids, rid)
+
+
+# --------------------------------------------------------------- union
+def _union(ids, E):
+    n, K = ids.shape
+    cap = min(n * K, E)
+    U = torch.full((1,), -9, dtype=torch.int32, device=DEV)
+    uid = torch.full((cap,), -9, dtype=torch.int32, device=DEV)
+    off = torch.full((cap + 1,), -9, dtype=torch.int32, device=DEV)
+    perm = torch.full((n * K,), -9, dtype=torch.int32, device=DEV)
+    rank = torch.full((n * K,), -9, dtype=torch.int32, device=DEV)
+    L.moe_build_union(dev(ids.astype(np.int32)), n, K, E, U, uid, off, perm, rank)
+    torch.cuda.synchronize()
+    return {"U": int(U.item()), "union_ids": uid.cpu().numpy(), "offsets": off.cpu().numpy(),
+            "perm": perm.cpu().numpy(), "slot_rank": rank.cpu().numpy()}
+
+
+@pytest.mark.parametrize("n,E,K,pool", [(32, 256, 8, 256), (32, 256, 8, 12), (8, 64, 8, 64),
+                                        (4, 8, 2, 8), (1, 8, 8, 8), (32, 8, 8, 8), (17, 100, 5, 9),
+                                        (16, 64, 6, 64)])
+def test_build_union_bit_exact(n, E, K, pool):
+    g = np.random.default_rng(n * 31 + E + pool)
+    for rep in range(4):
+        # distinct ids per token drawn from a small subset -> heavy repetition across tokens
+        subset = g.choice(E, pool, replace=False)
+        ids = np.stack([g.choice(subset, K, replace=False) for _ in range(n)]).astype(np.int32)
+        got = _union(ids, E)
+        ref = oracle.build_union(ids, E)
+        for k in ("U", "union_ids", "offsets", "perm", "slot_rank"):
+            assert np.array_equal(np.asarray(got[k]), np.asarray(ref[k])), (k, rep)
+
+
+def test_build_union_flags_out_of_range_ids():
+    ids = np.array([[0, 3], [8, 1]], dtype=np.int32)
+    assert _union(ids, 8)["U"] == -1
+    ids = np.array([[0, -1]], dtype=np.int32)
+    assert _union(ids, 8)["U"] == -1
+
+
+# ----------------------------------------------------------- expert FFN
+RAGGED_BF16 = LayerConfig(name="ragged_bf16", cfg_id=80, E=16, K=4, d=264, f=136, S=1,
+                          w_dtype="bf16", x_dtype="bf16", n_values=(1, 5, 32),
+                          routing=("markov:0.8",), tolerance=1e-2)
+RAGGED_FP8 = LayerConfig(name="ragged_fp8", cfg_id=81, E=8, K=2, d=384, f=256, S=1,
+                         w_dtype="fp8_e4m3", x_dtype="bf16", n_values=(3, 9),
+                         routing=("markov:0.5",), tolerance=3e-2)
+RAGGED_F32 = LayerConfig(name="ragged_f32", cfg_id=82, E=6, K=3, d=300, f=68, S=2,
+                         w_dtype="f32", x_dtype="f32", n_values=(2, 11),
+                         routing=("markov:0.5",), tolerance=1e-5)
+
+
+@pytest.mark.parametrize("cfg,n,routing,tree", [
+    (TINY, 4, None, False),
+    (RAGGED_BF16, 1, None, False), (RAGGED_BF16, 5, None, False), (RAGGED_BF16, 32, None, True),
+    (RAGGED_BF16, 32, "markov:1.0", False),
+    (RAGGED_FP8, 3, None, False), (RAGGED_FP8, 9, None, False),
+    (RAGGED_F32, 2, None, False), (RAGGED_F32, 11, None, False),
+])
+def test_ffn_small_and_ragged(cfg, n, routing, tree):
+    case = make_case(cfg, n, routing, seed=2, tree=tree)
+    run_case(case)
+
+
+@pytest.mark.parametrize("n,p", [(1, 0.5), (2, 0.5), (4, 0.5), (8, 0.5), (8, 0.0), (8, 0.8)])
+def test_ffn_olmoe_shape(n, p):
+    run_case(make_case(OLMOE, n, "markov:%s" % p, seed=0))
+
+
+@pytest.mark.parametrize("n", [1, 5, 8])
+def test_ffn_qwen3_shape(n):
+    run_case(make_case(QWEN3, n, None, seed=1))
+
+
+@pytest.mark.parametrize("n,tree", [(3, False), (8, False), (16, True)])
+def test_ffn_dsv2lite_shape(n, tree):
+    run_case(make_case(DSV2LITE, n, "markov:0.5", seed=0, tree=tree))
+
+
+@pytest.mark.parametrize("n,routing", [(1, "iid"), (2, "markov:0.5")])
+def test_ffn_dsv3_shape(n, routing):
+    run_case(make_case(DSV3, n, routing, seed=0))
+
+
+# ------------------------------------------------------- invalid expert ids
+def test_perslot_bad_id_gives_zero_row_and_error():
+    from moe_speculative_decoding_amd.layer import VerifyBuffers
+    from gpu_harness import upload_layer
+    case = make_case(TINY, 2, None, seed=5)
+    layer = upload_layer(case)
+    buf = VerifyBuffers(layer, 2, DEV)
+    ids = np.array([[1, 2], [3, 99]], dtype=np.int32)
+    buf.y_slots.fill_(7.0)
+    L.moe_expert_ffn_perslot(layer.shape, layer.weights, dev(case.x), 2, dev(ids), buf.y_slots,
+                             None, buf.bytes, buf.ws, buf.ws_bytes)
+    assert L.moe_get_error(buf.ws) == L.MOE_ERR_BAD_IDS
+    assert L.moe_get_error(buf.ws) == L.MOE_OK  # cleared
+    y = buf.y_slots.cpu().numpy()
+    assert np.all(y[1, 1] == 0.0)
+    assert np.all(np.isfinite(y[0])) and not np.all(y[0, 0] == 7.0)
+
+
+def test_dedup_after_bad_union_reports_error():
+    from moe_speculative_decoding_amd.layer import VerifyBuffers
+    from gpu_harness import upload_layer
+    case = make_case(TINY, 2, None, seed=5)
+    layer = upload_layer(case)
+    buf = VerifyBuffers(layer, 2, DEV)
+    ids = dev(np.array([[1, 2], [3, -4]], dtype=np.int32))
+    L.moe_build_union(ids, 2, 2, 8, buf.U, buf.union_ids, buf.offsets, buf.perm, buf.slot_rank)
+    L.moe_expert_ffn_dedup(layer.shape, layer.weights, dev(case.x), 2, buf.U, buf.union_ids,
+                           buf.offsets, buf.perm, buf.y_slots, None, buf.bytes, buf.ws, buf.ws_bytes)
+    assert L.moe_get_error(buf.ws) == L.MOE_ERR_BAD_IDS
+    assert int(buf.U.item()) == -1
+
+
+def test_combine_matches_oracle_f32_and_bf16():
+    g = np.random.default_rng(12)
+    n, K, S, d = 7, 6, 2, 1000
+    y = g.standard_normal((n, K, d)).astype(np.float32)
+    gates = g.random((n, K)).astype(np.float32)
+    ysh = g.standard_normal((n, S, d)).astype(np.float32)
+    ref = oracle.combine(y.astype(np.float64), gates.astype(np.float64), ysh.astype(np.float64))
+    out = torch.empty(n, d, dtype=torch.float32, device=DEV)
+    L.moe_combine(dev(y), dev(gates), dev(ysh), n, K, S, d, out, L.MOE_F32)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - ref)) <= 1e-5 * (1 + np.max(np.abs(ref)))
+    outb = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+    L.moe_combine(dev(y), dev(gates), dev(ysh), n, K, S, d, outb, L.MOE_BF16)
+    gotb = outb.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(gotb - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
