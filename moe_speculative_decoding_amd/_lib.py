@@ -106,7 +106,10 @@ def make_shape(E: int, K: int, d: int, f: int, S: int, w_dtype: str, x_dtype: st
 
 def make_weights(**tensors) -> moe_weights:
     w = moe_weights()
+    fields = {f[0] for f in moe_weights._fields_}
     for k, v in tensors.items():
+        if k not in fields:
+            raise KeyError("moe_weights has no field %r" % k)
         setattr(w, k, ptr(v))
     return w
 

@@ -34,8 +34,8 @@ class DeviceLayer:
         self.routed = routed
         self.shared = shared or {}
         kw = {k: routed.get(k) for k in ROUTED}
-        for k in ROUTED:
-            kw["sh_" + k] = self.shared.get(k)
+        for k in ROUTED:  # w_gate -> sh_gate, s_gate -> sh_s_gate
+            kw["sh_" + (k[2:] if k.startswith("w_") else k)] = self.shared.get(k)
         self.weights = L.make_weights(**kw)
 
     @classmethod
