@@ -4,20 +4,24 @@ Workload (default): the OLMoE-shaped layer (E=64, K=8, d=2048, f=1024, bf16
 weights and tokens, fp32 accumulation), Markov-reuse routing with p = 0.5,
 pass sizes n = 1, 2, 4, 8, over `--layers` distinct layers of weights (each
 layer its own 805 MB of experts, so consecutive operations stream different
-weights, as a verify pass through a model does).
+weights, as a verify pass through a model does; 8 layers are 6.4 GB, far
+beyond the 256 MB Infinity Cache).
 
 A step is one verify operation (route -> union -> deduplicating expert FFN
--> combine) for every (n, layer) pair.  The step is captured once in a HIP
-graph and replayed; `value` is union bytes streamed per step over the step
-time (effective HBM GB/s on union bytes, the deduplicating kernel's
-bandwidth definition of the expert-bytes page, Fig. 2).
+-> combine) for every (n, layer) pair, captured once in a HIP graph and
+replayed.  `value` is union bytes streamed per step over the step time
+(effective HBM GB/s on union bytes, the deduplicating kernel's bandwidth
+definition of the expert-bytes page, Fig. 2).
 
-Per-operation detail is measured separately with a cold cache (a 1 GiB
-scrub before every operation, outside the events): the expert FFN of both
-modes alone and the whole operation, timed with HIP events on the stream the
-kernels run on; r(n), u(n), the bytes/bandwidth + fixed-time fit and the
-roofline object come from these.  The CPU baseline times the float64 oracle
-on the host on a bounded sample (one layer, n = 1, 2, 4, 8).
+Per pass size, the expert FFN alone (deduplicating and per-slot) is timed
+the same way: a graph holding that n's calls for every layer, replayed, with
+HIP events on the stream the kernels run on around the replays.  From these
+come u(n), beta_dedup(n) on union bytes, beta_slot(n) on requested bytes,
+r(n) (Table 1 of the expert-bytes page), the bytes/bandwidth + fixed-time
+fit and the roofline object.  `--cold` adds per-operation timings after a
+read-only 1 GiB scrub that evicts L2 and the Infinity Cache.  The CPU
+baseline times the float64 oracle on a bounded sample (one layer, n = 1, 2,
+4, 8, one thread).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--layers 8]
 """
@@ -43,8 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=8)
-    ap.add_argument("--reps", type=int, default=3, help="cold-cache repetitions per operation")
+    ap.add_argument("--reps", type=int, default=20, help="graph replays per FFN timing")
     ap.add_argument("--p", type=float, default=0.5, help="Markov reuse probability")
+    ap.add_argument("--cold", action="store_true", help="also time operations after a scrub")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
     return ap.parse_args()
@@ -72,10 +77,11 @@ def cpu_baseline(cfg, p, budget_s):
             total_bytes += r["union_bytes"]
             total_s += dt
             done.append(n)
-            log("cpu oracle n=%d: %.2f s" % (n, dt))
+            log("cpu oracle n=%d: %.3f s" % (n, dt))
             if total_s > budget_s:
                 break
-    return {"value": total_bytes / total_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
             "sample": "float64 numpy oracle, dedup mode, one OLMoE-shaped layer, Markov p=%s, "
                       "n in %s (route+union+FFN+combine incl. weight decode), one thread"
                       % (p, done)}
@@ -104,6 +110,7 @@ def main():
     ns = (1, 2, 4, 8)
     routing = "markov:%s" % args.p
     stream = torch.cuda.current_stream()
+    DEDUP, SLOT = L.MOE_MODE_DEDUP, L.MOE_MODE_PERSLOT
 
     log("generating %d layers of %s weights on the device" % (args.layers, cfg.name))
     layers = []
@@ -122,13 +129,13 @@ def main():
 
     # eager pass of both modes: byte counts, and the reference for graph replays
     for op in ops:
-        verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"], op["n"], L.MOE_MODE_DEDUP)
-        verify_pass(layers[op["layer"]], op["buf_slot"], op["x"], op["logits"], op["n"],
-                    L.MOE_MODE_PERSLOT)
+        verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"], op["n"], DEDUP)
+        verify_pass(layers[op["layer"]], op["buf_slot"], op["x"], op["logits"], op["n"], SLOT)
     torch.cuda.synchronize()
     for op in ops:
-        if L.moe_get_error(op["buf"].ws) != L.MOE_OK:
-            raise RuntimeError("device error word set")
+        for b in (op["buf"], op["buf_slot"]):
+            if L.moe_get_error(b.ws) != L.MOE_OK:
+                raise RuntimeError("device error word set")
         b = op["buf"].bytes.cpu().tolist()
         op["U"] = int(op["buf"].U.item())
         op["union_bytes"], op["requested_bytes"] = int(b[0]), int(b[1])
@@ -139,123 +146,139 @@ def main():
             raise RuntimeError("dedup and per-slot outputs differ (rel %.2e)" % rel)
     step_union_bytes = sum(op["union_bytes"] for op in ops)
 
-    # one step captured in a graph
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                fn()
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        return g
+
+    def ffn(op, mode, st=None):
+        lay = layers[op["layer"]]
+        if mode == DEDUP:
+            b = op["buf"]
+            L.moe_expert_ffn_dedup(lay.shape, lay.weights, op["x"], op["n"], b.U, b.union_ids,
+                                   b.offsets, b.perm, b.y_slots, None, b.bytes, b.ws, b.ws_bytes, st)
+        else:
+            b = op["buf_slot"]
+            L.moe_expert_ffn_perslot(lay.shape, lay.weights, op["x"], op["n"], b.ids, b.y_slots,
+                                     None, b.bytes, b.ws, b.ws_bytes, st)
+
+    # ---------------------------------------------------------- the step
     log("capturing one step (%d operations) in a graph" % len(ops))
-    graph = torch.cuda.CUDAGraph()
-    cap_stream = torch.cuda.Stream()
-    cap_stream.wait_stream(stream)
-    with torch.cuda.stream(cap_stream):
-        with torch.cuda.graph(graph, stream=cap_stream):
-            for op in ops:
-                verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"], op["n"],
-                            L.MOE_MODE_DEDUP)
-    stream.wait_stream(cap_stream)
-    torch.cuda.synchronize()
+    g_step = capture(lambda: [verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"],
+                                          op["n"], DEDUP) for op in ops])
     for rep in range(3):  # replays must reproduce the eager results exactly
         for op in ops:
             op["buf"].out.zero_()
         torch.cuda.synchronize()
-        graph.replay()
+        g_step.replay()
         torch.cuda.synchronize()
         for op in ops:
             if not torch.equal(op["buf"].out[:op["n"]], op["out_eager"]):
                 raise RuntimeError("graph replay %d differs from the eager pass" % rep)
-
     for _ in range(args.warmup):
-        graph.replay()
+        g_step.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        graph.replay()
+        g_step.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = step_union_bytes / (ms_per_step * 1e-3) / 1e9
-    log("graph step: %.3f ms, %.1f GB/s on union bytes" % (ms_per_step, value))
+    log("step: %.3f ms, %.1f GB/s on union bytes" % (ms_per_step, value))
 
-    # cold-cache per-operation timing with events on the kernels' stream
-    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    scrub.zero_()
-    rec = []
-    for rep in range(args.reps):
-        for op in ops:
-            lay = layers[op["layer"]]
-            for mode, buf in (("dedup", op["buf"]), ("slot", op["buf_slot"])):
-                scrub.add_(1.0)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                if mode == "dedup":
-                    L.moe_expert_ffn_dedup(lay.shape, lay.weights, op["x"], op["n"], buf.U,
-                                           buf.union_ids, buf.offsets, buf.perm, buf.y_slots, None,
-                                           buf.bytes, buf.ws, buf.ws_bytes, stream)
-                else:
-                    L.moe_expert_ffn_perslot(lay.shape, lay.weights, op["x"], op["n"], buf.ids,
-                                             buf.y_slots, None, buf.bytes, buf.ws, buf.ws_bytes,
-                                             stream)
-                e1.record(stream)
-                scrub.add_(1.0)
-                w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                w0.record(stream)
-                verify_pass(lay, buf, op["x"], op["logits"], op["n"],
-                            L.MOE_MODE_DEDUP if mode == "dedup" else L.MOE_MODE_PERSLOT, stream)
-                w1.record(stream)
-                rec.append((op, mode, e0, e1, w0, w1))
-    torch.cuda.synchronize()
-    for op in ops:
-        op.setdefault("t_ffn", {"dedup": [], "slot": []})
-        op.setdefault("t_op", {"dedup": [], "slot": []})
-    for op, mode, e0, e1, w0, w1 in rec:
-        op["t_ffn"][mode].append(e0.elapsed_time(e1) * 1e-3)
-        op["t_op"][mode].append(w0.elapsed_time(w1) * 1e-3)
+    # -------------------------------------------- FFN alone, per n and mode
+    def time_graph(g, calls):
+        for _ in range(2):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (args.reps * calls)
 
-    detail = {}
-    fit_rows = {"dedup": ([], []), "slot": ([], [])}
-    agg_all = []
+    per_n = {}
     for n in ns:
         sel = [op for op in ops if op["n"] == n]
-        rows = []
-        for op in sel:
-            td = float(np.median(op["t_ffn"]["dedup"]))
-            ts = float(np.median(op["t_ffn"]["slot"]))
-            rows.append({"union_bytes": op["union_bytes"], "requested_bytes": op["requested_bytes"],
-                         "t_dedup": td, "t_slot": ts})
-            fit_rows["dedup"][0].append(op["union_bytes"]); fit_rows["dedup"][1].append(td)
-            fit_rows["slot"][0].append(op["requested_bytes"]); fit_rows["slot"][1].append(ts)
-        agg_all.extend(rows)
-        a = cm.aggregate(rows)
-        t_op = float(np.mean([np.median(op["t_op"]["dedup"]) for op in sel]))
+        t = {}
+        for mode in (DEDUP, SLOT):
+            g = capture(lambda: [ffn(op, mode) for op in sel])
+            t[mode] = time_graph(g, len(sel))
+            del g
+        ub = sum(op["union_bytes"] for op in sel) / len(sel)
+        rb = sum(op["requested_bytes"] for op in sel) / len(sel)
+        per_n[n] = {"t_dedup": t[DEDUP], "t_slot": t[SLOT], "union_bytes": ub,
+                    "requested_bytes": rb, "U": float(np.mean([op["U"] for op in sel]))}
+
+    # whole operation per n (graph of that n's operations)
+    for n in ns:
+        sel = [op for op in ops if op["n"] == n]
+        g = capture(lambda: [verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"],
+                                         op["n"], DEDUP) for op in sel])
+        per_n[n]["t_op"] = time_graph(g, len(sel))
+        del g
+
+    detail = {}
+    for n in ns:
+        a = cm.aggregate([per_n[n]])
         detail["n=%d" % n] = {
-            "U_mean": float(np.mean([op["U"] for op in sel])),
-            "u": round(a["u"], 4),
-            "us_ffn_dedup": round(1e6 * float(np.mean([r["t_dedup"] for r in rows])), 2),
-            "us_ffn_perslot": round(1e6 * float(np.mean([r["t_slot"] for r in rows])), 2),
-            "us_op_dedup": round(1e6 * t_op, 2),
+            "U_mean": round(per_n[n]["U"], 3), "u": round(a["u"], 4),
+            "us_op_dedup": round(1e6 * per_n[n]["t_op"], 2),
+            "us_ffn_dedup": round(1e6 * per_n[n]["t_dedup"], 2),
+            "us_ffn_perslot": round(1e6 * per_n[n]["t_slot"], 2),
             "GBs_dedup_union": round(a["beta_dedup"] / 1e9, 1),
             "GBs_perslot_requested": round(a["beta_slot"] / 1e9, 1),
             "pct_peak_dedup": round(100 * a["beta_dedup"] / 1e9 / PEAK_GBS, 1),
-            "r": round(a["r"], 4),
-            "dedup_faster": cm.dedup_faster(a["u"], a["r"]),
+            "r": round(a["r"], 4), "dedup_faster": cm.dedup_faster(a["u"], a["r"]),
+            "saving_us": round(1e6 * a["saving"], 2),
         }
         log("n=%d %s" % (n, json.dumps(detail["n=%d" % n])))
     fit = {}
-    for mode, (b, t) in fit_rows.items():
-        beta, t0_ = cm.fit_bandwidth(b, t)
+    for mode, bkey, tkey in (("dedup", "union_bytes", "t_dedup"), ("slot", "requested_bytes", "t_slot")):
+        beta, t0_ = cm.fit_bandwidth([per_n[n][bkey] for n in ns], [per_n[n][tkey] for n in ns])
         fit[mode] = {"GBs": round(beta / 1e9, 1), "t0_us": round(t0_ * 1e6, 2)}
-    rr = cm.fit_reread([op["U"] for op in ops], [op["n"] * cfg.K for op in ops],
-                       layers[0].expert_bytes(), [r["t_slot"] for r in agg_all])
+    rr = cm.fit_reread([per_n[n]["U"] for n in ns], [n * cfg.K for n in ns],
+                       layers[0].expert_bytes(), [per_n[n]["t_slot"] for n in ns])
     fit["slot_reread_cost"] = round(rr["reread_cost"], 3)
+    fit["crossover_n"] = cm.crossover(ns, [per_n[n]["t_slot"] - per_n[n]["t_dedup"] for n in ns])
 
-    tot_bytes = sum(r["union_bytes"] for r in agg_all)
-    tot_t = sum(r["t_dedup"] for r in agg_all)
-    achieved = tot_bytes / tot_t / 1e9
+    tot_b = sum(per_n[n]["union_bytes"] for n in ns)
+    tot_t = sum(per_n[n]["t_dedup"] for n in ns)
+    achieved = tot_b / tot_t / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
-                "kernel": "expert FFN, deduplicating (up + down kernels), cold cache",
+                "kernel": "moe_expert_ffn_dedup (ffn_stream_kernel up + down), mean over n=1,2,4,8",
                 "bytes_per_launch": "(U + S) * 3*d*f*2 B"}
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(cfg, args.p, args.cpu_seconds)
+    cold = None
+    if args.cold:
+        scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        rec = []
+        for op in ops:
+            for mode in (DEDUP, SLOT):
+                float(scrub.sum())  # read-only eviction of L2 and the Infinity Cache
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                ffn(op, mode)
+                e1.record(stream)
+                rec.append((op["n"], mode, e0, e1))
+        torch.cuda.synchronize()
+        cold = {}
+        for n in ns:
+            for mode, name in ((DEDUP, "us_ffn_dedup"), (SLOT, "us_ffn_perslot")):
+                v = [e0.elapsed_time(e1) * 1e3 for (nn, m, e0, e1) in rec if nn == n and m == mode]
+                cold.setdefault("n=%d" % n, {})[name] = round(float(np.median(v)), 2)
+        log("cold (event-timed, includes ~6 us of dispatch): %s" % json.dumps(cold))
+
+    cpu = None if args.no_cpu else cpu_baseline(cfg, args.p, args.cpu_seconds)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -268,6 +291,8 @@ def main():
                    "global_batch": sum(ns) * args.layers, "seq_len": 1, "parallelism": "none"},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fit": fit,
     }
+    if cold is not None:
+        line["cold"] = cold
     print(json.dumps(line), flush=True)
 
 

@@ -14,7 +14,8 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_verify.so")
+# MOE_VERIFY_LIB may name another build of the same library (same ABI)
+LIB_PATH = os.environ.get("MOE_VERIFY_LIB") or os.path.join(_HERE, "libmoe_verify.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, 1, 2, 3
 MOE_ERR_HIP, MOE_ERR_BAD_IDS, MOE_ERR_TIMEOUT = 4, 5, 6

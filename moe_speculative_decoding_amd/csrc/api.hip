@@ -106,6 +106,7 @@ moe::FfnParams make_params(const moe_shape* s, const moe_weights* w, const void*
   p.shs[2] = w->sh_s_down;
   p.x = static_cast<const uint8_t*>(x);
   p.err = static_cast<uint32_t*>(ws);
+  p.zeros = static_cast<const uint8_t*>(ws) + moe::kZeroOffset;
   p.H = static_cast<uint8_t*>(ws) + kCtrlBytes;
   p.y_slots = y_slots;
   p.y_shared = y_shared;

@@ -20,9 +20,11 @@ enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
 enum { MODE_DEDUP = 0, MODE_PERSLOT = 1 };
 enum : uint32_t { ERRBIT_BAD_IDS = 1u, ERRBIT_TIMEOUT = 2u };
 
-// Workspace: [0, kCtrlBytes) control words (error word first), then the
+// Workspace: [0, kCtrlBytes) control words (error word first; bytes
+// [kZeroOffset, kZeroOffset + 16) are never written and stay zero), then the
 // intermediate activations H [n*(K+S)][f] in the token storage type.
 constexpr size_t kCtrlBytes = 256;
+constexpr size_t kZeroOffset = 128;
 
 // ----------------------------------------------------------------- loads
 __device__ __forceinline__ u32x4 ld16(const void* p) {
@@ -70,6 +72,7 @@ struct FfnParams {
   const int32_t* perm;
   const int32_t* ids;     // per-slot: [n][K]
   uint32_t* err;          // error word (workspace)
+  const uint8_t* zeros;   // 16 zero bytes inside the workspace control block
   uint64_t* bytes;        // [2] or null
   unsigned long long expert_bytes;
   int n, K, S, E, d, f;

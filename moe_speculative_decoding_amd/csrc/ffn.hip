@@ -25,6 +25,9 @@
 // 16 codes.  Partial sums are combined across the wavefront by recursive
 // halving (each shuffle stage halves the values per lane), so a wave reduces
 // R*T values with about R*T shuffles instead of 6*R*T.
+#include <map>
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -151,57 +154,36 @@ struct Group {
   int s_idx;   // shared expert index (dedup) or (token * S + s) pair (per-slot)
 };
 
-__device__ __forceinline__ bool group_of(const FfnParams& p, int g, Group& G, bool report) {
-  if (p.mode == MODE_DEDUP) {
-    if (g < p.ucap) {
-      const int U = *p.U;
-      if (U < 0) {
-        if (report) atomicOr(p.err, ERRBIT_BAD_IDS);
-        return false;
-      }
-      if (g >= U) return false;
-      G.e = p.union_ids[g];
-      G.shared = 0;
-      G.first = p.offsets[g];
-      G.cnt = p.offsets[g + 1] - G.first;
-      G.s_idx = 0;
-      return G.cnt > 0;
-    }
-    const int s = g - p.ucap;
-    if (s >= p.S) return false;
-    G.e = s;
-    G.shared = 1;
-    G.first = 0;
-    G.cnt = p.n;
-    G.s_idx = s;
-    return true;
-  }
+// ------------------------------------------------------ routing metadata
+// The union arrays (dedup) or the slot ids (per-slot) are copied to LDS once
+// per workgroup before the stream starts: loads issued later would complete
+// in order behind the weight prefetch, so reading them from global memory in
+// the loop would drain the prefetch every time.
+constexpr int kMaxSlots = 256;  // n*K <= 32*8
+struct Meta {
+  int a[kMaxSlots + 1];  // dedup: offsets[0..cap]; per-slot: ids[0..nK)
+  int b[kMaxSlots];      // dedup: union_ids[0..cap)
+  int c[kMaxSlots];      // dedup: perm[0..nK)
+};
+
+__device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
   const int nk = p.n * p.K;
-  if (g < nk) {
-    G.e = p.ids[g];
-    G.shared = 0;
-    G.first = g;
-    G.cnt = 1;
-    G.s_idx = 0;
-    return true;
+  if (p.mode == MODE_DEDUP) {
+    for (int i = threadIdx.x; i <= p.ucap; i += kBlock) m.a[i] = p.offsets[i];
+    for (int i = threadIdx.x; i < p.ucap; i += kBlock) m.b[i] = p.union_ids[i];
+    for (int i = threadIdx.x; i < nk; i += kBlock) m.c[i] = p.perm[i];
+  } else {
+    for (int i = threadIdx.x; i < nk; i += kBlock) m.a[i] = p.ids[i];
   }
-  const int q = g - nk;
-  if (q >= p.n * p.S) return false;
-  G.e = q % p.S;
-  G.shared = 1;
-  G.first = q;
-  G.cnt = 1;
-  G.s_idx = q;
-  return true;
 }
 
 // token j of a group: its row in x, its row in H and its output row
-__device__ __forceinline__ void token_of(const FfnParams& p, const Group& G, int j, int& xrow,
-                                         int& hrow, float*& yrow) {
+__device__ __forceinline__ void token_of(const FfnParams& p, const Meta& mt, const Group& G, int j,
+                                         int& xrow, int& hrow, float*& yrow) {
   const int nk = p.n * p.K;
   if (p.mode == MODE_DEDUP) {
     if (!G.shared) {
-      const int slot = p.perm[G.first + j];
+      const int slot = mt.c[G.first + j];
       xrow = slot / p.K;
       hrow = G.first + j;
       yrow = p.y_slots + static_cast<size_t>(slot) * p.d;
@@ -223,241 +205,465 @@ __device__ __forceinline__ void token_of(const FfnParams& p, const Group& G, int
   }
 }
 
-// ------------------------------------------------------------- main tile
-// Wave-level product of R stored rows of NMAT matrices (each Kdim long) with
-// up to TC token vectors staged chunk by chunk in LDS.  acc[(m*R + r)*TC + tt].
-// All waves of the workgroup must call it together (it holds barriers).
-template <int WT, int TC, int R, int NMAT, bool FROM_H>
-__device__ __forceinline__ void rows_times_tokens(
-    const FfnParams& p, const Group& G, int tile, int nt, const uint8_t* const (&Wrow)[NMAT],
-    const float* const (&Srow)[NMAT], int rv, int Kdim, uint8_t* xs, float* acc) {
+// ------------------------------------------------------------ the walk
+// One phase (up: gate/up rows, or down rows) is a list of units: (group g,
+// row block of 4*R rows), groups in order, row blocks in order.  Workgroup b
+// owns the contiguous unit range [b*NU/G, (b+1)*NU/G), so every workgroup
+// streams the same number of bytes and all finish together.  It walks its
+// range chunk by chunk (K split in chunks of SPC load steps): for each group
+// segment, for each token tile of that group, for each unit, for each chunk.
+// The walk is the same for every lane of the workgroup.
+struct Walk {
+  int g, tile, u, kc, done;
+  int ntile, seg_lo, seg_hi;
+  int valid;  // expert id in range
+  Group G;
+};
+
+// group g of a phase: dedup 0..U-1 routed union experts, then the S shared;
+// per-slot 0..n*K-1 slots, then the n*S (token, shared expert) pairs
+__device__ __forceinline__ void group_at(const FfnParams& p, const Meta& mt, int U, int g,
+                                         Group& G) {
+  if (p.mode == MODE_DEDUP) {
+    if (g < U) {
+      G.e = mt.b[g];
+      G.shared = 0;
+      G.first = mt.a[g];
+      G.cnt = mt.a[g + 1] - G.first;
+      G.s_idx = 0;
+    } else {
+      G.e = g - U;
+      G.shared = 1;
+      G.first = 0;
+      G.cnt = p.n;
+      G.s_idx = g - U;
+    }
+    return;
+  }
+  const int nk = p.n * p.K;
+  if (g < nk) {
+    G.e = mt.a[g];
+    G.shared = 0;
+    G.first = g;
+    G.cnt = 1;
+    G.s_idx = 0;
+  } else {
+    const int q = g - nk;
+    G.e = q % p.S;
+    G.shared = 1;
+    G.first = q;
+    G.cnt = 1;
+    G.s_idx = q;
+  }
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int TC>
+__device__ __forceinline__ void walk_group(const FfnParams& p, const Meta& mt, int U, Walk& w,
+                                           int g, long long lo, long long hi, int upg) {
+  // every field is the same in all lanes: keep the walk in scalar registers
+  w.g = uni(g);
+  group_at(p, mt, U, w.g, w.G);
+  w.G.e = uni(w.G.e);
+  w.G.shared = uni(w.G.shared);
+  w.G.cnt = uni(w.G.cnt);
+  w.G.first = uni(w.G.first);
+  w.G.s_idx = uni(w.G.s_idx);
+  w.valid = w.G.shared || (w.G.e >= 0 && w.G.e < p.E);
+  w.ntile = (w.G.cnt + TC - 1) / TC;
+  w.tile = 0;
+  const long long glo = static_cast<long long>(g) * upg;
+  w.seg_lo = uni(static_cast<int>(lo > glo ? lo : glo));
+  w.seg_hi = uni(static_cast<int>(hi < glo + upg ? hi : glo + upg));
+  w.u = w.seg_lo;
+  w.kc = 0;
+}
+
+template <int TC>
+__device__ __forceinline__ void walk_next(const FfnParams& p, const Meta& mt, int U, Walk& w,
+                                          int nchunks, long long lo, long long hi, int upg) {
+  if (++w.kc < nchunks) return;
+  w.kc = 0;
+  if (++w.u < w.seg_hi) return;
+  if (++w.tile < w.ntile) {
+    w.u = w.seg_lo;
+    return;
+  }
+  if (w.seg_hi >= hi) {
+    w.done = 1;
+    return;
+  }
+  walk_group<TC>(p, mt, U, w, w.g + 1, lo, hi, upg);
+}
+
+// ------------------------------------------------------- streaming kernel
+// UP (NMAT = 2): rows j of W_gate and W_up (Kdim = d) -> H[token][j] = silu(a) * v.
+// DOWN (NMAT = 1): rows c of W_down (Kdim = f, tokens read from H) -> y[slot][c].
+// Each wave owns R rows of the current unit; the weights of the next chunk
+// are in flight while the current chunk is multiplied (two register buffers).
+template <int WT, int TC, int R, int NMAT, int SPC>
+struct StreamCfg {
   using T = WTraits<WT>;
-  constexpr int STEP = kWave * T::VEC;
-  constexpr int KC = T::SPC * STEP;
-  constexpr int VPT = KC * T::XB / 16;  // 16-byte vectors per staged token chunk
-  const int lane = threadIdx.x & 63;
+  static constexpr int STEP = kWave * T::VEC;  // elements per load step
+  static constexpr int CH = SPC * STEP;        // elements per chunk
+  static constexpr int V = NMAT * R * TC;      // partial sums per lane
+  static constexpr int SH = 6 - ilog2(V);
+  static_assert((V & (V - 1)) == 0 && V <= 64, "values per lane must be a power of two <= 64");
+  static_assert(NMAT == 1 || V >= 2, "gate/up pairing needs two values");
+};
+
+template <int WT, int TC, int R, int NMAT, int SPC>
+__device__ __forceinline__ void load_chunk(const FfnParams& p, const Walk& w, int rows, int Kdim,
+                                           int upg, int lane, int wave,
+                                           u32x4 (&buf)[NMAT][SPC][R], float (&sc)[NMAT][SPC]) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  using T = typename C::T;
+  // Every lane issues every load, outside any branch, and nothing inspects the
+  // loaded value before the multiply, so the next chunk stays in flight while
+  // the current one is used.  Masked lanes read 16 zero bytes of the
+  // workspace's control block instead of weights.
+  const int r0 = (w.u - w.g * upg) * (kBlock / kWave) * R + wave * R;
+  const int rv = (w.valid && !w.done) ? max(0, min(R, rows - r0)) : 0;
   const size_t row_bytes = static_cast<size_t>(Kdim) * T::EB;
-
+  const size_t mat = static_cast<size_t>(rows) * row_bytes;
+  const int kb = Kdim / 128;
+  const int e = rv > 0 ? w.G.e : 0;
 #pragma unroll
-  for (int i = 0; i < NMAT * R * TC; ++i) acc[i] = 0.0f;
+  for (int m = 0; m < NMAT; ++m) {
+    const int mi = NMAT == 1 ? 2 : m;
+    const uint8_t* base = (w.G.shared ? p.shw[mi] : p.w[mi]) + static_cast<size_t>(e) * mat +
+                          static_cast<size_t>(r0) * row_bytes;
+    const float* sbase = nullptr;
+    if (WT == WT_FP8)
+      sbase = (w.G.shared ? p.shs[mi] : p.s[mi]) +
+              (static_cast<size_t>(e) * (rows / 128) + (rv > 0 ? r0 / 128 : 0)) * kb;
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+      const int k = w.kc * C::CH + s * C::STEP + lane * T::VEC;
+      const bool kin = k < Kdim;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool ok = kin && r < rv;
+        const uint8_t* a = ok ? base + static_cast<size_t>(r) * row_bytes +
+                                    static_cast<size_t>(k) * T::EB
+                              : p.zeros;
+        // streamed once: non-temporal, so the weights do not evict tokens,
+        // H and routing data from the caches (measured: +13% bandwidth)
+        buf[m][s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+      }
+      if (WT == WT_FP8) {
+        const bool ok = kin && rv > 0;
+        sc[m][s] = *(ok ? sbase + (k >> 7) : reinterpret_cast<const float*>(p.zeros));
+      }
+    }
+  }
+}
 
-  for (int kc = 0; kc < Kdim; kc += KC) {
-    // weights of this chunk first, so their latency overlaps the staging
-    u32x4 wv[NMAT][T::SPC][R];
-    float sc[NMAT][T::SPC];
+template <int WT, int TC, int R, int NMAT, int SPC, int NT>
+__device__ __forceinline__ void mul_chunk_nt(int kc, int Kpad, int lane, const uint8_t* xs,
+                                             const u32x4 (&buf)[NMAT][SPC][R],
+                                             const float (&sc)[NMAT][SPC], float* acc) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  using T = typename C::T;
+#pragma unroll
+  for (int s = 0; s < SPC; ++s) {
+    const int k = kc * C::CH + s * C::STEP + lane * T::VEC;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
 #pragma unroll
-      for (int s = 0; s < T::SPC; ++s) {
-        const int k = kc + s * STEP + lane * T::VEC;
-        const bool kin = k < Kdim;
+      for (int r = 0; r < R; ++r) {
+        const typename Dot<WT>::W wt = Dot<WT>::prep(buf[m][s][r]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          wv[m][s][r] = (kin && r < rv)
-                            ? ld16(Wrow[m] + static_cast<size_t>(r) * row_bytes +
-                                   static_cast<size_t>(k) * T::EB)
-                            : u32x4{0u, 0u, 0u, 0u};
-        }
-        sc[m][s] = (WT == WT_FP8 && kin && rv > 0) ? Srow[m][k >> 7] : 0.0f;
-      }
-    }
-    __syncthreads();  // everyone is done reading the previous chunk
-    for (int v = threadIdx.x; v < TC * VPT; v += kBlock) {
-      const int tt = v / VPT;
-      const int c = v - tt * VPT;
-      const int k = kc + c * (16 / T::XB);
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (tt < nt && k < Kdim) {
-        int xrow, hrow;
-        float* yrow;
-        token_of(p, G, tile + tt, xrow, hrow, yrow);
-        const uint8_t* src = FROM_H ? p.H + static_cast<size_t>(hrow) * Kdim * T::XB
-                                    : p.x + static_cast<size_t>(xrow) * Kdim * T::XB;
-        val = ld16(src + static_cast<size_t>(k) * T::XB);
-      }
-      st16(xs + static_cast<size_t>(tt) * KC * T::XB + c * 16, val);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < T::SPC; ++s) {
-      const int kl = s * STEP + lane * T::VEC;  // element offset within the chunk
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const typename Dot<WT>::W w = Dot<WT>::prep(wv[m][s][r]);
-#pragma unroll
-          for (int tt = 0; tt < TC; ++tt) {
-            if (tt < nt) {
-              const uint8_t* xp = xs + (static_cast<size_t>(tt) * KC + kl) * T::XB;
-              float& a = acc[(m * R + r) * TC + tt];
-              a = Dot<WT>::run(w, xp, a, sc[m][s]);
-            }
-          }
+        for (int tt = 0; tt < NT; ++tt) {
+          float& a = acc[(m * R + r) * TC + tt];
+          a = Dot<WT>::run(wt, xs + (static_cast<size_t>(tt) * Kpad + k) * T::XB, a,
+                           WT == WT_FP8 ? sc[m][s] : 0.0f);
         }
       }
     }
   }
 }
 
-// -------------------------------------------------------------- kernel 1
-// grid.x: blocks of 4*R intermediate rows j; grid.y: groups.
-template <int WT, int TC, int R>
-__global__ __launch_bounds__(kBlock) void ffn_up_kernel(FfnParams p) {
+// all TC staged tokens are multiplied: tokens beyond the tile's count are
+// zero in LDS, and a branch on the count would cost the prefetch pipeline
+template <int WT, int TC, int R, int NMAT, int SPC>
+__device__ __forceinline__ void mul_chunk(int kc, int Kpad, int lane, const uint8_t* xs,
+                                          const u32x4 (&buf)[NMAT][SPC][R],
+                                          const float (&sc)[NMAT][SPC], float* acc) {
+  mul_chunk_nt<WT, TC, R, NMAT, SPC, TC>(kc, Kpad, lane, xs, buf, sc, acc);
+}
+
+// tokens of (group, tile) -> LDS [TC][Kpad], zero beyond Kdim and beyond the
+// tile; the H row and output row of every token go to LDS too, so the
+// epilogue issues no global loads
+template <int WT, int TC, bool FROM_H>
+__device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt, const Walk& w,
+                                             int Kdim, int Kpad, uint8_t* xs, int* tok_h,
+                                             float** tok_y) {
   using T = WTraits<WT>;
-  constexpr int KC = T::SPC * kWave * T::VEC;
-  constexpr int V = 2 * R * TC;
-  static_assert((V & (V - 1)) == 0 && V <= 64, "values per lane must be a power of two <= 64");
-  __shared__ __attribute__((aligned(16))) uint8_t xs[TC * KC * T::XB];
-  __shared__ float red[kBlock / kWave][V];
-
-  Group G;
-  if (!group_of(p, blockIdx.y, G, blockIdx.x == 0 && threadIdx.x == 0)) return;
-  if (!G.shared && (G.e < 0 || G.e >= p.E)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
-    return;
+  constexpr int EPV = 16 / T::XB;  // elements per 16-byte vector
+  const int vpt = Kpad / EPV;
+  const int nt = min(TC, w.G.cnt - w.tile * TC);
+  if (threadIdx.x < TC) {
+    int xrow = 0, hrow = 0;
+    float* yrow = nullptr;
+    if (static_cast<int>(threadIdx.x) < nt) token_of(p, mt, w.G, w.tile * TC + threadIdx.x, xrow, hrow, yrow);
+    tok_h[threadIdx.x] = hrow;
+    tok_y[threadIdx.x] = yrow;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rows = p.f, Kdim = p.d;
-  const int r0 = (blockIdx.x * (kBlock / kWave) + wave) * R;
-  const int rv = max(0, min(R, rows - r0));
-  const size_t mat = static_cast<size_t>(rows) * Kdim * T::EB;
-  const size_t row_bytes = static_cast<size_t>(Kdim) * T::EB;
-  const uint8_t* w0 = G.shared ? p.shw[0] : p.w[0];
-  const uint8_t* w1 = G.shared ? p.shw[1] : p.w[1];
-  const uint8_t* const Wrow[2] = {
-      w0 + static_cast<size_t>(G.e) * mat + static_cast<size_t>(r0) * row_bytes,
-      w1 + static_cast<size_t>(G.e) * mat + static_cast<size_t>(r0) * row_bytes};
-  const int kb = Kdim / 128;
-  const size_t sexp = static_cast<size_t>(rows / 128) * kb;
-  const size_t soff = static_cast<size_t>(G.e) * sexp + static_cast<size_t>(r0 / 128) * kb;
-  const float* const Srow[2] = {
-      WT == WT_FP8 ? (G.shared ? p.shs[0] : p.s[0]) + soff : nullptr,
-      WT == WT_FP8 ? (G.shared ? p.shs[1] : p.s[1]) + soff : nullptr};
+  for (int v = threadIdx.x; v < TC * vpt; v += kBlock) {
+    const int tt = v / vpt;
+    const int k = (v - tt * vpt) * EPV;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (tt < nt && k < Kdim) {
+      int xrow, hrow;
+      float* yrow;
+      token_of(p, mt, w.G, w.tile * TC + tt, xrow, hrow, yrow);
+      const uint8_t* src = FROM_H ? p.H + static_cast<size_t>(hrow) * Kdim * T::XB
+                                  : p.x + static_cast<size_t>(xrow) * Kdim * T::XB;
+      val = ld16(src + static_cast<size_t>(k) * T::XB);
+    }
+    st16(xs + static_cast<size_t>(v) * 16, val);
+  }
+}
 
-  for (int tile = 0; tile < G.cnt; tile += TC) {
-    const int nt = min(TC, G.cnt - tile);
-    float acc[V];
-    rows_times_tokens<WT, TC, R, 2, false>(p, G, tile, nt, Wrow, Srow, rv, Kdim, xs, acc);
-    Halve<V>::run(acc, lane, 32);
-    constexpr int SH = 6 - ilog2(V);
-    if ((lane & ((1 << SH) - 1)) == 0) red[wave][lane >> SH] = acc[0];
-    __syncthreads();
-    if (lane < R * TC) {
-      const int r = lane / TC, tt = lane - (lane / TC) * TC;
+template <int WT, int TC, int R, int NMAT, int SPC>
+__device__ __forceinline__ void finish_unit(const FfnParams& p, const Walk& w, int rows, int upg,
+                                            int lane, int wave, const int* tok_h,
+                                            float* const* tok_y, float* acc) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  Halve<C::V>::run(acc, lane, 32);
+  const int r0 = (w.u - w.g * upg) * (kBlock / kWave) * R + wave * R;
+  const int rv = max(0, min(R, rows - r0));
+  const int nt = min(TC, w.G.cnt - w.tile * TC);
+  if (NMAT == 2) {
+    const float v = __shfl_xor(acc[0], 32);  // the up value pairs with this gate value
+    if (lane < 32 && (lane & ((1 << C::SH) - 1)) == 0) {
+      const int idx = lane >> C::SH;
+      const int r = idx / TC, tt = idx - (idx / TC) * TC;
       if (r < rv && tt < nt) {
-        const float a = red[wave][(0 * R + r) * TC + tt];
-        const float v = red[wave][(1 * R + r) * TC + tt];
+        const float a = acc[0];
         const float h = a / (1.0f + expf(-a)) * v;
-        int xrow, hrow;
-        float* yrow;
-        token_of(p, G, tile + tt, xrow, hrow, yrow);
-        const size_t off = static_cast<size_t>(hrow) * rows + r0 + r;
-        if (T::XB == 4) {
+        const size_t off = static_cast<size_t>(tok_h[tt]) * rows + r0 + r;
+        if (WTraits<WT>::XB == 4) {
           reinterpret_cast<float*>(p.H)[off] = h;
         } else {
           reinterpret_cast<uint16_t*>(p.H)[off] = f32_to_bf16_bits(h);
         }
       }
     }
-    // the next tile's first barrier orders red[] reuse
+  } else {
+    if ((lane & ((1 << C::SH) - 1)) == 0) {
+      const int idx = lane >> C::SH;
+      const int r = idx / TC, tt = idx - (idx / TC) * TC;
+      if (r < rv && tt < nt) tok_y[tt][r0 + r] = acc[0];
+    }
   }
+#pragma unroll
+  for (int i = 0; i < C::V; ++i) acc[i] = 0.0f;
 }
 
-// -------------------------------------------------------------- kernel 2
-// grid.x: blocks of 4*R output rows c; grid.y: groups.
-template <int WT, int TC, int R>
-__global__ __launch_bounds__(kBlock) void ffn_down_kernel(FfnParams p) {
-  using T = WTraits<WT>;
-  constexpr int KC = T::SPC * kWave * T::VEC;
-  constexpr int V = R * TC;
-  static_assert((V & (V - 1)) == 0 && V <= 64, "values per lane must be a power of two <= 64");
-  __shared__ __attribute__((aligned(16))) uint8_t xs[TC * KC * T::XB];
-  __shared__ float red[kBlock / kWave][V];
+template <int WT, int TC, int R, int NMAT, int SPC>
+__global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  constexpr bool UP = NMAT == 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  __shared__ int tok_h[TC];
+  __shared__ float* tok_y[TC];
+  __shared__ Meta mt;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = UP ? p.f : p.d;
+  const int Kdim = UP ? p.d : p.f;
+  const int nchunks = (Kdim + C::CH - 1) / C::CH;
+  const int Kpad = nchunks * C::CH;
+  const int upg = (rows + (kBlock / kWave) * R - 1) / ((kBlock / kWave) * R);
 
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && p.bytes != nullptr) {
+  if (!UP && blockIdx.x == 0 && threadIdx.x == 0 && p.bytes != nullptr) {
     const unsigned long long req =
         static_cast<unsigned long long>(p.n) * (p.K + p.S) * p.expert_bytes;
     unsigned long long got = req;
     if (p.mode == MODE_DEDUP) {
-      const int U = *p.U;
-      got = U < 0 ? 0ull : static_cast<unsigned long long>(U + p.S) * p.expert_bytes;
+      const int U0 = *p.U;
+      got = U0 < 0 ? 0ull : static_cast<unsigned long long>(U0 + p.S) * p.expert_bytes;
     }
     p.bytes[0] = got;
     p.bytes[1] = req;
   }
 
-  Group G;
-  if (!group_of(p, blockIdx.y, G, false)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rows = p.d, Kdim = p.f;
-  const int r0 = (blockIdx.x * (kBlock / kWave) + wave) * R;
-  const int rv = max(0, min(R, rows - r0));
-  if (!G.shared && (G.e < 0 || G.e >= p.E)) {
-    // per-slot slot with an invalid id: defined zero output
-    int xrow, hrow;
-    float* yrow;
-    token_of(p, G, 0, xrow, hrow, yrow);
-    if (lane < rv) yrow[r0 + lane] = 0.0f;
-    return;
-  }
-  const size_t mat = static_cast<size_t>(rows) * Kdim * T::EB;
-  const size_t row_bytes = static_cast<size_t>(Kdim) * T::EB;
-  const uint8_t* w2 = G.shared ? p.shw[2] : p.w[2];
-  const uint8_t* const Wrow[1] = {w2 + static_cast<size_t>(G.e) * mat +
-                                  static_cast<size_t>(r0) * row_bytes};
-  const int kb = Kdim / 128;
-  const size_t sexp = static_cast<size_t>(rows / 128) * kb;
-  const size_t soff = static_cast<size_t>(G.e) * sexp + static_cast<size_t>(r0 / 128) * kb;
-  const float* const Srow[1] = {WT == WT_FP8 ? (G.shared ? p.shs[2] : p.s[2]) + soff : nullptr};
-
-  for (int tile = 0; tile < G.cnt; tile += TC) {
-    const int nt = min(TC, G.cnt - tile);
-    float acc[V];
-    rows_times_tokens<WT, TC, R, 1, true>(p, G, tile, nt, Wrow, Srow, rv, Kdim, xs, acc);
-    Halve<V>::run(acc, lane, 32);
-    constexpr int SH = 6 - ilog2(V);
-    if ((lane & ((1 << SH) - 1)) == 0) red[wave][lane >> SH] = acc[0];
-    __syncthreads();
-    if (lane < R * TC) {
-      const int r = lane / TC, tt = lane - (lane / TC) * TC;
-      if (r < rv && tt < nt) {
-        int xrow, hrow;
-        float* yrow;
-        token_of(p, G, tile + tt, xrow, hrow, yrow);
-        yrow[r0 + r] = red[wave][r * TC + tt];
-      }
+  int U = 0, NG;
+  if (p.mode == MODE_DEDUP) {
+    U = uni(*p.U);
+    if (U < 0) {
+      if (UP && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+      return;
     }
+    NG = U + p.S;
+  } else {
+    NG = p.n * (p.K + p.S);
+  }
+  const long long NU = static_cast<long long>(NG) * upg;
+  const long long lo = NU * blockIdx.x / gridDim.x;
+  const long long hi = NU * (blockIdx.x + 1) / gridDim.x;
+  if (lo >= hi) return;
+
+  load_meta(p, mt);
+  __syncthreads();
+  Walk cur;
+  cur.done = 0;
+  walk_group<TC>(p, mt, U, cur, static_cast<int>(lo / upg), lo, hi, upg);
+  if (UP && !cur.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+
+  u32x4 b0[NMAT][SPC][R], b1[NMAT][SPC][R];
+  float s0[NMAT][SPC], s1[NMAT][SPC];
+  float acc[C::V];
+#pragma unroll
+  for (int i = 0; i < C::V; ++i) acc[i] = 0.0f;
+
+  load_chunk<WT, TC, R, NMAT, SPC>(p, cur, rows, Kdim, upg, lane, wave, b0, s0);
+  stage_tokens<WT, TC, !UP>(p, mt, cur, Kdim, Kpad, xs, tok_h, tok_y);
+  __syncthreads();
+
+  Walk nxt = cur;
+  walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
+  // two chunks per trip so the register buffers keep fixed names
+  while (true) {
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt, rows, Kdim, upg, lane, wave, b1, s1);
+    mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b0, s0, acc);
+    if (cur.kc == nchunks - 1)
+      finish_unit<WT, TC, R, NMAT, SPC>(p, cur, rows, upg, lane, wave, tok_h, tok_y, acc);
+    if (nxt.done) break;
+    if (nxt.g != cur.g || nxt.tile != cur.tile) {
+      if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+      __syncthreads();
+      stage_tokens<WT, TC, !UP>(p, mt, nxt, Kdim, Kpad, xs, tok_h, tok_y);
+      __syncthreads();
+    }
+    cur = nxt;
+    walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
+
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt, rows, Kdim, upg, lane, wave, b0, s0);
+    mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b1, s1, acc);
+    if (cur.kc == nchunks - 1)
+      finish_unit<WT, TC, R, NMAT, SPC>(p, cur, rows, upg, lane, wave, tok_h, tok_y, acc);
+    if (nxt.done) break;
+    if (nxt.g != cur.g || nxt.tile != cur.tile) {
+      if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+      __syncthreads();
+      stage_tokens<WT, TC, !UP>(p, mt, nxt, Kdim, Kpad, xs, tok_h, tok_y);
+      __syncthreads();
+    }
+    cur = nxt;
+    walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
   }
 }
 
 // ------------------------------------------------------------------ launch
-template <int WT, int TC>
-static hipError_t launch_typed(const FfnParams& p, hipStream_t s) {
-  constexpr int R_UP = 2, R_DOWN = 4;
-  const int groups = p.mode == MODE_DEDUP ? p.ucap + p.S : p.n * (p.K + p.S);
-  const int rows_up = (kBlock / kWave) * R_UP;
-  const int rows_down = (kBlock / kWave) * R_DOWN;
-  dim3 g1((p.f + rows_up - 1) / rows_up, groups);
-  dim3 g2((p.d + rows_down - 1) / rows_down, groups);
-  hipLaunchKernelGGL((ffn_up_kernel<WT, TC, R_UP>), g1, dim3(kBlock), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ffn_down_kernel<WT, TC, R_DOWN>), g2, dim3(kBlock), 0, s, p);
+struct OccKey {
+  const void* fn;
+  size_t smem;
+  int dev;
+  bool operator<(const OccKey& o) const {
+    if (fn != o.fn) return fn < o.fn;
+    if (smem != o.smem) return smem < o.smem;
+    return dev < o.dev;
+  }
+};
+
+// resident workgroups of a kernel on the whole device (cached per process)
+static int resident_blocks(const void* fn, size_t smem) {
+  static std::mutex mu;
+  static std::map<OccKey, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> g(mu);
+  const OccKey key{fn, smem, dev};
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, smem) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int total = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  cache[key] = total;
+  return total;
+}
+
+template <int WT, int TC, int R, int NMAT, int SPC>
+static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  constexpr bool UP = NMAT == 2;
+  const int rows = UP ? p.f : p.d;
+  const int Kdim = UP ? p.d : p.f;
+  const int Kpad = (Kdim + C::CH - 1) / C::CH * C::CH;
+  const size_t smem = static_cast<size_t>(TC) * Kpad * C::T::XB;
+  const void* fn = reinterpret_cast<const void*>(&ffn_stream_kernel<WT, TC, R, NMAT, SPC>);
+  const int upg = (rows + (kBlock / kWave) * R - 1) / ((kBlock / kWave) * R);
+  const int groups_max = p.mode == MODE_DEDUP ? p.ucap + p.S : p.n * (p.K + p.S);
+  const long long units_max = static_cast<long long>(groups_max) * upg;
+  long long grid = resident_blocks(fn, smem);
+  if (grid <= 0) return hipErrorInvalidConfiguration;
+#ifdef MOE_TUNE_MAXBPC
+  if (grid > 256LL * MOE_TUNE_MAXBPC) grid = 256LL * MOE_TUNE_MAXBPC;
+#endif
+  if (grid > units_max) grid = units_max;
+  hipLaunchKernelGGL((ffn_stream_kernel<WT, TC, R, NMAT, SPC>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kBlock), smem, s, p);
   return hipGetLastError();
 }
 
+// Tile shape knobs (rows per wave R, load steps per chunk SPC) of the up and
+// down kernels; the defaults are the measured best on MI355X.
+#ifndef MOE_TUNE_RU
+#define MOE_TUNE_RU 2
+#endif
+#ifndef MOE_TUNE_SPCU
+#define MOE_TUNE_SPCU 2
+#endif
+#ifndef MOE_TUNE_RD
+#define MOE_TUNE_RD 4
+#endif
+#ifndef MOE_TUNE_SPCD
+#define MOE_TUNE_SPCD 2
+#endif
+
+template <int WT, int TC>
+static hipError_t launch_pair(const FfnParams& p, hipStream_t s) {
+  // up: R rows of W_gate and W_up per wave; down: R rows of W_down per wave
+  constexpr int RU = WT == WT_FP8 ? 4 : MOE_TUNE_RU;
+  constexpr int SPCU = WT == WT_FP8 ? 1 : MOE_TUNE_SPCU;
+  constexpr int RD = MOE_TUNE_RD;
+  constexpr int SPCD = WT == WT_FP8 ? 1 : MOE_TUNE_SPCD;
+  hipError_t e = launch_phase<WT, TC, RU, 2, SPCU>(p, s);
+  if (e != hipSuccess) return e;
+  return launch_phase<WT, TC, RD, 1, SPCD>(p, s);
+}
+
+// token tile: a group serves at most n tokens (a token names an expert once),
+// so the tile is the next power of two of min(n, 8); larger groups (shared
+// experts of a long pass, trees) take several tiles
+static int token_tile(const FfnParams& p) {
+  if (p.mode == MODE_PERSLOT) return 1;
+  const int n = p.n;
+  return n >= 5 ? 8 : (n >= 3 ? 4 : (n == 2 ? 2 : 1));
+}
+
+template <int WT>
+static hipError_t launch_typed(const FfnParams& p, hipStream_t s) {
+  switch (token_tile(p)) {
+    case 1: return launch_pair<WT, 1>(p, s);
+    case 2: return launch_pair<WT, 2>(p, s);
+    case 4: return launch_pair<WT, 4>(p, s);
+    default: return launch_pair<WT, 8>(p, s);
+  }
+}
+
 hipError_t launch_expert_ffn(const FfnParams& p, int w_dtype, hipStream_t s) {
-  const bool dedup = p.mode == MODE_DEDUP;
   switch (w_dtype) {
-    case WT_F32:
-      return dedup ? launch_typed<WT_F32, 8>(p, s) : launch_typed<WT_F32, 1>(p, s);
-    case WT_BF16:
-      return dedup ? launch_typed<WT_BF16, 8>(p, s) : launch_typed<WT_BF16, 1>(p, s);
-    case WT_FP8:
-      return dedup ? launch_typed<WT_FP8, 8>(p, s) : launch_typed<WT_FP8, 1>(p, s);
-    default:
-      return hipErrorInvalidValue;
+    case WT_F32: return launch_typed<WT_F32>(p, s);
+    case WT_BF16: return launch_typed<WT_BF16>(p, s);
+    case WT_FP8: return launch_typed<WT_FP8>(p, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
