@@ -117,6 +117,14 @@ moe_status moe_build_union(const int32_t* ids, int32_t n, int32_t K, int32_t E,
                            int32_t* U, int32_t* union_ids, int32_t* offsets,
                            int32_t* perm, int32_t* slot_rank, moe_stream_t stream);
 
+/* Route and union in one launch: the same outputs as moe_route_topk followed
+ * by moe_build_union on its ids (one workgroup routes every token into LDS and
+ * builds the union from there).  Errors: MOE_ERR_ARG. */
+moe_status moe_route_union(const float* logits, int32_t n, int32_t E, int32_t K,
+                           int32_t* ids, float* gates, int32_t* U, int32_t* union_ids,
+                           int32_t* offsets, int32_t* perm, int32_t* slot_rank,
+                           moe_stream_t stream);
+
 /* Deduplicating expert FFN: each expert of the union (and each shared expert)
  * is streamed from HBM once and applied to every slot routed to it (the
  * expert-bytes page, abstract).  The union arrays are those of
@@ -180,6 +188,10 @@ moe_status moe_get_error(void* ws, moe_stream_t stream);
  * same conversion the fp8 FFN kernels use. */
 moe_status moe_decode_fp8(const uint8_t* codes, float* out, int64_t count,
                           moe_stream_t stream);
+
+/* The hipError_t behind this thread's most recent MOE_ERR_HIP, and its text. */
+int32_t moe_last_hip_error(void);
+const char* moe_hip_error_string(void);
 
 const char* moe_status_str(int32_t status);
 int32_t moe_abi_version(void);

@@ -28,7 +28,10 @@ DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
+        msg = "%s: %s (status %d)" % (where, status_str(status), status)
+        if status == MOE_ERR_HIP:
+            msg += ": hipError %d %s" % (lib.moe_last_hip_error(), lib.moe_hip_error_string().decode())
+        super().__init__(msg)
 
 
 class moe_shape(C.Structure):
@@ -56,6 +59,7 @@ _I = C.c_int32
 _SIG = {
     "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_build_union": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_route_union": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_dedup": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _I, _P, _P,
                                   _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_expert_ffn_perslot": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _I, _P, _P,
@@ -68,6 +72,8 @@ _SIG = {
     "moe_get_error": (_I, [_P, _P]),
     "moe_decode_fp8": (_I, [_P, _P, C.c_int64, _P]),
     "moe_status_str": (C.c_char_p, [_I]),
+    "moe_last_hip_error": (_I, []),
+    "moe_hip_error_string": (C.c_char_p, []),
     "moe_abi_version": (_I, []),
 }
 for _name, (_res, _args) in _SIG.items():
@@ -124,6 +130,13 @@ def moe_route_topk(logits, n, E, K, ids, gates, stream=None) -> None:
 def moe_build_union(ids, n, K, E, U, union_ids, offsets, perm, slot_rank, stream=None) -> None:
     _check(lib.moe_build_union(ptr(ids), n, K, E, ptr(U), ptr(union_ids), ptr(offsets), ptr(perm),
                                ptr(slot_rank), _stream(stream)), "moe_build_union")
+
+
+def moe_route_union(logits, n, E, K, ids, gates, U, union_ids, offsets, perm, slot_rank,
+                    stream=None) -> None:
+    _check(lib.moe_route_union(ptr(logits), n, E, K, ptr(ids), ptr(gates), ptr(U), ptr(union_ids),
+                               ptr(offsets), ptr(perm), ptr(slot_rank), _stream(stream)),
+           "moe_route_union")
 
 
 def moe_expert_ffn_dedup(shape: moe_shape, w: moe_weights, x, n, U, union_ids, offsets, perm,

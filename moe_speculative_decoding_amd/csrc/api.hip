@@ -14,6 +14,15 @@ constexpr int kMaxN = 32, kMaxK = 8, kMaxE = 256, kMaxS = 4, kMaxDim = 65536;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+thread_local hipError_t g_last_hip = hipSuccess;
+
+// MOE_OK, or MOE_ERR_HIP with the HIP error remembered for moe_last_hip_error()
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = e;
+  return MOE_ERR_HIP;
+}
+
 int elem_bytes(int dt) {
   switch (dt) {
     case MOE_F32: return 4;
@@ -150,10 +159,7 @@ moe_status moe_route_topk(const float* logits, int32_t n, int32_t E, int32_t K, 
   if (n < 1 || n > kMaxN || K < 1 || K > kMaxK || E < K || E > kMaxE) return MOE_ERR_ARG;
   if (logits == nullptr || ids == nullptr || gates == nullptr) return MOE_ERR_ARG;
   if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4)) return MOE_ERR_ARG;
-  return moe::launch_route_topk(logits, n, E, K, ids, gates, static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
-             ? MOE_OK
-             : MOE_ERR_HIP;
+  return hip_status(moe::launch_route_topk(logits, n, E, K, ids, gates, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_build_union(const int32_t* ids, int32_t n, int32_t K, int32_t E, int32_t* U,
@@ -163,10 +169,19 @@ moe_status moe_build_union(const int32_t* ids, int32_t n, int32_t K, int32_t E, 
   const void* ptrs[6] = {ids, U, union_ids, offsets, perm, slot_rank};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
-  return moe::launch_build_union(ids, n, K, E, U, union_ids, offsets, perm, slot_rank,
-                                 static_cast<hipStream_t>(stream)) == hipSuccess
-             ? MOE_OK
-             : MOE_ERR_HIP;
+  return hip_status(moe::launch_build_union(ids, n, K, E, U, union_ids, offsets, perm, slot_rank,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route_union(const float* logits, int32_t n, int32_t E, int32_t K, int32_t* ids,
+                           float* gates, int32_t* U, int32_t* union_ids, int32_t* offsets,
+                           int32_t* perm, int32_t* slot_rank, moe_stream_t stream) {
+  if (n < 1 || n > kMaxN || K < 1 || K > kMaxK || E < K || E > kMaxE) return MOE_ERR_ARG;
+  const void* ptrs[8] = {logits, ids, gates, U, union_ids, offsets, perm, slot_rank};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+  return hip_status(moe::launch_route_union(logits, n, E, K, ids, gates, U, union_ids, offsets, perm,
+                                 slot_rank, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_ffn_dedup(const moe_shape* shape, const moe_weights* w, const void* x,
@@ -186,10 +201,7 @@ moe_status moe_expert_ffn_dedup(const moe_shape* shape, const moe_weights* w, co
   p.union_ids = union_ids;
   p.offsets = offsets;
   p.perm = perm;
-  return moe::launch_expert_ffn(p, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
-             ? MOE_OK
-             : MOE_ERR_HIP;
+  return hip_status(moe::launch_expert_ffn(p, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_ffn_perslot(const moe_shape* shape, const moe_weights* w, const void* x,
@@ -203,10 +215,7 @@ moe_status moe_expert_ffn_perslot(const moe_shape* shape, const moe_weights* w, 
   moe::FfnParams p = make_params(shape, w, x, n, y_slots, y_shared, bytes, ws);
   p.mode = moe::MODE_PERSLOT;
   p.ids = ids;
-  return moe::launch_expert_ffn(p, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
-             ? MOE_OK
-             : MOE_ERR_HIP;
+  return hip_status(moe::launch_expert_ffn(p, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_combine(const float* y_slots, const float* gates, const float* y_shared,
@@ -219,10 +228,8 @@ moe_status moe_combine(const float* y_slots, const float* gates, const float* y_
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!aligned(y_slots, 4) || !aligned(gates, 4) || !aligned(out, 2)) return MOE_ERR_ARG;
   if (out_dtype == MOE_F32 && !aligned(out, 4)) return MOE_ERR_ARG;
-  return moe::launch_combine(y_slots, gates, y_shared, n, K, S, d, out, out_dtype == MOE_BF16,
-                             static_cast<hipStream_t>(stream)) == hipSuccess
-             ? MOE_OK
-             : MOE_ERR_HIP;
+  return hip_status(moe::launch_combine(y_slots, gates, y_shared, n, K, S, d, out, out_dtype == MOE_BF16,
+                             static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode) {
@@ -234,9 +241,7 @@ size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode) {
 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
-  return moe::launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? MOE_OK
-             : MOE_ERR_HIP;
+  return hip_status(moe::launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_byte_counts(const moe_shape* shape, int32_t n, int32_t U, uint64_t* union_bytes,
@@ -252,15 +257,22 @@ moe_status moe_byte_counts(const moe_shape* shape, int32_t n, int32_t U, uint64_
   return MOE_OK;
 }
 
+int32_t moe_last_hip_error(void) { return static_cast<int32_t>(g_last_hip); }
+
+const char* moe_hip_error_string(void) { return hipGetErrorString(g_last_hip); }
+
 moe_status moe_get_error(void* ws, moe_stream_t stream) {
   if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  moe_status st = hip_status(hipStreamSynchronize(s));
+  if (st != MOE_OK) return st;
   uint32_t word = 0;
-  if (hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  st = hip_status(hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost));
+  if (st != MOE_OK) return st;
   if (word == 0) return MOE_OK;
   const uint32_t zero = 0;
-  if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return MOE_ERR_HIP;
+  st = hip_status(hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice));
+  if (st != MOE_OK) return st;
   if (word & moe::ERRBIT_BAD_IDS) return MOE_ERR_BAD_IDS;
   return MOE_ERR_TIMEOUT;
 }

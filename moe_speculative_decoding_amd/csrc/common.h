@@ -85,6 +85,9 @@ hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* 
 hipError_t launch_build_union(const int32_t* ids, int n, int K, int E, int32_t* U,
                               int32_t* union_ids, int32_t* offsets, int32_t* perm,
                               int32_t* slot_rank, hipStream_t s);
+hipError_t launch_route_union(const float* logits, int n, int E, int K, int32_t* ids,
+                              float* gates, int32_t* U, int32_t* union_ids, int32_t* offsets,
+                              int32_t* perm, int32_t* slot_rank, hipStream_t s);
 hipError_t launch_expert_ffn(const FfnParams& p, int w_dtype, hipStream_t s);
 hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
                           int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s);

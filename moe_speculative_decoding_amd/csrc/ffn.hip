@@ -313,6 +313,22 @@ struct StreamCfg {
   static_assert(NMAT == 1 || V >= 2, "gate/up pairing needs two values");
 };
 
+// matrix MI's base pointer (0 gate, 1 up, 2 down), routed or shared; the
+// fields are read with constant indices so the argument block stays in
+// scalar registers (a selected address would force a copy to scratch)
+template <int MI>
+__device__ __forceinline__ const uint8_t* wptr(const FfnParams& p, int shared) {
+  const uint8_t* a = p.w[MI];
+  const uint8_t* b = p.shw[MI];
+  return shared ? b : a;
+}
+template <int MI>
+__device__ __forceinline__ const float* sptr(const FfnParams& p, int shared) {
+  const float* a = p.s[MI];
+  const float* b = p.shs[MI];
+  return shared ? b : a;
+}
+
 template <int WT, int TC, int R, int NMAT, int SPC>
 __device__ __forceinline__ void load_chunk(const FfnParams& p, const Walk& w, int rows, int Kdim,
                                            int upg, int lane, int wave,
@@ -331,12 +347,13 @@ __device__ __forceinline__ void load_chunk(const FfnParams& p, const Walk& w, in
   const int e = rv > 0 ? w.G.e : 0;
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
-    const int mi = NMAT == 1 ? 2 : m;
-    const uint8_t* base = (w.G.shared ? p.shw[mi] : p.w[mi]) + static_cast<size_t>(e) * mat +
-                          static_cast<size_t>(r0) * row_bytes;
+    const uint8_t* base = (NMAT == 1 ? wptr<2>(p, w.G.shared)
+                                     : (m == 0 ? wptr<0>(p, w.G.shared) : wptr<1>(p, w.G.shared))) +
+                          static_cast<size_t>(e) * mat + static_cast<size_t>(r0) * row_bytes;
     const float* sbase = nullptr;
     if (WT == WT_FP8)
-      sbase = (w.G.shared ? p.shs[mi] : p.s[mi]) +
+      sbase = (NMAT == 1 ? sptr<2>(p, w.G.shared)
+                         : (m == 0 ? sptr<0>(p, w.G.shared) : sptr<1>(p, w.G.shared))) +
               (static_cast<size_t>(e) * (rows / 128) + (rv > 0 ? r0 / 128 : 0)) * kb;
 #pragma unroll
     for (int s = 0; s < SPC; ++s) {
@@ -629,12 +646,14 @@ static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
 
 template <int WT, int TC>
 static hipError_t launch_pair(const FfnParams& p, hipStream_t s) {
-  // up: R rows of W_gate and W_up per wave; down: R rows of W_down per wave
+  // up: R rows of W_gate and W_up per wave; down: R rows of W_down per wave.
+  // fp8 (d = 7168): the up phase stages at most 4 tokens (56 KB of LDS)
   constexpr int RU = WT == WT_FP8 ? 4 : MOE_TUNE_RU;
   constexpr int SPCU = WT == WT_FP8 ? 1 : MOE_TUNE_SPCU;
   constexpr int RD = MOE_TUNE_RD;
   constexpr int SPCD = WT == WT_FP8 ? 1 : MOE_TUNE_SPCD;
-  hipError_t e = launch_phase<WT, TC, RU, 2, SPCU>(p, s);
+  constexpr int TCU = (WT == WT_FP8 && TC > 4) ? 4 : TC;
+  hipError_t e = launch_phase<WT, TCU, RU, 2, SPCU>(p, s);
   if (e != hipSuccess) return e;
   return launch_phase<WT, TC, RD, 1, SPCD>(p, s);
 }

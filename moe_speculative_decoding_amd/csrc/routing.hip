@@ -37,22 +37,17 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
-// One wavefront per token; each lane holds up to 4 of the E <= 256 logits.
-__global__ __launch_bounds__(kBlock) void route_topk_kernel(const float* __restrict__ logits,
-                                                            int n, int E, int K,
-                                                            int32_t* __restrict__ ids,
-                                                            float* __restrict__ gates) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kBlock / kWave) + wave;
-  if (t >= n) return;  // wave-uniform
-  const float* row = logits + static_cast<size_t>(t) * E;
+// One wavefront routes one token; each lane holds up to 4 of the E <= 256
+// logits.  Lane k (< K) ends with the k-th selected id and its gate.
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int K, int lane,
+                                            int& my_id, float& my_gate) {
   unsigned long long key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
     key[j] = (e < E) ? topk_key(row[e], e) : 0ull;
   }
-  int my_id = 0;
+  my_id = 0;
   for (int k = 0; k < K; ++k) {
     unsigned long long best = key[0];
 #pragma unroll
@@ -71,15 +66,28 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float* __restr
     if (lane == k) my_id = e;
   }
   // softmax over the selected logits; the first selection holds the maximum
-  float l = (lane < K) ? row[my_id] : 0.0f;
+  const float l = (lane < K) ? row[my_id] : 0.0f;
   const float top = __shfl(l, 0);
-  float ex = (lane < K) ? expf(l - top) : 0.0f;
+  const float ex = (lane < K) ? expf(l - top) : 0.0f;
   float sum = ex;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  my_gate = ex / sum;
+}
+
+__global__ __launch_bounds__(kBlock) void route_topk_kernel(const float* __restrict__ logits,
+                                                            int n, int E, int K,
+                                                            int32_t* __restrict__ ids,
+                                                            float* __restrict__ gates) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kBlock / kWave) + wave;
+  if (t >= n) return;  // wave-uniform
+  int id;
+  float g;
+  route_token(logits + static_cast<size_t>(t) * E, E, K, lane, id, g);
   if (lane < K) {
-    ids[static_cast<size_t>(t) * K + lane] = my_id;
-    gates[static_cast<size_t>(t) * K + lane] = ex / sum;
+    ids[static_cast<size_t>(t) * K + lane] = id;
+    gates[static_cast<size_t>(t) * K + lane] = g;
   }
 }
 
@@ -92,37 +100,44 @@ hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* 
 }
 
 // ------------------------------------------------------------------ union
-// One workgroup of 256 lanes; lane s owns slot s (n*K <= 256) and expert e = s
-// (E <= 256).
-__global__ __launch_bounds__(kBlock) void build_union_kernel(
-    const int32_t* __restrict__ ids, int n, int K, int E, int32_t* __restrict__ U_out,
-    int32_t* __restrict__ union_ids, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ slot_rank) {
-  __shared__ int wcnt[kBlock / kWave][256];  // per-wave histogram of ids
-  __shared__ int rank_of[256];               // expert -> union position
-  __shared__ int start_of[256];              // expert -> first position in perm
-  __shared__ int wtot_present[kBlock / kWave];
-  __shared__ int wtot_count[kBlock / kWave];
-  __shared__ int bad;
+// Lanes 0..255 of the workgroup: lane s owns slot s (n*K <= 256) and expert
+// e = s (E <= 256).  `ids` may point to LDS or global memory.
+struct UnionLds {
+  int wcnt[4][256];  // per-wave histogram of ids
+  int rank_of[256];  // expert -> union position
+  int start_of[256]; // expert -> first position in perm
+  int wtot_present[4];
+  int wtot_count[4];
+  int bad;
+};
 
+// Every thread of the workgroup calls this (it holds __syncthreads); threads
+// 0..255 do the work.
+__device__ __forceinline__ void build_union_256(const int32_t* ids, int n, int K, int E,
+                                                int32_t* __restrict__ U_out,
+                                                int32_t* __restrict__ union_ids,
+                                                int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ perm,
+                                                int32_t* __restrict__ slot_rank, UnionLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool mine = tid < 256;
   const int nk = n * K;
   const int cap = nk < E ? nk : E;
-  for (int i = tid; i < (kBlock / kWave) * 256; i += kBlock) (&wcnt[0][0])[i] = 0;
-  if (tid == 0) bad = 0;
+  for (int i = tid; i < 4 * 256; i += blockDim.x) (&sh.wcnt[0][0])[i] = 0;
+  if (tid == 0) sh.bad = 0;
   __syncthreads();
 
-  const bool act = tid < nk;
-  int id = act ? ids[tid] : 0;
+  const bool act = tid < nk;  // nk <= 256
+  const int id = act ? ids[tid] : 0;
   if (act) {
     if (id < 0 || id >= E) {
-      atomicOr(&bad, 1);
+      atomicOr(&sh.bad, 1);
     } else {
-      atomicAdd(&wcnt[wave][id], 1);
+      atomicAdd(&sh.wcnt[wave][id], 1);
     }
   }
   __syncthreads();
-  if (bad) {
+  if (sh.bad) {  // uniform
     if (tid == 0) *U_out = -1;
     return;
   }
@@ -130,7 +145,7 @@ __global__ __launch_bounds__(kBlock) void build_union_kernel(
   // exclusive scans over experts e = tid of "present" and of the slot count
   const int e = tid;
   int c = 0;
-  if (e < E) c = wcnt[0][e] + wcnt[1][e] + wcnt[2][e] + wcnt[3][e];
+  if (e < E) c = sh.wcnt[0][e] + sh.wcnt[1][e] + sh.wcnt[2][e] + sh.wcnt[3][e];
   const int pres = (e < E && c > 0) ? 1 : 0;
   const unsigned long long pmask = __ballot(pres);
   const int pre_present = __popcll(pmask & ((1ull << lane) - 1ull));
@@ -140,30 +155,34 @@ __global__ __launch_bounds__(kBlock) void build_union_kernel(
     const int up = __shfl_up(inc, o);
     if (lane >= o) inc += up;
   }
-  if (lane == kWave - 1) {
-    wtot_present[wave] = __popcll(pmask);
-    wtot_count[wave] = inc;
+  if (mine && lane == kWave - 1) {
+    sh.wtot_present[wave] = __popcll(pmask);
+    sh.wtot_count[wave] = inc;
   }
   __syncthreads();
   int base_p = 0, base_c = 0, Utot = 0;
 #pragma unroll
-  for (int w = 0; w < kBlock / kWave; ++w) {
+  for (int w = 0; w < 4; ++w) {
     if (w < wave) {
-      base_p += wtot_present[w];
-      base_c += wtot_count[w];
+      base_p += sh.wtot_present[w];
+      base_c += sh.wtot_count[w];
     }
-    Utot += wtot_present[w];
+    Utot += sh.wtot_present[w];
   }
   const int rank = base_p + pre_present;
   const int start = base_c + inc - c;
-  rank_of[e] = rank;
-  start_of[e] = start;
+  if (mine) {
+    sh.rank_of[e] = rank;
+    sh.start_of[e] = start;
+  }
   if (pres) {
     union_ids[rank] = e;
     offsets[rank] = start;
   }
-  for (int i = Utot + tid; i < cap; i += kBlock) union_ids[i] = -1;
-  for (int i = Utot + tid; i <= cap; i += kBlock) offsets[i] = nk;
+  if (mine) {
+    for (int i = Utot + tid; i < cap; i += 256) union_ids[i] = -1;
+    for (int i = Utot + tid; i <= cap; i += 256) offsets[i] = nk;
+  }
   if (tid == 0) *U_out = Utot;
   __syncthreads();
 
@@ -179,11 +198,52 @@ __global__ __launch_bounds__(kBlock) void build_union_kernel(
   }
   if (act) {
     int before = 0;
-    for (int w = 0; w < wave; ++w) before += wcnt[w][id];
-    const int pos = start_of[id] + before + __popcll(same & ((1ull << lane) - 1ull));
+    for (int w = 0; w < wave; ++w) before += sh.wcnt[w][id];
+    const int pos = sh.start_of[id] + before + __popcll(same & ((1ull << lane) - 1ull));
     perm[pos] = tid;
-    slot_rank[tid] = rank_of[id];
+    slot_rank[tid] = sh.rank_of[id];
   }
+}
+
+__global__ __launch_bounds__(kBlock) void build_union_kernel(
+    const int32_t* __restrict__ ids, int n, int K, int E, int32_t* __restrict__ U_out,
+    int32_t* __restrict__ union_ids, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ slot_rank) {
+  __shared__ UnionLds sh;
+  build_union_256(ids, n, K, E, U_out, union_ids, offsets, perm, slot_rank, sh);
+}
+
+// Route every token (one wavefront each, 16 wavefronts) into LDS, then build
+// the union from LDS: one launch for both steps of the pass.
+constexpr int kRouteUnionBlock = 1024;
+
+__global__ __launch_bounds__(kRouteUnionBlock) void route_union_kernel(
+    const float* __restrict__ logits, int n, int E, int K, int32_t* __restrict__ ids,
+    float* __restrict__ gates, int32_t* __restrict__ U_out, int32_t* __restrict__ union_ids,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ slot_rank) {
+  __shared__ int32_t ids_lds[256];
+  __shared__ UnionLds sh;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int t = wave; t < n; t += kRouteUnionBlock / kWave) {
+    int id;
+    float g;
+    route_token(logits + static_cast<size_t>(t) * E, E, K, lane, id, g);
+    if (lane < K) {
+      ids[static_cast<size_t>(t) * K + lane] = id;
+      gates[static_cast<size_t>(t) * K + lane] = g;
+      ids_lds[t * K + lane] = id;
+    }
+  }
+  __syncthreads();
+  build_union_256(ids_lds, n, K, E, U_out, union_ids, offsets, perm, slot_rank, sh);
+}
+
+hipError_t launch_route_union(const float* logits, int n, int E, int K, int32_t* ids,
+                              float* gates, int32_t* U, int32_t* union_ids, int32_t* offsets,
+                              int32_t* perm, int32_t* slot_rank, hipStream_t s) {
+  hipLaunchKernelGGL(route_union_kernel, dim3(1), dim3(kRouteUnionBlock), 0, s, logits, n, E, K,
+                     ids, gates, U, union_ids, offsets, perm, slot_rank);
+  return hipGetLastError();
 }
 
 hipError_t launch_build_union(const int32_t* ids, int n, int K, int E, int32_t* U,

@@ -81,14 +81,14 @@ def verify_pass(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor, logits:
                 n: int, mode: int = L.MOE_MODE_DEDUP, stream=None) -> None:
     """route -> (union) -> expert FFN -> combine, all enqueued on one stream."""
     K, E, S, d = layer.K, layer.E, layer.S, layer.d
-    L.moe_route_topk(logits, n, E, K, buf.ids, buf.gates, stream)
     ysh = buf.y_shared if S > 0 else None
     if mode == L.MOE_MODE_DEDUP:
-        L.moe_build_union(buf.ids, n, K, E, buf.U, buf.union_ids, buf.offsets, buf.perm,
-                          buf.slot_rank, stream)
+        L.moe_route_union(logits, n, E, K, buf.ids, buf.gates, buf.U, buf.union_ids, buf.offsets,
+                          buf.perm, buf.slot_rank, stream)
         L.moe_expert_ffn_dedup(layer.shape, layer.weights, x, n, buf.U, buf.union_ids, buf.offsets,
                                buf.perm, buf.y_slots, ysh, buf.bytes, buf.ws, buf.ws_bytes, stream)
     else:
+        L.moe_route_topk(logits, n, E, K, buf.ids, buf.gates, stream)
         L.moe_expert_ffn_perslot(layer.shape, layer.weights, x, n, buf.ids, buf.y_slots, ysh,
                                  buf.bytes, buf.ws, buf.ws_bytes, stream)
     L.moe_combine(buf.y_slots, buf.gates, ysh, n, K, S, d, buf.out, buf.out_dtype, stream)

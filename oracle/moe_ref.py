@@ -62,6 +62,14 @@ def decode_fp8_e4m3fn(codes: np.ndarray) -> np.ndarray:
     e == 15, m == 7  -> NaN
     otherwise        -> (-1)^s * 2^(e-7) * (1 + m/8)
     """
+    c = np.asarray(codes)
+    if c.dtype == np.uint8 and c.size > 256:
+        # same formula, evaluated once per code value, then looked up
+        return _decode_fp8_formula(np.arange(256))[c]
+    return _decode_fp8_formula(c)
+
+
+def _decode_fp8_formula(codes: np.ndarray) -> np.ndarray:
     c = np.asarray(codes).astype(np.int64)
     s = (c >> 7) & 1
     e = (c >> 3) & 0xF
@@ -84,8 +92,9 @@ def decode_matrix(w: np.ndarray, w_dtype: str, scale: Optional[np.ndarray] = Non
         v = decode_fp8_e4m3fn(w)
         rows, cols = v.shape
         s = np.asarray(scale, dtype=np.float32).astype(np.float64)
-        full = np.repeat(np.repeat(s, FP8_BLOCK, axis=0), FP8_BLOCK, axis=1)[:rows, :cols]
-        return v * full
+        # element (i, j) takes the scale of block (i // 128, j // 128)
+        blocks = v.reshape(rows // FP8_BLOCK, FP8_BLOCK, cols // FP8_BLOCK, FP8_BLOCK)
+        return (blocks * s[:, None, :, None]).reshape(rows, cols)
     raise ValueError(w_dtype)
 
 

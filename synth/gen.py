@@ -79,15 +79,19 @@ def to_fp8_codes(a: np.ndarray) -> np.ndarray:
 
 
 def quantize_fp8_blocks(w: np.ndarray):
-    """[rows][cols] float32 -> (codes uint8 [rows][cols], scales f32 [rows/128][cols/128])."""
+    """[rows][cols] float32 -> (codes uint8 [rows][cols], scales f32 [rows/128][cols/128]).
+
+    float32 throughout (torch CPU ops): scale = amax / 448, codes = RNE of the
+    clipped quotient."""
     rows, cols = w.shape
     rb, cb = rows // FP8_BLOCK, cols // FP8_BLOCK
-    blocks = w.reshape(rb, FP8_BLOCK, cb, FP8_BLOCK)
-    amax = np.abs(blocks).max(axis=(1, 3)).astype(np.float32)
-    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
-    q = blocks / scale[:, None, :, None]
-    q = np.clip(q, -FP8_MAX, FP8_MAX).astype(np.float32).reshape(rows, cols)
-    return to_fp8_codes(q), scale
+    blocks = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).view(
+        rb, FP8_BLOCK, cb, FP8_BLOCK)
+    amax = blocks.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    q = (blocks / scale[:, None, :, None]).clamp_(-FP8_MAX, FP8_MAX).reshape(rows, cols)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, scale.numpy().astype(np.float32)
 
 
 def store(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -100,12 +104,20 @@ def store(a: np.ndarray, dtype: str) -> np.ndarray:
 
 # ----------------------------------------------------------------------- weights
 def expert_weights(cfg: LayerConfig, e: int, seed: int = 0, layer: int = 0) -> Dict[str, np.ndarray]:
-    """Weights of expert e (routed e < E, shared e = E + s) in storage layout."""
-    g = expert_rng(cfg, seed, layer, e)
-    std = np.float32(1.0 / np.sqrt(cfg.d))
-    wg = g.standard_normal((cfg.f, cfg.d), dtype=np.float32) * std
-    wu = g.standard_normal((cfg.f, cfg.d), dtype=np.float32) * std
-    wd = g.standard_normal((cfg.d, cfg.f), dtype=np.float32) * std
+    """Weights of expert e (routed e < E, shared e = E + s) in storage layout.
+
+    Normals come from torch's CPU generator seeded from the expert's numpy
+    seed sequence (faster than numpy for the 44M values of a DeepSeek-V3
+    expert)."""
+    g = torch.Generator().manual_seed(int(expert_rng(cfg, seed, layer, e).integers(0, 2 ** 62)))
+    std = 1.0 / float(np.sqrt(cfg.d))
+
+    def draw(shape):
+        return (torch.randn(shape, generator=g, dtype=torch.float32) * std).numpy()
+
+    wg = draw((cfg.f, cfg.d))
+    wu = draw((cfg.f, cfg.d))
+    wd = draw((cfg.d, cfg.f))
     if cfg.w_dtype == FP8:
         qg, sg = quantize_fp8_blocks(wg)
         qu, su = quantize_fp8_blocks(wu)

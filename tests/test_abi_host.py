@@ -36,6 +36,23 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, name), name
 
 
+def _declared_arity():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(moe_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        args = m.group(2).strip()
+        out[m.group(1)] = 0 if args in ("", "void") else args.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_header():
+    # a missing argtype would pass pointers through ctypes' int default
+    arity = _declared_arity()
+    assert set(L._SIG) == set(arity), set(L._SIG) ^ set(arity)
+    for name, (_, args) in L._SIG.items():
+        assert len(args) == arity[name], name
+
+
 def test_abi_version_and_status_strings():
     assert L.moe_abi_version() == 1
     for s in range(7):

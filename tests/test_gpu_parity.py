@@ -108,6 +108,54 @@ def test_build_union_bit_exact(n, E, K, pool):
             assert np.array_equal(np.asarray(got[k]), np.asarray(ref[k])), (k, rep)
 
 
+@pytest.mark.parametrize("cfg,n,routing,tree", [
+    (TINY, 4, None, False), (QWEN3, 8, None, False), (OLMOE, 1, "markov:0.5", False),
+    (DSV3, 32, "markov:0.5", True), (DSV3, 32, "iid", True), (DSV2LITE, 16, "markov:0.8", True),
+])
+def test_route_union_fused_matches_oracle(cfg, n, routing, tree):
+    case = make_case(cfg, n, routing, seed=4, tree=tree)
+    E, K = cfg.E, cfg.K
+    cap = min(n * K, E)
+    out = {k: torch.full((m,), -9, dtype=torch.int32, device=DEV) for k, m in
+           (("ids", n * K), ("U", 1), ("union_ids", cap), ("offsets", cap + 1), ("perm", n * K),
+            ("slot_rank", n * K))}
+    gates = torch.zeros(n * K, dtype=torch.float32, device=DEV)
+    L.moe_route_union(dev(case.logits), n, E, K, out["ids"], gates, out["U"], out["union_ids"],
+                      out["offsets"], out["perm"], out["slot_rank"])
+    torch.cuda.synchronize()
+    rid, rg = oracle.route_topk(case.logits, K)
+    assert np.array_equal(out["ids"].cpu().numpy().reshape(n, K), rid)
+    g = gates.cpu().numpy().astype(np.float64).reshape(n, K)
+    assert np.all(np.abs(g - rg) <= 1e-6 + 1e-5 * np.abs(rg))
+    ref = oracle.build_union(rid, E)
+    assert int(out["U"].item()) == ref["U"]
+    for k in ("union_ids", "offsets", "perm", "slot_rank"):
+        assert np.array_equal(out[k].cpu().numpy(), ref[k]), k
+
+
+def test_route_union_with_ties_and_nan():
+    g = np.random.default_rng(77)
+    vals = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0, np.nan], dtype=np.float32)
+    for n, E, K in ((32, 256, 8), (9, 8, 8), (32, 12, 4)):
+        logits = vals[g.integers(0, len(vals), (n, E))]
+        cap = min(n * K, E)
+        ids = torch.empty(n * K, dtype=torch.int32, device=DEV)
+        gates = torch.empty(n * K, dtype=torch.float32, device=DEV)
+        U = torch.empty(1, dtype=torch.int32, device=DEV)
+        uid = torch.empty(cap, dtype=torch.int32, device=DEV)
+        off = torch.empty(cap + 1, dtype=torch.int32, device=DEV)
+        perm = torch.empty(n * K, dtype=torch.int32, device=DEV)
+        rank = torch.empty(n * K, dtype=torch.int32, device=DEV)
+        L.moe_route_union(dev(logits), n, E, K, ids, gates, U, uid, off, perm, rank)
+        torch.cuda.synchronize()
+        rid, _ = oracle.route_topk(logits, K)
+        assert np.array_equal(ids.cpu().numpy().reshape(n, K), rid)
+        ref = oracle.build_union(rid, E)
+        assert int(U.item()) == ref["U"]
+        assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+        assert np.array_equal(off.cpu().numpy(), ref["offsets"])
+
+
 def test_build_union_flags_out_of_range_ids():
     ids = np.array([[0, 3], [8, 1]], dtype=np.int32)
     assert _union(ids, 8)["U"] == -1
@@ -154,9 +202,20 @@ def test_ffn_dsv2lite_shape(n, tree):
     run_case(make_case(DSV2LITE, n, "markov:0.5", seed=0, tree=tree))
 
 
-@pytest.mark.parametrize("n,routing", [(1, "iid"), (2, "markov:0.5")])
+@pytest.mark.parametrize("n,routing", [(1, "iid"), (2, "markov:0.5"), (6, "markov:0.5")])
 def test_ffn_dsv3_shape(n, routing):
     run_case(make_case(DSV3, n, routing, seed=0))
+
+
+# the DeepSeek-V3 expert shape with 16 experts, so a 32-node tree puts up to
+# 32 tokens on one expert (8 token tiles in the up phase, 4 in the down phase)
+DSV3_E16 = LayerConfig(name="dsv3_e16", cfg_id=83, E=16, K=8, d=7168, f=2048, S=0,
+                       w_dtype="fp8_e4m3", x_dtype="bf16", n_values=(32,),
+                       routing=("markov:0.5",), tolerance=3e-2)
+
+
+def test_ffn_dsv3_expert_shape_tree32():
+    run_case(make_case(DSV3_E16, 32, "markov:0.5", seed=0, tree=True))
 
 
 # ------------------------------------------------------- invalid expert ids
