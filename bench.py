@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--cold", action="store_true", help="also time operations after a scrub")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--counters", metavar="MANIFEST",
+                    help="counter-collection mode: eager launches of every operation's route+union "
+                         "and deduplicating FFN plus three 1 GiB calibration copies; writes the "
+                         "launch order to MANIFEST (JSON) and no benchmark line")
     return ap.parse_args()
 
 
@@ -145,6 +149,32 @@ def main():
         if not rel < 1e-5:
             raise RuntimeError("dedup and per-slot outputs differ (rel %.2e)" % rel)
     step_union_bytes = sum(op["union_bytes"] for op in ops)
+
+    if args.counters:
+        # under rocprofv3 --pmc: one dispatch sequence per operation, in order
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        for op in ops:
+            lay = layers[op["layer"]]
+            b = op["buf"]
+            L.moe_route_union(op["logits"], op["n"], lay.E, lay.K, b.ids, b.gates, b.U, b.union_ids,
+                              b.offsets, b.perm, b.slot_rank)
+            L.moe_expert_ffn_dedup(lay.shape, lay.weights, op["x"], op["n"], b.U, b.union_ids,
+                                   b.offsets, b.perm, b.y_slots, None, b.bytes, b.ws, b.ws_bytes)
+            torch.cuda.synchronize()
+        manifest = {"copy_bytes": src.numel() * 4, "copies": 3,
+                    "ops": [{"n": op["n"], "layer": op["layer"], "U": op["U"],
+                             "union_bytes": op["union_bytes"],
+                             "requested_bytes": op["requested_bytes"]} for op in ops],
+                    "sequence": "per op: route_union_kernel, ffn up kernel, ffn down kernel"}
+        with open(args.counters, "w") as fh:
+            json.dump(manifest, fh)
+        log("counter mode: %d operations written to %s" % (len(ops), args.counters))
+        return
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
