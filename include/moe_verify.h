@@ -162,7 +162,9 @@ moe_status moe_expert_ffn_perslot(const moe_shape* shape, const moe_weights* w,
  * weighted sum of the selected experts):
  *   out[t] = sum_{k ascending} gates[t][k] * y_slots[t][k] + sum_s y_shared[t][s]
  * out (device) [n][d] of out_dtype (MOE_F32 or MOE_BF16, round to nearest even).
- * y_shared may be NULL when S == 0.  Errors: MOE_ERR_ARG / _UNSUPPORTED. */
+ * y_shared may be NULL when S == 0.  d must be a multiple of 4; y_slots,
+ * y_shared and out 16-byte aligned, gates 4-byte aligned.
+ * Errors: MOE_ERR_ARG (pointers, sizes) / _UNSUPPORTED (out_dtype, d). */
 moe_status moe_combine(const float* y_slots, const float* gates, const float* y_shared,
                        int32_t n, int32_t K, int32_t S, int32_t d, void* out,
                        int32_t out_dtype, moe_stream_t stream);

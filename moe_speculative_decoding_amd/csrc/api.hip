@@ -226,8 +226,9 @@ moe_status moe_combine(const float* y_slots, const float* gates, const float* y_
   if (y_slots == nullptr || gates == nullptr || out == nullptr) return MOE_ERR_ARG;
   if (S > 0 && y_shared == nullptr) return MOE_ERR_ARG;
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (!aligned(y_slots, 4) || !aligned(gates, 4) || !aligned(out, 2)) return MOE_ERR_ARG;
-  if (out_dtype == MOE_F32 && !aligned(out, 4)) return MOE_ERR_ARG;
+  if (d % 4 != 0) return MOE_ERR_UNSUPPORTED;  // four columns per lane
+  if (!aligned(y_slots, 16) || !aligned(gates, 4) || !aligned(out, 16)) return MOE_ERR_ARG;
+  if (S > 0 && !aligned(y_shared, 16)) return MOE_ERR_ARG;
   return hip_status(moe::launch_combine(y_slots, gates, y_shared, n, K, S, d, out, out_dtype == MOE_BF16,
                              static_cast<hipStream_t>(stream)));
 }

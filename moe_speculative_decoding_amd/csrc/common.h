@@ -78,6 +78,7 @@ struct FfnParams {
   int n, K, S, E, d, f;
   int ucap;               // dedup: upper bound of U = min(n*K, E)
   int mode;
+  int lds_slots;          // token slots in LDS (set by the launcher)
 };
 
 hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* ids,

@@ -330,8 +330,8 @@ __device__ __forceinline__ const float* sptr(const FfnParams& p, int shared) {
 }
 
 template <int WT, int TC, int R, int NMAT, int SPC>
-__device__ __forceinline__ void load_chunk(const FfnParams& p, const Walk& w, int rows, int Kdim,
-                                           int upg, int lane, int wave,
+__device__ __forceinline__ void load_chunk(const FfnParams& p, const Group& G, int live, int urel,
+                                           int kc, int rows, int Kdim, int lane, int wave,
                                            u32x4 (&buf)[NMAT][SPC][R], float (&sc)[NMAT][SPC]) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   using T = typename C::T;
@@ -339,25 +339,25 @@ __device__ __forceinline__ void load_chunk(const FfnParams& p, const Walk& w, in
   // loaded value before the multiply, so the next chunk stays in flight while
   // the current one is used.  Masked lanes read 16 zero bytes of the
   // workspace's control block instead of weights.
-  const int r0 = (w.u - w.g * upg) * (kBlock / kWave) * R + wave * R;
-  const int rv = (w.valid && !w.done) ? max(0, min(R, rows - r0)) : 0;
+  const int r0 = urel * (kBlock / kWave) * R + wave * R;
+  const int rv = live ? max(0, min(R, rows - r0)) : 0;
   const size_t row_bytes = static_cast<size_t>(Kdim) * T::EB;
   const size_t mat = static_cast<size_t>(rows) * row_bytes;
   const int kb = Kdim / 128;
-  const int e = rv > 0 ? w.G.e : 0;
+  const int e = rv > 0 ? G.e : 0;
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
-    const uint8_t* base = (NMAT == 1 ? wptr<2>(p, w.G.shared)
-                                     : (m == 0 ? wptr<0>(p, w.G.shared) : wptr<1>(p, w.G.shared))) +
+    const uint8_t* base = (NMAT == 1 ? wptr<2>(p, G.shared)
+                                     : (m == 0 ? wptr<0>(p, G.shared) : wptr<1>(p, G.shared))) +
                           static_cast<size_t>(e) * mat + static_cast<size_t>(r0) * row_bytes;
     const float* sbase = nullptr;
     if (WT == WT_FP8)
-      sbase = (NMAT == 1 ? sptr<2>(p, w.G.shared)
-                         : (m == 0 ? sptr<0>(p, w.G.shared) : sptr<1>(p, w.G.shared))) +
+      sbase = (NMAT == 1 ? sptr<2>(p, G.shared)
+                         : (m == 0 ? sptr<0>(p, G.shared) : sptr<1>(p, G.shared))) +
               (static_cast<size_t>(e) * (rows / 128) + (rv > 0 ? r0 / 128 : 0)) * kb;
 #pragma unroll
     for (int s = 0; s < SPC; ++s) {
-      const int k = w.kc * C::CH + s * C::STEP + lane * T::VEC;
+      const int k = kc * C::CH + s * C::STEP + lane * T::VEC;
       const bool kin = k < Kdim;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -446,14 +446,13 @@ __device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt,
 }
 
 template <int WT, int TC, int R, int NMAT, int SPC>
-__device__ __forceinline__ void finish_unit(const FfnParams& p, const Walk& w, int rows, int upg,
+__device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int urel, int rows,
                                             int lane, int wave, const int* tok_h,
                                             float* const* tok_y, float* acc) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   Halve<C::V>::run(acc, lane, 32);
-  const int r0 = (w.u - w.g * upg) * (kBlock / kWave) * R + wave * R;
+  const int r0 = urel * (kBlock / kWave) * R + wave * R;
   const int rv = max(0, min(R, rows - r0));
-  const int nt = min(TC, w.G.cnt - w.tile * TC);
   if (NMAT == 2) {
     const float v = __shfl_xor(acc[0], 32);  // the up value pairs with this gate value
     if (lane < 32 && (lane & ((1 << C::SH) - 1)) == 0) {
@@ -486,8 +485,8 @@ __global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   constexpr bool UP = NMAT == 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
-  __shared__ int tok_h[TC];
-  __shared__ float* tok_y[TC];
+  __shared__ int tok_h[2 * TC];
+  __shared__ float* tok_y[2 * TC];
   __shared__ Meta mt;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = UP ? p.f : p.d;
@@ -526,10 +525,6 @@ __global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
 
   load_meta(p, mt);
   __syncthreads();
-  Walk cur;
-  cur.done = 0;
-  walk_group<TC>(p, mt, U, cur, static_cast<int>(lo / upg), lo, hi, upg);
-  if (UP && !cur.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
 
   u32x4 b0[NMAT][SPC][R], b1[NMAT][SPC][R];
   float s0[NMAT][SPC], s1[NMAT][SPC];
@@ -537,7 +532,87 @@ __global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
 #pragma unroll
   for (int i = 0; i < C::V; ++i) acc[i] = 0.0f;
 
-  load_chunk<WT, TC, R, NMAT, SPC>(p, cur, rows, Kdim, upg, lane, wave, b0, s0);
+  // Fast path: the range touches at most two groups, each within one token
+  // tile, and LDS has two token slots: stage both up front, then stream with
+  // no load other than the weights (a load that must be waited for would,
+  // with in-order completion, drain the weight prefetch).
+  const int g0 = uni(static_cast<int>(lo / upg));
+  const int g1 = uni(static_cast<int>((hi - 1) / upg));
+  Group G0, G1;
+  group_at(p, mt, U, g0, G0);
+  group_at(p, mt, U, g1, G1);
+  G0.e = uni(G0.e); G0.shared = uni(G0.shared); G0.cnt = uni(G0.cnt);
+  G0.first = uni(G0.first); G0.s_idx = uni(G0.s_idx);
+  G1.e = uni(G1.e); G1.shared = uni(G1.shared); G1.cnt = uni(G1.cnt);
+  G1.first = uni(G1.first); G1.s_idx = uni(G1.s_idx);
+  const bool fast = g1 - g0 <= 1 && G0.cnt <= TC && G1.cnt <= TC && (g1 == g0 || p.lds_slots >= 2);
+  if (fast) {
+    const int v0 = G0.shared || (G0.e >= 0 && G0.e < p.E);
+    const int v1 = G1.shared || (G1.e >= 0 && G1.e < p.E);
+    if (UP && threadIdx.x == 0 && (!v0 || !v1)) atomicOr(p.err, ERRBIT_BAD_IDS);
+    const int base0 = g0 * upg;
+    const int nct = static_cast<int>(hi - lo) * nchunks;  // chunks of this range
+    const size_t slot_bytes = static_cast<size_t>(TC) * Kpad * C::T::XB;
+    uint8_t* xs1 = xs + (g1 != g0 ? slot_bytes : 0);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, G0, v0, static_cast<int>(lo) - base0, 0, rows, Kdim, lane,
+                                     wave, b0, s0);
+    {
+      Walk w;
+      w.G = G0;
+      w.tile = 0;
+      stage_tokens<WT, TC, !UP>(p, mt, w, Kdim, Kpad, xs, tok_h, tok_y);
+      if (g1 != g0) {
+        w.G = G1;
+        stage_tokens<WT, TC, !UP>(p, mt, w, Kdim, Kpad, xs1, tok_h + TC, tok_y + TC);
+      }
+    }
+    __syncthreads();
+    // chunk c: unit lo + c / nchunks, K chunk c % nchunks.  One step
+    // prefetches chunk cc + 1 into one buffer and multiplies chunk cc from
+    // the other.  The loop runs whole pairs of steps, so on every path back
+    // to its head the only loads in flight are the prefetch of the next
+    // chunk (a half-finished pair would leave a buffer that the head
+    // overwrites in flight, and the compiler would wait for every load there).
+    auto step = [&](int cc, u32x4 (&bl)[NMAT][SPC][R], float (&sl)[NMAT][SPC],
+                    const u32x4 (&bm)[NMAT][SPC][R], const float (&sm)[NMAT][SPC],
+                    bool prefetch) {
+      if (prefetch) {
+        const int un = static_cast<int>(lo) + (cc + 1) / nchunks;  // unit of the next chunk
+        const int kn = (cc + 1) - ((cc + 1) / nchunks) * nchunks;
+        const int sn = un - base0 >= upg;  // next chunk in the second group
+        load_chunk<WT, TC, R, NMAT, SPC>(p, sn ? G1 : G0, (cc + 1 < nct) && (sn ? v1 : v0),
+                                         un - base0 - (sn ? upg : 0), kn, rows, Kdim, lane, wave,
+                                         bl, sl);
+#ifdef MOE_TUNE_SCHED
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+      }
+      const int uc = static_cast<int>(lo) + cc / nchunks;
+      const int kcc = cc - (cc / nchunks) * nchunks;
+      const int sc_ = uc - base0 >= upg;
+      mul_chunk<WT, TC, R, NMAT, SPC>(kcc, Kpad, lane, sc_ ? xs1 : xs, bm, sm, acc);
+      if (kcc == nchunks - 1)
+        finish_unit<WT, TC, R, NMAT, SPC>(p, sc_ ? G1.cnt : G0.cnt, uc - base0 - (sc_ ? upg : 0),
+                                          rows, lane, wave, tok_h + (sc_ ? TC : 0),
+                                          tok_y + (sc_ ? TC : 0), acc);
+    };
+    int c = 0;
+    for (; c + 2 <= nct; c += 2) {
+      step(c, b1, s1, b0, s0, true);
+      step(c + 1, b0, s0, b1, s1, true);
+    }
+    if (c < nct) step(c, b1, s1, b0, s0, false);  // odd count: the last chunk is in b0
+    return;
+  }
+
+  // General path: restage tokens at every (group, token tile) change.
+  Walk cur;
+  cur.done = 0;
+  walk_group<TC>(p, mt, U, cur, g0, lo, hi, upg);
+  if (UP && !cur.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+
+  load_chunk<WT, TC, R, NMAT, SPC>(p, cur.G, cur.valid, cur.u - cur.g * upg, cur.kc, rows, Kdim,
+                                   lane, wave, b0, s0);
   stage_tokens<WT, TC, !UP>(p, mt, cur, Kdim, Kpad, xs, tok_h, tok_y);
   __syncthreads();
 
@@ -545,10 +620,12 @@ __global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
   walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
   // two chunks per trip so the register buffers keep fixed names
   while (true) {
-    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt, rows, Kdim, upg, lane, wave, b1, s1);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, nxt.valid && !nxt.done, nxt.u - nxt.g * upg, nxt.kc,
+                                     rows, Kdim, lane, wave, b1, s1);
     mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b0, s0, acc);
     if (cur.kc == nchunks - 1)
-      finish_unit<WT, TC, R, NMAT, SPC>(p, cur, rows, upg, lane, wave, tok_h, tok_y, acc);
+      finish_unit<WT, TC, R, NMAT, SPC>(p, min(TC, cur.G.cnt - cur.tile * TC), cur.u - cur.g * upg,
+                                        rows, lane, wave, tok_h, tok_y, acc);
     if (nxt.done) break;
     if (nxt.g != cur.g || nxt.tile != cur.tile) {
       if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
@@ -559,10 +636,12 @@ __global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
     cur = nxt;
     walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
 
-    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt, rows, Kdim, upg, lane, wave, b0, s0);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, nxt.valid && !nxt.done, nxt.u - nxt.g * upg, nxt.kc,
+                                     rows, Kdim, lane, wave, b0, s0);
     mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b1, s1, acc);
     if (cur.kc == nchunks - 1)
-      finish_unit<WT, TC, R, NMAT, SPC>(p, cur, rows, upg, lane, wave, tok_h, tok_y, acc);
+      finish_unit<WT, TC, R, NMAT, SPC>(p, min(TC, cur.G.cnt - cur.tile * TC), cur.u - cur.g * upg,
+                                        rows, lane, wave, tok_h, tok_y, acc);
     if (nxt.done) break;
     if (nxt.g != cur.g || nxt.tile != cur.tile) {
       if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
@@ -613,8 +692,19 @@ static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
   const int rows = UP ? p.f : p.d;
   const int Kdim = UP ? p.d : p.f;
   const int Kpad = (Kdim + C::CH - 1) / C::CH * C::CH;
-  const size_t smem = static_cast<size_t>(TC) * Kpad * C::T::XB;
   const void* fn = reinterpret_cast<const void*>(&ffn_stream_kernel<WT, TC, R, NMAT, SPC>);
+  // A second token slot lets ranges that cross a group boundary take the
+  // fast path; it is used only when it costs no resident workgroups.
+  const size_t slot = static_cast<size_t>(TC) * Kpad * C::T::XB;
+#ifndef MOE_TUNE_SLOTS
+  const int slots =
+      2 * slot <= 65536 && resident_blocks(fn, 2 * slot) >= resident_blocks(fn, slot) ? 2 : 1;
+#else
+  const int slots = MOE_TUNE_SLOTS;
+#endif
+  const size_t smem = slots * slot;
+  FfnParams q = p;
+  q.lds_slots = slots;
   const int upg = (rows + (kBlock / kWave) * R - 1) / ((kBlock / kWave) * R);
   const int groups_max = p.mode == MODE_DEDUP ? p.ucap + p.S : p.n * (p.K + p.S);
   const long long units_max = static_cast<long long>(groups_max) * upg;
@@ -625,7 +715,7 @@ static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
 #endif
   if (grid > units_max) grid = units_max;
   hipLaunchKernelGGL((ffn_stream_kernel<WT, TC, R, NMAT, SPC>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kBlock), smem, s, p);
+                     dim3(kBlock), smem, s, q);
   return hipGetLastError();
 }
 

@@ -8,35 +8,69 @@
 
 namespace moe {
 
-__global__ __launch_bounds__(kBlock) void combine_kernel(const float* __restrict__ y_slots,
-                                                         const float* __restrict__ gates,
-                                                         const float* __restrict__ y_shared,
-                                                         int n, int K, int S, int d,
-                                                         void* __restrict__ out, int out_bf16) {
+// One lane: four consecutive columns of one token.  Every load of the lane
+// (K slot rows, S shared rows) is issued before the first use, so the kernel
+// waits for memory once; the sum runs k ascending, then the shared experts.
+constexpr int kCombineBlock = 64;
+
+__global__ __launch_bounds__(kCombineBlock) void combine_kernel(
+    const float* __restrict__ y_slots, const float* __restrict__ gates,
+    const float* __restrict__ y_shared, int n, int K, int S, int d, void* __restrict__ out,
+    int out_bf16) {
   const int t = blockIdx.y;
-  const int c = blockIdx.x * kBlock + threadIdx.x;
+  const int c = (blockIdx.x * kCombineBlock + threadIdx.x) * 4;
   if (t >= n || c >= d) return;
-  float acc = 0.0f;
   const float* g = gates + static_cast<size_t>(t) * K;
   const float* y = y_slots + static_cast<size_t>(t) * K * d + c;
-  for (int k = 0; k < K; ++k) acc = fmaf(g[k], y[static_cast<size_t>(k) * d], acc);
-  if (S > 0) {
-    const float* ys = y_shared + static_cast<size_t>(t) * S * d + c;
-    for (int s = 0; s < S; ++s) acc += ys[static_cast<size_t>(s) * d];
+  f32x4 yv[8], sv[4];
+  float gv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k < K) {
+      yv[k] = *reinterpret_cast<const f32x4*>(y + static_cast<size_t>(k) * d);
+      gv[k] = g[k];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < S)
+      sv[q] = *reinterpret_cast<const f32x4*>(y_shared + (static_cast<size_t>(t) * S + q) * d + c);
+  }
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k < K) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(gv[k], yv[k][i], acc[i]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < S) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += sv[q][i];
+    }
   }
   const size_t o = static_cast<size_t>(t) * d + c;
   if (out_bf16) {
-    reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(acc);
+    uint2 packed;
+    packed.x = f32_to_bf16_bits(acc[0]) | (static_cast<unsigned>(f32_to_bf16_bits(acc[1])) << 16);
+    packed.y = f32_to_bf16_bits(acc[2]) | (static_cast<unsigned>(f32_to_bf16_bits(acc[3])) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + o) = packed;
   } else {
-    reinterpret_cast<float*>(out)[o] = acc;
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = acc[i];
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = r;
   }
 }
 
 hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
                           int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s) {
-  dim3 grid((d + kBlock - 1) / kBlock, n);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kBlock), 0, s, y_slots, gates, y_shared, n, K,
-                     S, d, out, out_bf16);
+  const int lanes = (d + 3) / 4;
+  dim3 grid((lanes + kCombineBlock - 1) / kCombineBlock, n);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineBlock), 0, s, y_slots, gates, y_shared,
+                     n, K, S, d, out, out_bf16);
   return hipGetLastError();
 }
 

@@ -18,61 +18,119 @@ namespace moe {
 
 // ------------------------------------------------------------------ top-K
 // Key order = (logit descending, id ascending); NaN below every number,
-// -0.0 equal to +0.0.  Larger key wins; every real entry has a non-zero key.
-__device__ __forceinline__ unsigned long long topk_key(float v, int e) {
+// -0.0 equal to +0.0.  The 32-bit key orders the values: every number maps
+// above 1, NaN maps to 1 and 0 marks an entry that is absent (beyond E) or
+// already taken; equal keys are split by the id afterwards.
+__device__ __forceinline__ unsigned topk_key(float v) {
   unsigned b = __float_as_uint(v);
-  if (b == 0x80000000u) b = 0u;  // -0.0 -> +0.0
-  unsigned k32;
-  if ((b & 0x7fffffffu) > 0x7f800000u) {
-    k32 = 0u;  // NaN
-  } else {
-    k32 = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  }
-  return (static_cast<unsigned long long>(k32) << 32) | static_cast<unsigned>(~static_cast<unsigned>(e));
+  if (b == 0x80000000u) b = 0u;                     // -0.0 -> +0.0
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 1u;  // NaN
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // -inf -> 0x007fffff
 }
 
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
-  unsigned lo = __shfl_xor(static_cast<unsigned>(v), o);
-  unsigned hi = __shfl_xor(static_cast<unsigned>(v >> 32), o);
-  return (static_cast<unsigned long long>(hi) << 32) | lo;
+// Cross-lane moves inside rows of 16 lanes (DPP): no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp(unsigned v) {
+  return static_cast<unsigned>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// maximum over the wavefront, returned in a scalar register
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+  v = max(v, dpp<kDppQuadXor1>(v));
+  v = max(v, dpp<kDppQuadXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));  // max over 8 lanes
+  v = max(v, dpp<kDppMirror>(v));      // max over the row of 16
+  const unsigned a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const unsigned c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
-// One wavefront routes one token; each lane holds up to 4 of the E <= 256
-// logits.  Lane k (< K) ends with the k-th selected id and its gate.
+// inclusive prefix sum over the wavefront: Hillis-Steele inside each row of
+// 16 lanes, then the row totals added in from scalar registers
+__device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
+  unsigned u = static_cast<unsigned>(v);
+  u += dpp<0x111>(u);  // row_shr:1 (lanes shifted in from outside the row read 0)
+  u += dpp<0x112>(u);  // row_shr:2
+  u += dpp<0x114>(u);  // row_shr:4
+  u += dpp<0x118>(u);  // row_shr:8
+  const unsigned r0 = __builtin_amdgcn_readlane(u, 15);
+  const unsigned r1 = __builtin_amdgcn_readlane(u, 31);
+  const unsigned r2 = __builtin_amdgcn_readlane(u, 47);
+  u += (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+  return static_cast<int>(u);
+}
+
+// One wavefront routes one token; lane l holds the logits of experts
+// l, l+64, l+128, l+192 (E <= 256).  Lane k (< K) ends with the k-th selected
+// id and its gate.  Each of the K rounds takes the wavefront maximum of the
+// lanes' best remaining keys, then the lowest id holding it (id = l + 64 j,
+// so the lowest j first, then the lowest lane).
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int K, int lane,
                                             int& my_id, float& my_gate) {
-  unsigned long long key[4];
+  float val[4];
+  unsigned key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
-    key[j] = (e < E) ? topk_key(row[e], e) : 0ull;
+    val[j] = (e < E) ? row[e] : 0.0f;
+    key[j] = (e < E) ? topk_key(val[j]) : 0u;
   }
-  my_id = 0;
-  for (int k = 0; k < K; ++k) {
-    unsigned long long best = key[0];
+  int sel_id[8];
+  float sel_l[8];
 #pragma unroll
-    for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
+  for (int k = 0; k < 8; ++k) {
+    sel_id[k] = 0;
+    sel_l[k] = 0.0f;
+    if (k < K) {
+      unsigned best = 0u;
+      int bj = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const unsigned long long other = shfl_xor_u64(best, o);
-      best = other > best ? other : best;
+      for (int j = 0; j < 4; ++j) {
+        if (key[j] > best) {  // strict: the lowest j keeps a tie
+          best = key[j];
+          bj = j;
+        }
+      }
+      const unsigned M = wave_max_u32(best);
+      int e = 0;
+      const bool hit = best == M;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {  // the lowest j with a hit wins
+        const unsigned long long m = __ballot(hit && bj == j);
+        if (m != 0ull) e = j * kWave + static_cast<int>(__builtin_ctzll(m));
+      }
+      e = __builtin_amdgcn_readfirstlane(e);
+      const int ej = e >> 6, el = e & 63;
+      const float lv = ej == 0 ? val[0] : (ej == 1 ? val[1] : (ej == 2 ? val[2] : val[3]));
+      sel_l[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), el));
+      sel_id[k] = e;
+      if (lane == el) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j == ej) key[j] = 0u;
+      }
     }
-    const int e = static_cast<int>(~static_cast<unsigned>(best));
-    if (lane == (e & 63)) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j == (e >> 6)) key[j] = 0ull;
-    }
-    if (lane == k) my_id = e;
   }
   // softmax over the selected logits; the first selection holds the maximum
-  const float l = (lane < K) ? row[my_id] : 0.0f;
-  const float top = __shfl(l, 0);
-  const float ex = (lane < K) ? expf(l - top) : 0.0f;
-  float sum = ex;
+  const float top = sel_l[0];
+  float sum = 0.0f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-  my_gate = ex / sum;
+  for (int k = 0; k < 8; ++k)
+    if (k < K) sum += expf(sel_l[k] - top);
+  my_id = 0;
+  float l = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (lane == k) {
+      my_id = sel_id[k];
+      l = sel_l[k];
+    }
+  my_gate = expf(l - top) / sum;
 }
 
 __global__ __launch_bounds__(kBlock) void route_topk_kernel(const float* __restrict__ logits,
@@ -149,12 +207,7 @@ __device__ __forceinline__ void build_union_256(const int32_t* ids, int n, int K
   const int pres = (e < E && c > 0) ? 1 : 0;
   const unsigned long long pmask = __ballot(pres);
   const int pre_present = __popcll(pmask & ((1ull << lane) - 1ull));
-  int inc = c;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int up = __shfl_up(inc, o);
-    if (lane >= o) inc += up;
-  }
+  const int inc = wave_inclusive_sum(c, lane);
   if (mine && lane == kWave - 1) {
     sh.wtot_present[wave] = __popcll(pmask);
     sh.wtot_count[wave] = inc;

@@ -135,6 +135,9 @@ def test_routing_and_combine_validation():
     cb = L.lib.moe_combine
     assert cb(FAKE, FAKE, None, 4, 2, 1, 256, FAKE, L.MOE_F32, None) == L.MOE_ERR_ARG
     assert cb(FAKE, FAKE, None, 4, 2, 0, 256, FAKE, L.MOE_FP8_E4M3, None) == L.MOE_ERR_UNSUPPORTED
+    assert cb(FAKE, FAKE, None, 4, 2, 0, 254, FAKE, L.MOE_F32, None) == L.MOE_ERR_UNSUPPORTED
+    assert cb(FAKE, FAKE, None, 4, 2, 0, 256, FAKE + 8, L.MOE_BF16, None) == L.MOE_ERR_ARG
+    assert cb(FAKE + 4, FAKE, None, 4, 2, 0, 256, FAKE, L.MOE_F32, None) == L.MOE_ERR_ARG
     assert L.lib.moe_decode_fp8(None, FAKE, 5, None) == L.MOE_ERR_ARG
     assert L.lib.moe_workspace_init(FAKE + 8, 1024, None) == L.MOE_ERR_WORKSPACE
 
