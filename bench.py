@@ -103,7 +103,8 @@ def main():
 
     from moe_speculative_decoding_amd import _lib as L
     from moe_speculative_decoding_amd import costmodel as cm
-    from moe_speculative_decoding_amd.layer import DeviceLayer, VerifyBuffers, to_device, verify_pass
+    from moe_speculative_decoding_amd.layer import (DeviceLayer, VerifyBuffers, to_device,
+                                                    verify_layer, verify_pass)
     from synth import make_case
     from synth.configs import OLMOE
     from synth.gen import device_layer_weights
@@ -128,18 +129,31 @@ def main():
             ops.append({"n": n, "layer": l, "x": to_device(case.x, dev),
                         "logits": to_device(case.logits, dev),
                         "buf": VerifyBuffers(layers[l], n, dev),
-                        "buf_slot": VerifyBuffers(layers[l], n, dev)})
+                        "buf_slot": VerifyBuffers(layers[l], n, dev),
+                        "buf_layer": VerifyBuffers(layers[l], n, dev),
+                        "buf_layer_slot": VerifyBuffers(layers[l], n, dev)})
     torch.cuda.synchronize()
 
-    # eager pass of both modes: byte counts, and the reference for graph replays
+    # eager pass of both modes, chained and in one launch: byte counts, and
+    # the reference for graph replays
+    def layer_call(op, mode):
+        b = op["buf_layer"] if mode == DEDUP else op["buf_layer_slot"]
+        verify_layer(layers[op["layer"]], b, op["x"], op["logits"], op["n"], mode)
+
     for op in ops:
         verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"], op["n"], DEDUP)
         verify_pass(layers[op["layer"]], op["buf_slot"], op["x"], op["logits"], op["n"], SLOT)
+        layer_call(op, DEDUP)
+        layer_call(op, SLOT)
     torch.cuda.synchronize()
     for op in ops:
-        for b in (op["buf"], op["buf_slot"]):
+        for b in (op["buf"], op["buf_slot"], op["buf_layer"], op["buf_layer_slot"]):
             if L.moe_get_error(b.ws) != L.MOE_OK:
                 raise RuntimeError("device error word set")
+        n = op["n"]
+        if not (torch.equal(op["buf_layer"].out[:n], op["buf"].out[:n]) and
+                torch.equal(op["buf_layer_slot"].out[:n], op["buf_slot"].out[:n])):
+            raise RuntimeError("one-launch and chained passes differ")
         b = op["buf"].bytes.cpu().tolist()
         op["U"] = int(op["buf"].U.item())
         op["union_bytes"], op["requested_bytes"] = int(b[0]), int(b[1])
@@ -159,18 +173,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         for op in ops:
-            lay = layers[op["layer"]]
-            b = op["buf"]
-            L.moe_route_union(op["logits"], op["n"], lay.E, lay.K, b.ids, b.gates, b.U, b.union_ids,
-                              b.offsets, b.perm, b.slot_rank)
-            L.moe_expert_ffn_dedup(lay.shape, lay.weights, op["x"], op["n"], b.U, b.union_ids,
-                                   b.offsets, b.perm, b.y_slots, None, b.bytes, b.ws, b.ws_bytes)
+            layer_call(op, DEDUP)
             torch.cuda.synchronize()
         manifest = {"copy_bytes": src.numel() * 4, "copies": 3,
                     "ops": [{"n": op["n"], "layer": op["layer"], "U": op["U"],
                              "union_bytes": op["union_bytes"],
                              "requested_bytes": op["requested_bytes"]} for op in ops],
-                    "sequence": "per op: route_union_kernel, ffn up kernel, ffn down kernel"}
+                    "kernel": "layer_kernel", "per_op": 1,
+                    "sequence": "per op: one layer_kernel (deduplicating mode)"}
         with open(args.counters, "w") as fh:
             json.dump(manifest, fh)
         log("counter mode: %d operations written to %s" % (len(ops), args.counters))
@@ -199,17 +209,18 @@ def main():
                                      None, b.bytes, b.ws, b.ws_bytes, st)
 
     # ---------------------------------------------------------- the step
-    log("capturing one step (%d operations) in a graph" % len(ops))
-    g_step = capture(lambda: [verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"],
-                                          op["n"], DEDUP) for op in ops])
+    log("capturing one step (%d operations, one launch each) in a graph" % len(ops))
+    g_step = capture(lambda: [layer_call(op, DEDUP) for op in ops])
     for rep in range(3):  # replays must reproduce the eager results exactly
         for op in ops:
-            op["buf"].out.zero_()
+            op["buf_layer"].out.zero_()
         torch.cuda.synchronize()
         g_step.replay()
         torch.cuda.synchronize()
         for op in ops:
-            if not torch.equal(op["buf"].out[:op["n"]], op["out_eager"]):
+            if L.moe_get_error(op["buf_layer"].ws) != L.MOE_OK:
+                raise RuntimeError("device error word set in replay %d" % rep)
+            if not torch.equal(op["buf_layer"].out[:op["n"]], op["out_eager"]):
                 raise RuntimeError("graph replay %d differs from the eager pass" % rep)
     for _ in range(args.warmup):
         g_step.replay()
@@ -248,22 +259,39 @@ def main():
         per_n[n] = {"t_dedup": t[DEDUP], "t_slot": t[SLOT], "union_bytes": ub,
                     "requested_bytes": rb, "U": float(np.mean([op["U"] for op in sel]))}
 
-    # whole operation per n (graph of that n's operations)
+    # whole operation per n (graph of that n's operations): the chain of entry
+    # points, and one launch in each mode
     for n in ns:
         sel = [op for op in ops if op["n"] == n]
         g = capture(lambda: [verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"],
                                          op["n"], DEDUP) for op in sel])
         per_n[n]["t_op"] = time_graph(g, len(sel))
         del g
+        for mode, key in ((DEDUP, "t_layer_dedup"), (SLOT, "t_layer_slot")):
+            g = capture(lambda: [layer_call(op, mode) for op in sel])
+            per_n[n][key] = time_graph(g, len(sel))
+            del g
 
+    # chained step, for comparison with the one-launch step
+    g_chain = capture(lambda: [verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"],
+                                           op["n"], DEDUP) for op in ops])
+    ms_chain = time_graph(g_chain, 1) * 1e3
+    del g_chain
+
+    # the cost model on the one-launch pass (whole operation in either mode)
+    for n in ns:
+        per_n[n]["t_dedup_ffn"], per_n[n]["t_slot_ffn"] = per_n[n]["t_dedup"], per_n[n]["t_slot"]
+        per_n[n]["t_dedup"], per_n[n]["t_slot"] = per_n[n]["t_layer_dedup"], per_n[n]["t_layer_slot"]
     detail = {}
     for n in ns:
         a = cm.aggregate([per_n[n]])
         detail["n=%d" % n] = {
             "U_mean": round(per_n[n]["U"], 3), "u": round(a["u"], 4),
-            "us_op_dedup": round(1e6 * per_n[n]["t_op"], 2),
-            "us_ffn_dedup": round(1e6 * per_n[n]["t_dedup"], 2),
-            "us_ffn_perslot": round(1e6 * per_n[n]["t_slot"], 2),
+            "us_layer_dedup": round(1e6 * per_n[n]["t_layer_dedup"], 2),
+            "us_layer_perslot": round(1e6 * per_n[n]["t_layer_slot"], 2),
+            "us_chain_op_dedup": round(1e6 * per_n[n]["t_op"], 2),
+            "us_chain_ffn_dedup": round(1e6 * per_n[n]["t_dedup_ffn"], 2),
+            "us_chain_ffn_perslot": round(1e6 * per_n[n]["t_slot_ffn"], 2),
             "GBs_dedup_union": round(a["beta_dedup"] / 1e9, 1),
             "GBs_perslot_requested": round(a["beta_slot"] / 1e9, 1),
             "pct_peak_dedup": round(100 * a["beta_dedup"] / 1e9 / PEAK_GBS, 1),
@@ -279,14 +307,15 @@ def main():
                        layers[0].expert_bytes(), [per_n[n]["t_slot"] for n in ns])
     fit["slot_reread_cost"] = round(rr["reread_cost"], 3)
     fit["crossover_n"] = cm.crossover(ns, [per_n[n]["t_slot"] - per_n[n]["t_dedup"] for n in ns])
+    fit["ms_per_step_chained"] = round(ms_chain, 4)
 
     tot_b = sum(per_n[n]["union_bytes"] for n in ns)
-    tot_t = sum(per_n[n]["t_dedup"] for n in ns)
+    tot_t = sum(per_n[n]["t_layer_dedup"] for n in ns)
     achieved = tot_b / tot_t / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
-                "kernel": "moe_expert_ffn_dedup (ffn_stream_kernel up + down), mean over n=1,2,4,8",
-                "bytes_per_launch": "(U + S) * 3*d*f*2 B"}
+                "kernel": "layer_kernel (moe_verify_layer, deduplicating), launches of n=1,2,4,8",
+                "bytes_per_launch": "(U + S) * 3*d*f*2 B (union expert bytes)"}
 
     cold = None
     if args.cold:
@@ -316,8 +345,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "OLMoE-shaped MoE layer verify op (route, union, dedup SwiGLU "
-                               "experts, combine), E=64 K=8 d=2048 f=1024, Markov routing "
-                               "p=%s, n=1,2,4,8, %d layers, HIP-graph step" % (args.p, args.layers),
+                               "experts, combine; one launch per op), E=64 K=8 d=2048 f=1024, "
+                               "Markov routing p=%s, n=1,2,4,8, %d layers, HIP-graph step"
+                               % (args.p, args.layers),
                    "global_batch": sum(ns) * args.layers, "seq_len": 1, "parallelism": "none"},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fit": fit,
     }

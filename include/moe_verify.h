@@ -169,8 +169,35 @@ moe_status moe_combine(const float* y_slots, const float* gates, const float* y_
                        int32_t n, int32_t K, int32_t S, int32_t d, void* out,
                        int32_t out_dtype, moe_stream_t stream);
 
-/* Bytes of workspace the FFN calls need for passes of up to n_max tokens
- * (0 for an invalid shape). */
+/* One MoE layer of a verify pass in one launch: the route of moe_route_topk,
+ * the union of moe_build_union (deduplicating mode), the expert FFN of
+ * moe_expert_ffn_dedup or moe_expert_ffn_perslot (mode) and the combine of
+ * moe_combine, with the same results bit for bit (the pages of each step are
+ * cited at those calls).  Every workgroup routes the pass itself; UP and DOWN
+ * work is handed out with a ticket counter and exchanged between workgroups
+ * through device-coherent stores, with bounded waits.
+ *   logits    (device) f32 [n][E];  x (device) [n][d] in shape->x_dtype
+ *   out       (device) [n][d] of out_dtype (MOE_F32 or MOE_BF16)
+ *   ids, gates (device, optional) [n][K] routing outputs
+ *   U, union_ids, offsets, perm, slot_rank (device, optional: all or none)
+ *             the union outputs of moe_build_union; written in dedup mode only
+ *   y_slots [n][K][d], y_shared [n][S][d] (device f32, optional, 16-byte
+ *             aligned): slot outputs; NULL keeps them in the workspace
+ *   bytes     (device, optional) uint64 [2] as in the FFN calls
+ *   ws        workspace of at least moe_workspace_size(shape, n, mode) bytes,
+ *             zero-filled before its first use; the call leaves its counters
+ *             zero.  Calls sharing a workspace must not overlap in time.
+ * Errors: MOE_ERR_ARG / _UNSUPPORTED / _WORKSPACE on the host; a bounded
+ * device wait that gives up records MOE_ERR_TIMEOUT (moe_get_error). */
+moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const float* logits,
+                            const void* x, int32_t n, int32_t mode, void* out, int32_t out_dtype,
+                            int32_t* ids, float* gates, int32_t* U, int32_t* union_ids,
+                            int32_t* offsets, int32_t* perm, int32_t* slot_rank, float* y_slots,
+                            float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
+                            moe_stream_t stream);
+
+/* Bytes of workspace any FFN or layer call needs for passes of up to n_max
+ * tokens (0 for an invalid shape). */
 size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode);
 
 /* Zero-fill a workspace on `stream` (with a kernel, never a memset node). */

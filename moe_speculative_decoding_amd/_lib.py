@@ -65,6 +65,8 @@ _SIG = {
     "moe_expert_ffn_perslot": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _I, _P, _P,
                                     _P, _P, _P, C.c_size_t, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]),
+    "moe_verify_layer": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I, _I, _P,
+                              _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_workspace_size": (C.c_size_t, [C.POINTER(moe_shape), _I, _I]),
     "moe_workspace_init": (_I, [_P, C.c_size_t, _P]),
     "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
@@ -157,6 +159,17 @@ def moe_expert_ffn_perslot(shape: moe_shape, w: moe_weights, x, n, ids, y_slots,
 def moe_combine(y_slots, gates, y_shared, n, K, S, d, out, out_dtype, stream=None) -> None:
     _check(lib.moe_combine(ptr(y_slots), ptr(gates), ptr(y_shared), n, K, S, d, ptr(out),
                            out_dtype, _stream(stream)), "moe_combine")
+
+
+def moe_verify_layer(shape: moe_shape, w: moe_weights, logits, x, n, mode, out, out_dtype,
+                     ids=None, gates=None, U=None, union_ids=None, offsets=None, perm=None,
+                     slot_rank=None, y_slots=None, y_shared=None, bytes_=None, ws=None,
+                     ws_bytes=0, stream=None) -> None:
+    _check(lib.moe_verify_layer(C.byref(shape), C.byref(w), ptr(logits), ptr(x), n, mode, ptr(out),
+                                out_dtype, ptr(ids), ptr(gates), ptr(U), ptr(union_ids),
+                                ptr(offsets), ptr(perm), ptr(slot_rank), ptr(y_slots),
+                                ptr(y_shared), ptr(bytes_), ptr(ws), ws_bytes, _stream(stream)),
+           "moe_verify_layer")
 
 
 def moe_workspace_size(shape: moe_shape, n_max: int, mode: int) -> int:

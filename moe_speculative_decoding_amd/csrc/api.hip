@@ -9,6 +9,7 @@
 namespace {
 
 using moe::kCtrlBytes;
+using moe::kHOffset;
 
 constexpr int kMaxN = 32, kMaxK = 8, kMaxE = 256, kMaxS = 4, kMaxDim = 65536;
 
@@ -60,6 +61,20 @@ size_t h_bytes(const moe_shape* s, int n) {
   return static_cast<size_t>(n) * (s->K + s->S) * s->f * token_bytes(s->w_dtype);
 }
 
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// workspace regions of the one-launch pass after kHOffset: H in f32, then the
+// slot outputs the caller does not keep
+size_t layer_h_bytes(const moe_shape* s, int n) {
+  return round256(static_cast<size_t>(n) * (s->K + s->S) * s->f * 4);
+}
+size_t layer_ys_bytes(const moe_shape* s, int n) {
+  return round256(static_cast<size_t>(n) * s->K * s->d * 4);
+}
+size_t layer_ysh_bytes(const moe_shape* s, int n) {
+  return round256(static_cast<size_t>(n) * s->S * s->d * 4);
+}
+
 moe_status check_weights(const moe_shape* s, const moe_weights* w) {
   if (w == nullptr) return MOE_ERR_ARG;
   const void* need[3] = {w->w_gate, w->w_up, w->w_down};
@@ -94,7 +109,7 @@ moe_status check_ffn_common(const moe_shape* s, const moe_weights* w, const void
     return MOE_ERR_ARG;
   if (s->S > 0 && (y_shared == nullptr || !aligned(y_shared, 4))) return MOE_ERR_ARG;
   if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
-  if (ws_bytes < kCtrlBytes + h_bytes(s, n)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < kHOffset + h_bytes(s, n)) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
@@ -116,7 +131,7 @@ moe::FfnParams make_params(const moe_shape* s, const moe_weights* w, const void*
   p.x = static_cast<const uint8_t*>(x);
   p.err = static_cast<uint32_t*>(ws);
   p.zeros = static_cast<const uint8_t*>(ws) + moe::kZeroOffset;
-  p.H = static_cast<uint8_t*>(ws) + kCtrlBytes;
+  p.H = static_cast<uint8_t*>(ws) + kHOffset;
   p.y_slots = y_slots;
   p.y_shared = y_shared;
   p.bytes = bytes;
@@ -236,8 +251,72 @@ moe_status moe_combine(const float* y_slots, const float* gates, const float* y_
 size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode) {
   if (check_shape(shape) != MOE_OK || n_max < 1 || n_max > kMaxN) return 0;
   if (mode != MOE_MODE_DEDUP && mode != MOE_MODE_PERSLOT) return 0;
-  const size_t h = h_bytes(shape, n_max);
-  return kCtrlBytes + ((h + 255) / 256) * 256;
+  // the largest need of any entry point: the one-launch pass keeping its
+  // slot outputs in the workspace
+  return kHOffset + layer_h_bytes(shape, n_max) + layer_ys_bytes(shape, n_max) +
+         layer_ysh_bytes(shape, n_max);
+}
+
+moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const float* logits,
+                            const void* x, int32_t n, int32_t mode, void* out, int32_t out_dtype,
+                            int32_t* ids, float* gates, int32_t* U, int32_t* union_ids,
+                            int32_t* offsets, int32_t* perm, int32_t* slot_rank, float* y_slots,
+                            float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
+                            moe_stream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (n < 1 || n > kMaxN) return MOE_ERR_ARG;
+  if (mode != MOE_MODE_DEDUP && mode != MOE_MODE_PERSLOT) return MOE_ERR_ARG;
+  st = check_weights(shape, w);
+  if (st != MOE_OK) return st;
+  if (logits == nullptr || !aligned(logits, 4)) return MOE_ERR_ARG;
+  if (x == nullptr || !aligned(x, 16) || out == nullptr || !aligned(out, 16)) return MOE_ERR_ARG;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((ids != nullptr && !aligned(ids, 4)) || (gates != nullptr && !aligned(gates, 4)))
+    return MOE_ERR_ARG;
+  const void* uni[5] = {U, union_ids, offsets, perm, slot_rank};
+  int given = 0;
+  for (const void* p : uni) {
+    if (p != nullptr && !aligned(p, 4)) return MOE_ERR_ARG;
+    given += p != nullptr;
+  }
+  if (given != 0 && given != 5) return MOE_ERR_ARG;
+  if ((y_slots != nullptr && !aligned(y_slots, 16)) ||
+      (y_shared != nullptr && !aligned(y_shared, 16)))
+    return MOE_ERR_ARG;
+  if (bytes != nullptr && !aligned(bytes, 8)) return MOE_ERR_ARG;
+  if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  const size_t need = kHOffset + layer_h_bytes(shape, n) +
+                      (y_slots == nullptr ? layer_ys_bytes(shape, n) : 0) +
+                      (y_shared == nullptr ? layer_ysh_bytes(shape, n) : 0);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* next = base + kHOffset + layer_h_bytes(shape, n);
+  if (y_slots == nullptr) {
+    y_slots = reinterpret_cast<float*>(next);
+    next += layer_ys_bytes(shape, n);
+  }
+  if (y_shared == nullptr) y_shared = reinterpret_cast<float*>(next);
+  moe::LayerParams lp{};
+  lp.f = make_params(shape, w, x, n, y_slots, y_shared, bytes, ws);
+  lp.f.mode = mode == MOE_MODE_DEDUP ? moe::MODE_DEDUP : moe::MODE_PERSLOT;
+  lp.logits = logits;
+  lp.ids = ids;
+  lp.gates = gates;
+  if (mode == MOE_MODE_DEDUP && given == 5) {
+    lp.U = U;
+    lp.union_ids = union_ids;
+    lp.offsets = offsets;
+    lp.perm = perm;
+    lp.slot_rank = slot_rank;
+  }
+  lp.out = out;
+  lp.out_bf16 = out_dtype == MOE_BF16;
+  lp.epoch = reinterpret_cast<unsigned*>(base + moe::kEpochOffset);
+  lp.up_flags = reinterpret_cast<unsigned*>(base + moe::kFlagsOffset);
+  lp.down_flags = lp.up_flags + moe::kMaxGrid;
+  return hip_status(moe::launch_layer(lp, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, moe_stream_t stream) {
@@ -281,9 +360,7 @@ moe_status moe_get_error(void* ws, moe_stream_t stream) {
 moe_status moe_decode_fp8(const uint8_t* codes, float* out, int64_t count, moe_stream_t stream) {
   if (count < 0 || (count > 0 && (codes == nullptr || out == nullptr))) return MOE_ERR_ARG;
   if (out != nullptr && !aligned(out, 4)) return MOE_ERR_ARG;
-  return moe::launch_decode_fp8(codes, out, count, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? MOE_OK
-             : MOE_ERR_HIP;
+  return hip_status(moe::launch_decode_fp8(codes, out, count, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -20,11 +20,21 @@ enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
 enum { MODE_DEDUP = 0, MODE_PERSLOT = 1 };
 enum : uint32_t { ERRBIT_BAD_IDS = 1u, ERRBIT_TIMEOUT = 2u };
 
-// Workspace: [0, kCtrlBytes) control words (error word first; bytes
-// [kZeroOffset, kZeroOffset + 16) are never written and stay zero), then the
-// intermediate activations H [n*(K+S)][f] in the token storage type.
+// Workspace: [0, kCtrlBytes) control words (error word first, the epoch of
+// the one-launch pass at kEpochOffset; bytes [kZeroOffset, kZeroOffset + 16)
+// are never written and stay zero), then the hand-over flags of the
+// one-launch pass (two arrays of kMaxGrid words), then the intermediate
+// activations H [n*(K+S)][f] (token storage type for the two-kernel FFN, f32
+// for the one-launch pass), then, for the one-launch pass, y_slots and
+// y_shared when the caller keeps none.
 constexpr size_t kCtrlBytes = 256;
+constexpr size_t kEpochOffset = 64;
 constexpr size_t kZeroOffset = 128;
+constexpr int kMaxGrid = 4096;
+constexpr size_t kFlagsOffset = kCtrlBytes;
+constexpr size_t kHOffset = kFlagsOffset + 2 * kMaxGrid * 4;
+// bounded waits: polls of about a microsecond each before a time-out
+constexpr int kSpinLimit = 1 << 21;
 
 // ----------------------------------------------------------------- loads
 __device__ __forceinline__ u32x4 ld16(const void* p) {
@@ -81,6 +91,52 @@ struct FfnParams {
   int lds_slots;          // token slots in LDS (set by the launcher)
 };
 
+// One MoE layer of a verify pass in one launch (fused.hip).
+struct LayerParams {
+  FfnParams f;            // weights, tokens, H (f32), slot outputs, shape, mode
+  const float* logits;    // [n][E]
+  int32_t* ids;           // optional [n][K]
+  float* gates;           // optional [n][K]
+  int32_t* U;             // optional (dedup): union size and arrays
+  int32_t* union_ids;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* slot_rank;
+  void* out;              // [n][d]
+  int out_bf16;
+  unsigned* epoch;        // call counter of the workspace
+  unsigned* up_flags;     // [kMaxGrid] UP range done (tag of the call)
+  unsigned* down_flags;   // [kMaxGrid] DOWN range done
+};
+
+// Tile shapes of the FFN phases (rows per wave R, load steps per chunk SPC
+// for UP and DOWN); the defaults are the measured best on MI355X.
+#ifndef MOE_TUNE_RU
+#define MOE_TUNE_RU 2
+#endif
+#ifndef MOE_TUNE_SPCU
+#define MOE_TUNE_SPCU 2
+#endif
+#ifndef MOE_TUNE_RD
+#define MOE_TUNE_RD 4
+#endif
+#ifndef MOE_TUNE_SPCD
+#define MOE_TUNE_SPCD 2
+#endif
+constexpr int kTuneRU = MOE_TUNE_RU, kTuneSPCU = MOE_TUNE_SPCU;
+constexpr int kTuneRD = MOE_TUNE_RD, kTuneSPCD = MOE_TUNE_SPCD;
+
+// token tile: a group serves at most n tokens (a token names an expert once),
+// so the tile is the next power of two of min(n, 8); larger groups (shared
+// experts of a long pass, trees) take several tiles
+inline int token_tile(int mode, int n) {
+  if (mode == MODE_PERSLOT) return 1;
+  return n >= 5 ? 8 : (n >= 3 ? 4 : (n == 2 ? 2 : 1));
+}
+
+// resident workgroups of a kernel of kBlock threads on the current device
+int resident_blocks(const void* fn, size_t smem);
+
 hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* ids,
                              float* gates, hipStream_t s);
 hipError_t launch_build_union(const int32_t* ids, int n, int K, int E, int32_t* U,
@@ -90,6 +146,7 @@ hipError_t launch_route_union(const float* logits, int n, int E, int K, int32_t*
                               float* gates, int32_t* U, int32_t* union_ids, int32_t* offsets,
                               int32_t* perm, int32_t* slot_rank, hipStream_t s);
 hipError_t launch_expert_ffn(const FfnParams& p, int w_dtype, hipStream_t s);
+hipError_t launch_layer(const LayerParams& lp, int w_dtype, hipStream_t s);
 hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
                           int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

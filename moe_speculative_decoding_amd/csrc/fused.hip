@@ -1,0 +1,291 @@
+// One launch for one MoE layer of a verify pass (gfx950): route, union,
+// expert FFN (deduplicating or per-slot) and combine.
+//
+// The pass is the expert operation of a speculative-decoding verification:
+// top-K routing of every drafted token ("Making Every Verified Token Count:
+// Adaptive Verification for MoE Speculative Decoding", Sec. 2.2, Eq. (4)),
+// the union of the routed experts ("Less Experts, Faster Decoding", Sec. 3,
+// Eq. (1)), the SwiGLU experts streamed once per union expert or once per
+// token-slot ("Speculative Decoding for Mixture-of-Experts Models: Expert
+// Bytes, Kernel Bandwidth and the Best Draft Length", abstract), and the
+// gate-weighted combine (adaptive-verification page, Sec. 2.2).
+//
+// Why one launch: at draft sizes of 1-8 tokens the expert bytes of a pass
+// take 15-70 us to stream, and every kernel boundary costs a drain, a launch
+// and a ramp of a few microseconds.  Here every workgroup routes the pass
+// itself (n*E logits from L2) and builds the union in LDS, so no kernel has
+// to publish it; workgroup b then streams UP range b and DOWN range b of the
+// balanced unit split, and the first workgroups combine.
+//
+// Exchange between workgroups (they run on all eight XCDs, whose L2 caches
+// are not coherent with one another):
+//   - H (f32) and the slot outputs are written with device-scope stores and
+//     read with device-scope loads (stream.h), never through a cache-wide
+//     writeback or invalidate;
+//   - a workgroup publishes a finished range once its stores completed
+//     (vmcnt(0) in every wave, then a barrier) by storing the call's tag in
+//     its UP or DOWN flag; a DOWN group waits for the UP flags of the
+//     workgroups that own its units, the combine for every DOWN flag;
+//   - the tag is the workspace epoch + 1, read at the start; workgroup 0
+//     advances the epoch after it has seen every DOWN flag (so every
+//     workgroup has read it), which retires all flags of the call at once.
+//     There are no read-modify-write atomics on shared words: contended
+//     device-scope atomics serialise at the memory side.
+// The grid is the device's resident capacity for the kernel, so every
+// workgroup runs at once; each wait is bounded besides and records a
+// time-out in the error word instead of hanging.
+#include <map>
+#include <mutex>
+
+#include "route.h"
+#include "stream.h"
+
+namespace moe {
+
+// routing scratch, overlaid on the dynamic LDS before the stream uses it:
+// the union builder's tables, the top-K scratch of each wavefront, then the
+// pass's logits [n][E]
+struct RouteLds {
+  UnionLds ul;
+  int slot_rank[kMaxSlots];
+};
+constexpr size_t kRouteTopkOffset = (sizeof(RouteLds) + 15) / 16 * 16;
+constexpr size_t kRouteLogitsOffset = kRouteTopkOffset + (kBlock / kWave) * sizeof(TopkLds);
+
+// at most 168 VGPRs, so three workgroups fit on a CU (the streaming needs
+// the bytes in flight of three)
+template <int WT, int TCU, int RU, int SPCU, int TCD, int RD, int SPCD>
+#ifndef MOE_TUNE_WPE
+#define MOE_TUNE_WPE 3
+#endif
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MOE_TUNE_WPE)))
+void layer_kernel(LayerParams lp) {
+  constexpr int TCM = TCU > TCD ? TCU : TCD;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  __shared__ int tok_h[2 * TCM];
+  __shared__ float* tok_y[2 * TCM];
+  __shared__ Meta mt;
+  __shared__ int ids_l[kMaxSlots];
+  __shared__ float gates_l[kMaxSlots];
+  __shared__ int U_l;
+  const FfnParams& p = lp.f;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = p.n, K = p.K, E = p.E, S = p.S, nk = n * K;
+
+  // ---- route every token and build the union, in every workgroup; the
+  // logits are copied to LDS first (one round trip to memory for all tokens)
+  RouteLds& rl = *reinterpret_cast<RouteLds*>(xs);
+  float* lg = reinterpret_cast<float*>(xs + kRouteLogitsOffset);
+  {
+    // eight loads per lane in flight at once (clamped in bounds), then the stores
+    constexpr int kPer = 8;
+    const int words = n * E;
+    for (int base = 0; base < words; base += kBlock * kPer) {
+      float v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) v[i] = lp.logits[min(base + i * kBlock + tid, words - 1)];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (base + i * kBlock + tid < words) lg[base + i * kBlock + tid] = v[i];
+    }
+  }
+  __syncthreads();
+  TopkLds* tk = reinterpret_cast<TopkLds*>(xs + kRouteTopkOffset);
+  for (int t = wave; t < n; t += kBlock / kWave) {
+    int id;
+    float g;
+    route_token(lg + t * E, E, K, lane, tk[wave], id, g);
+    if (lane < K) {
+      ids_l[t * K + lane] = id;
+      gates_l[t * K + lane] = g;
+    }
+  }
+  __syncthreads();
+  int U = 0;
+  if (p.mode == MODE_DEDUP) {
+    build_union_256(ids_l, n, K, E, &U_l, mt.b, mt.a, mt.c, rl.slot_rank, rl.ul);
+    __syncthreads();
+    U = uni(U_l);
+  } else {
+    for (int i = tid; i < nk; i += kBlock) mt.a[i] = ids_l[i];
+    __syncthreads();
+  }
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < nk; i += kBlock) {
+      if (lp.ids != nullptr) lp.ids[i] = ids_l[i];
+      if (lp.gates != nullptr) lp.gates[i] = gates_l[i];
+    }
+    if (p.mode == MODE_DEDUP && lp.U != nullptr) {
+      const int cap = p.ucap;
+      for (int i = tid; i < nk; i += kBlock) {
+        lp.perm[i] = mt.c[i];
+        lp.slot_rank[i] = rl.slot_rank[i];
+      }
+      for (int i = tid; i < cap; i += kBlock) lp.union_ids[i] = mt.b[i];
+      for (int i = tid; i <= cap; i += kBlock) lp.offsets[i] = mt.a[i];
+      if (tid == 0) *lp.U = U;
+    }
+    if (tid == 0 && p.bytes != nullptr) {
+      const unsigned long long req =
+          static_cast<unsigned long long>(n) * (K + S) * p.expert_bytes;
+      p.bytes[0] = p.mode == MODE_DEDUP ? static_cast<unsigned long long>(U + S) * p.expert_bytes
+                                        : req;
+      p.bytes[1] = req;
+    }
+  }
+  __syncthreads();  // the routing scratch in xs is dead from here
+
+  // ---- UP range b, then DOWN range b
+  __shared__ unsigned tag_l;
+  if (tid == 0) tag_l = coh_load_u32(lp.epoch) + 1u;
+  __syncthreads();
+  const unsigned tag = tag_l;
+  const int NG = p.mode == MODE_DEDUP ? U + S : n * (K + S);
+  const int upg_u = (p.f + (kBlock / kWave) * RU - 1) / ((kBlock / kWave) * RU);
+  const int upg_d = (p.d + (kBlock / kWave) * RD - 1) / ((kBlock / kWave) * RD);
+  const long long NUu = static_cast<long long>(NG) * upg_u;
+  const long long NUd = static_cast<long long>(NG) * upg_d;
+  const int G = gridDim.x, b = blockIdx.x;
+  const Sync sy{lp.up_flags, tag, NUu, G, upg_u, p.err};
+  {
+    const long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
+    if (lo < hi) run_range<WT, TCU, RU, 2, SPCU, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, sy);
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(lp.up_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  {
+    const long long lo = NUd * b / G, hi = NUd * (b + 1) / G;
+    if (lo < hi) run_range<WT, TCD, RD, 1, SPCD, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, sy);
+    wait_stores();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(lp.down_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- combine: one lane per (token, 4 columns), first workgroups only
+  const int quads = p.d / 4;
+  const int tasks = n * quads;
+  if (b * kBlock >= tasks) return;
+  wait_flags(lp.down_flags, 0, G - 1, tag, p.err);
+  if (b == 0 && tid == 0)  // every workgroup has read the epoch: retire this call's flags
+    __hip_atomic_store(lp.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned ys_size = static_cast<unsigned>(static_cast<size_t>(nk) * p.d * 4);
+  const unsigned sh_size = static_cast<unsigned>(static_cast<size_t>(n) * S * p.d * 4);
+  for (int task = b * kBlock + tid; task < tasks; task += G * kBlock) {
+    const int t = task / quads;
+    const int c = (task - t * quads) * 4;
+    u32x4 yv[8], sv[4];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < K)
+        yv[k] = coh_ld16(p.y_slots,
+                         static_cast<unsigned>(((static_cast<size_t>(t) * K + k) * p.d + c) * 4),
+                         ys_size);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < S)
+        sv[q] = coh_ld16(p.y_shared,
+                         static_cast<unsigned>(((static_cast<size_t>(t) * S + q) * p.d + c) * 4),
+                         sh_size);
+    // the order of moe_combine: k ascending, then the shared experts
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < K) {
+        const float g = gates_l[t * K + k];
+        acc[0] = fmaf(g, __uint_as_float(yv[k].x), acc[0]);
+        acc[1] = fmaf(g, __uint_as_float(yv[k].y), acc[1]);
+        acc[2] = fmaf(g, __uint_as_float(yv[k].z), acc[2]);
+        acc[3] = fmaf(g, __uint_as_float(yv[k].w), acc[3]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < S) {
+        acc[0] += __uint_as_float(sv[q].x);
+        acc[1] += __uint_as_float(sv[q].y);
+        acc[2] += __uint_as_float(sv[q].z);
+        acc[3] += __uint_as_float(sv[q].w);
+      }
+    }
+    const size_t o = static_cast<size_t>(t) * p.d + c;
+    if (lp.out_bf16) {
+      uint2 pk;
+      pk.x = f32_to_bf16_bits(acc[0]) | (static_cast<unsigned>(f32_to_bf16_bits(acc[1])) << 16);
+      pk.y = f32_to_bf16_bits(acc[2]) | (static_cast<unsigned>(f32_to_bf16_bits(acc[3])) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(lp.out) + o) = pk;
+    } else {
+      f32x4 r;
+      r.x = acc[0];
+      r.y = acc[1];
+      r.z = acc[2];
+      r.w = acc[3];
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(lp.out) + o) = r;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <int WT, int TCU, int RU, int SPCU, int TCD, int RD, int SPCD>
+static hipError_t launch_layer_t(const LayerParams& lp0, hipStream_t s) {
+  using CU = StreamCfg<WT, TCU, RU, 2, SPCU>;
+  using CD = StreamCfg<WT, TCD, RD, 1, SPCD>;
+  const FfnParams& p = lp0.f;
+  const void* fn =
+      reinterpret_cast<const void*>(&layer_kernel<WT, TCU, RU, SPCU, TCD, RD, SPCD>);
+  const size_t slot_u = static_cast<size_t>(TCU) * ((p.d + CU::CH - 1) / CU::CH * CU::CH) * CU::T::XB;
+  const size_t slot_d = static_cast<size_t>(TCD) * ((p.f + CD::CH - 1) / CD::CH * CD::CH) * CD::T::XB;
+  const size_t slot = slot_u > slot_d ? slot_u : slot_d;
+  const size_t floor_bytes = kRouteLogitsOffset + static_cast<size_t>(p.n) * p.E * 4;
+  auto need = [&](int slots) {
+    const size_t b = slots * slot;
+    return b > floor_bytes ? b : floor_bytes;
+  };
+  const int slots =
+      2 * slot <= 65536 && resident_blocks(fn, need(2)) >= resident_blocks(fn, need(1)) ? 2 : 1;
+  const size_t smem = need(slots);
+  LayerParams lp = lp0;
+  lp.f.lds_slots = slots;
+  int grid = resident_blocks(fn, smem);
+  if (grid <= 0) return hipErrorInvalidConfiguration;
+#ifdef MOE_TUNE_MAXBPC
+  if (grid > 256 * MOE_TUNE_MAXBPC) grid = 256 * MOE_TUNE_MAXBPC;
+#endif
+  if (grid > kMaxGrid) grid = kMaxGrid;
+  hipLaunchKernelGGL((layer_kernel<WT, TCU, RU, SPCU, TCD, RD, SPCD>), dim3(grid), dim3(kBlock),
+                     smem, s, lp);
+  return hipGetLastError();
+}
+
+template <int WT, int TC>
+static hipError_t launch_layer_tc(const LayerParams& lp, hipStream_t s) {
+  // the tile shapes of the two-kernel FFN
+  constexpr int RU = WT == WT_FP8 ? 4 : kTuneRU;
+  constexpr int SPCU = WT == WT_FP8 ? 1 : kTuneSPCU;
+  constexpr int RD = kTuneRD;
+  constexpr int SPCD = WT == WT_FP8 ? 1 : kTuneSPCD;
+  constexpr int TCU = (WT == WT_FP8 && TC > 4) ? 4 : TC;
+  return launch_layer_t<WT, TCU, RU, SPCU, TC, RD, SPCD>(lp, s);
+}
+
+template <int WT>
+static hipError_t launch_layer_w(const LayerParams& lp, hipStream_t s) {
+  switch (token_tile(lp.f.mode, lp.f.n)) {
+    case 1: return launch_layer_tc<WT, 1>(lp, s);
+    case 2: return launch_layer_tc<WT, 2>(lp, s);
+    case 4: return launch_layer_tc<WT, 4>(lp, s);
+    default: return launch_layer_tc<WT, 8>(lp, s);
+  }
+}
+
+hipError_t launch_layer(const LayerParams& lp, int w_dtype, hipStream_t s) {
+  switch (w_dtype) {
+    case WT_F32: return launch_layer_w<WT_F32>(lp, s);
+    case WT_BF16: return launch_layer_w<WT_BF16>(lp, s);
+    case WT_FP8: return launch_layer_w<WT_FP8>(lp, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,261 @@
+// Router top-K and expert union of one verify pass: device functions shared
+// by the routing kernels and the one-launch layer pass (gfx950).
+//
+// Top-K: "Making Every Verified Token Count: Adaptive Verification for MoE
+// Speculative Decoding", Sec. 2.2, Eq. (4) — the indices of the K largest
+// router scores, normalised (softmax over the K here).
+// Union: "Less Experts, Faster Decoding", Sec. 3, Eq. (1), and the same page
+// family's Eq. (5) / (A2): the distinct experts of all verified tokens; the
+// slot permutation sorts rows by expert as the MLX-LM deduplicating engine
+// does (expert-bytes page, Table 6).
+//
+// Both are integer-exact: top-K compares integer keys built from the fp32
+// bit pattern (no float arithmetic decides a selection) with DPP maxima
+// inside rows of 16 lanes and splits equal keys by the lowest id, and the
+// union uses an LDS
+// histogram per wavefront, DPP prefix sums and a ballot-based match of equal
+// ids, so every output is deterministic.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ top-K
+// Key order = (logit descending, id ascending); NaN below every number,
+// -0.0 equal to +0.0.  The 32-bit key orders the values: every number maps
+// above 1, NaN maps to 1 and 0 marks an entry that is absent (beyond E) or
+// already taken; equal keys are split by the id afterwards.
+__device__ __forceinline__ unsigned topk_key(float v) {
+  unsigned b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;                     // -0.0 -> +0.0
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 1u;  // NaN
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // -inf -> 0x007fffff
+}
+
+// Cross-lane moves inside rows of 16 lanes (DPP): no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp(unsigned v) {
+  return static_cast<unsigned>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// reductions over each row of 16 lanes; every lane of the row ends with it
+__device__ __forceinline__ unsigned row_max_u32(unsigned v) {
+  v = max(v, dpp<kDppQuadXor1>(v));
+  v = max(v, dpp<kDppQuadXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));  // 8 lanes
+  return max(v, dpp<kDppMirror>(v));   // 16 lanes
+}
+__device__ __forceinline__ unsigned row_min_u32(unsigned v) {
+  v = min(v, dpp<kDppQuadXor1>(v));
+  v = min(v, dpp<kDppQuadXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  return min(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum_f32(float v) {
+  v += __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v)));
+  return v + __uint_as_float(dpp<kDppMirror>(__float_as_uint(v)));
+}
+
+// inclusive prefix sum over the wavefront: Hillis-Steele inside each row of
+// 16 lanes, then the row totals added in from scalar registers
+__device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
+  unsigned u = static_cast<unsigned>(v);
+  u += dpp<0x111>(u);  // row_shr:1 (lanes shifted in from outside the row read 0)
+  u += dpp<0x112>(u);  // row_shr:2
+  u += dpp<0x114>(u);  // row_shr:4
+  u += dpp<0x118>(u);  // row_shr:8
+  const unsigned r0 = __builtin_amdgcn_readlane(u, 15);
+  const unsigned r1 = __builtin_amdgcn_readlane(u, 31);
+  const unsigned r2 = __builtin_amdgcn_readlane(u, 47);
+  u += (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+  return static_cast<int>(u);
+}
+
+// Per-wavefront LDS scratch of the top-K.
+struct TopkLds {
+  unsigned long long key[256];  // 64-bit keys of the token's experts (0 beyond E)
+  int sel_id[8];
+  float sel_l[8];
+};
+
+// One wavefront routes one token (`row` in LDS or global memory); lane l
+// holds experts l, l+64, ..., l+64*(J-1) (E <= 64*J <= 256).  Every expert
+// gets a 64-bit key (32-bit value key, then 255 - id, so a larger key is a
+// larger logit or, for equal logits, a lower id), and its rank is the number
+// of keys above it: the experts of rank < K are the top K, in order.  All
+// comparisons are independent (no chain of K dependent rounds), and the keys
+// are read back from LDS as broadcasts.  Lane k (< K) ends with the k-th
+// selected id and its gate: the softmax over the K selected logits, whose
+// first selection holds the maximum.
+template <int J>
+__device__ __forceinline__ void route_token_j(const float* __restrict__ row, int E, int K, int lane,
+                                              TopkLds& sc, int& my_id, float& my_gate) {
+  float val[J];
+  unsigned long long key[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) val[j] = row[min(lane + kWave * j, E - 1)];  // all loads first
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + kWave * j;
+    key[j] = e < E ? (static_cast<unsigned long long>(topk_key(val[j])) << 8) |
+                         static_cast<unsigned>(255 - e)
+                   : 0ull;
+    sc.key[e] = key[j];
+  }
+  __builtin_amdgcn_wave_barrier();  // LDS ops of one wavefront run in order
+  int rank[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) rank[j] = 0;
+#pragma unroll 1
+  for (int i = 0; i < J * kWave; i += 16) {
+    // eight broadcast reads (the same address in every lane) in flight at once
+    u32x4 kk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kk[q] = ld16(&sc.key[i + 2 * q]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const unsigned long long k0 = (static_cast<unsigned long long>(kk[q].y) << 32) | kk[q].x;
+      const unsigned long long k1 = (static_cast<unsigned long long>(kk[q].w) << 32) | kk[q].z;
+#pragma unroll
+      for (int j = 0; j < J; ++j) rank[j] += (k0 > key[j]) + (k1 > key[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E && rank[j] < K) {
+      sc.sel_id[rank[j]] = e;
+      sc.sel_l[rank[j]] = val[j];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  my_id = lane < K ? sc.sel_id[lane] : 0;
+  const float top = sc.sel_l[0];
+  const float l = lane < K ? sc.sel_l[lane] : top;
+  const float ex = lane < K ? expf(l - top) : 0.0f;
+  // lanes 0..K-1 are all in the first row of 16: its DPP sum is the total
+  my_gate = ex / row_sum_f32(ex);
+  __builtin_amdgcn_wave_barrier();  // the scratch may be reused by the next token
+}
+
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int K, int lane,
+                                            TopkLds& sc, int& my_id, float& my_gate) {
+  if (E <= kWave) {
+    route_token_j<1>(row, E, K, lane, sc, my_id, my_gate);
+  } else if (E <= 2 * kWave) {
+    route_token_j<2>(row, E, K, lane, sc, my_id, my_gate);
+  } else {
+    route_token_j<4>(row, E, K, lane, sc, my_id, my_gate);
+  }
+}
+
+// ------------------------------------------------------------------ union
+// Lanes 0..255 of the workgroup: lane s owns slot s (n*K <= 256) and expert
+// e = s (E <= 256).  `ids` may point to LDS or global memory.
+struct UnionLds {
+  int wcnt[4][256];  // per-wave histogram of ids
+  int rank_of[256];  // expert -> union position
+  int start_of[256]; // expert -> first position in perm
+  int wtot_present[4];
+  int wtot_count[4];
+  int bad;
+};
+
+// Every thread of the workgroup calls this (it holds __syncthreads); threads
+// 0..255 do the work.
+__device__ __forceinline__ void build_union_256(const int32_t* ids, int n, int K, int E,
+                                                int32_t* __restrict__ U_out,
+                                                int32_t* __restrict__ union_ids,
+                                                int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ perm,
+                                                int32_t* __restrict__ slot_rank, UnionLds& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool mine = tid < 256;
+  const int nk = n * K;
+  const int cap = nk < E ? nk : E;
+  for (int i = tid; i < 4 * 256; i += blockDim.x) (&sh.wcnt[0][0])[i] = 0;
+  if (tid == 0) sh.bad = 0;
+  __syncthreads();
+
+  const bool act = tid < nk;  // nk <= 256
+  const int id = act ? ids[tid] : 0;
+  if (act) {
+    if (id < 0 || id >= E) {
+      atomicOr(&sh.bad, 1);
+    } else {
+      atomicAdd(&sh.wcnt[wave][id], 1);
+    }
+  }
+  __syncthreads();
+  if (sh.bad) {  // uniform
+    if (tid == 0) *U_out = -1;
+    return;
+  }
+
+  // exclusive scans over experts e = tid of "present" and of the slot count
+  const int e = tid;
+  int c = 0;
+  if (e < E) c = sh.wcnt[0][e] + sh.wcnt[1][e] + sh.wcnt[2][e] + sh.wcnt[3][e];
+  const int pres = (e < E && c > 0) ? 1 : 0;
+  const unsigned long long pmask = __ballot(pres);
+  const int pre_present = __popcll(pmask & ((1ull << lane) - 1ull));
+  const int inc = wave_inclusive_sum(c, lane);
+  if (mine && lane == kWave - 1) {
+    sh.wtot_present[wave] = __popcll(pmask);
+    sh.wtot_count[wave] = inc;
+  }
+  __syncthreads();
+  int base_p = 0, base_c = 0, Utot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) {
+      base_p += sh.wtot_present[w];
+      base_c += sh.wtot_count[w];
+    }
+    Utot += sh.wtot_present[w];
+  }
+  const int rank = base_p + pre_present;
+  const int start = base_c + inc - c;
+  if (mine) {
+    sh.rank_of[e] = rank;
+    sh.start_of[e] = start;
+  }
+  if (pres) {
+    union_ids[rank] = e;
+    offsets[rank] = start;
+  }
+  if (mine) {
+    for (int i = Utot + tid; i < cap; i += 256) union_ids[i] = -1;
+    for (int i = Utot + tid; i <= cap; i += 256) offsets[i] = nk;
+  }
+  if (tid == 0) *U_out = Utot;
+  __syncthreads();
+
+  // stable position of slot tid among the slots of its expert:
+  // slots of earlier waves (histograms) + earlier lanes of this wave with the
+  // same id (8 ballots over the id bits, ids < 256)
+  unsigned long long same = __ballot(act);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int bit = (id >> b) & 1;
+    const unsigned long long ones = __ballot(act && bit);
+    same &= bit ? ones : ~ones;
+  }
+  if (act) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += sh.wcnt[w][id];
+    const int pos = sh.start_of[id] + before + __popcll(same & ((1ull << lane) - 1ull));
+    perm[pos] = tid;
+    slot_rank[tid] = sh.rank_of[id];
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,722 @@
+// Streaming core of the expert FFN kernels (gfx950): weight traits, dot
+// products, the group walk, chunk loads and multiplies, token staging, unit
+// epilogues and the per-range streaming loop.  Included by the two-kernel
+// FFN (ffn.hip) and the one-launch layer pass (fused.hip).
+//
+// For every (expert, slot) pair: a = x W_gate, v = x W_up, h = silu(a) * v,
+// y = h W_down ("Speculative Decoding for Mixture-of-Experts Models: Expert
+// Bytes, Kernel Bandwidth and the Best Draft Length", abstract).  Work is a
+// batched matrix-vector product with at most a handful of tokens per weight
+// row, so it is bound by HBM bandwidth, not by matrix throughput.  Each
+// wavefront owns R weight rows (stored one row per output, so the reduction
+// runs along contiguous memory) and streams them with 16-byte loads, 64 lanes
+// covering 1 KiB of a row per step; the group's tokens sit in LDS as bf16
+// (f32 for f32 weights) and are reused by every row of the workgroup.
+// Products use v_dot2_f32_bf16 (two bf16 MACs, fp32 accumulate); fp8 codes
+// are widened to bf16 pairs exactly with v_cvt_scalef32_pk_bf16_fp8 and the
+// 128x128 block scale is applied once per 16 codes.  Partial sums are
+// combined across the wavefront by recursive halving (each shuffle stage
+// halves the values per lane), so a wave reduces R*T values with about R*T
+// shuffles instead of 6*R*T.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------- coherent exchange
+// Data handed between workgroups of one launch crosses XCDs, whose L2 caches
+// are not coherent with each other.  Stores and loads with the device-scope
+// bit (sc1) write through to, and read from, the coherent level, so only the
+// exchanged words pay for coherence (no cache-wide writeback or invalidate).
+__device__ __forceinline__ void coh_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned coh_load_u32(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at base + off with a device-scope buffer load (bytes at or beyond
+// `size` read as zero)
+constexpr int kAuxSc1 = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ u32x4 coh_ld16(const void* base, unsigned off, unsigned size) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(base), static_cast<short>(0), static_cast<int>(size), 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kAuxSc1);
+}
+// every store this wavefront issued has completed (is visible device-wide
+// for sc1 stores) before anything after this point
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// f32 H words at byte offset off -> one 16-byte LDS vector of the staged type
+template <int XB>
+__device__ __forceinline__ u32x4 coh_h_to_staged(const uint8_t* H, size_t off) {
+  const unsigned o = static_cast<unsigned>(off);
+  if (XB == 4) return coh_ld16(H, o, 0x7fffffffu);
+  const u32x4 a = coh_ld16(H, o, 0x7fffffffu), b = coh_ld16(H, o + 16, 0x7fffffffu);
+  u32x4 r;
+  r.x = f32_to_bf16_bits(__uint_as_float(a.x)) | (static_cast<unsigned>(f32_to_bf16_bits(__uint_as_float(a.y))) << 16);
+  r.y = f32_to_bf16_bits(__uint_as_float(a.z)) | (static_cast<unsigned>(f32_to_bf16_bits(__uint_as_float(a.w))) << 16);
+  r.z = f32_to_bf16_bits(__uint_as_float(b.x)) | (static_cast<unsigned>(f32_to_bf16_bits(__uint_as_float(b.y))) << 16);
+  r.w = f32_to_bf16_bits(__uint_as_float(b.z)) | (static_cast<unsigned>(f32_to_bf16_bits(__uint_as_float(b.w))) << 16);
+  return r;
+}
+
+// Hand-over inside one launch: workgroup c publishes the end of its UP range
+// by storing the call's tag in up_flags[c].  The tag is one more than the
+// epoch word the launch read at its start, so flags of earlier calls never
+// match and nothing has to be reset.
+struct Sync {
+  const unsigned* up_flags;
+  unsigned tag;
+  long long nu_up;  // UP units of the pass
+  int grid;         // workgroups (UP range c = [nu_up*c/grid, nu_up*(c+1)/grid))
+  int upg_up;       // UP units per group
+  uint32_t* err;
+};
+
+// every lane polls its share of the flags until they hold the tag (bounded:
+// a wait that gives up records a time-out in the error word and goes on)
+__device__ __forceinline__ void wait_flags(const unsigned* flags, int c_lo, int c_hi, unsigned tag,
+                                           uint32_t* err) {
+  for (int c = c_lo + static_cast<int>(threadIdx.x); c <= c_hi; c += kBlock) {
+    int spins = 0;
+    while (coh_load_u32(flags + c) != tag) {
+      if (++spins > kSpinLimit) {
+        atomicOr(err, ERRBIT_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// DOWN of group g may start once the workgroups owning g's UP units are done
+__device__ __forceinline__ void wait_group_ready(const Sync& sy, int g) {
+  // owner of UP unit u: the largest c with floor(nu_up * c / grid) <= u
+  const long long u0 = static_cast<long long>(g) * sy.upg_up;
+  const long long u1 = u0 + sy.upg_up - 1;
+  const int c_lo = static_cast<int>(((u0 + 1) * sy.grid - 1) / sy.nu_up);
+  const int c_hi = static_cast<int>(((u1 + 1) * sy.grid - 1) / sy.nu_up);
+  wait_flags(sy.up_flags, c_lo, c_hi, sy.tag, sy.err);
+}
+
+template <int WT>
+struct WTraits;
+// VEC: weight elements per 16-byte load; SPC: load steps per staged chunk;
+// EB: bytes per weight element; XB: bytes per staged token element.
+template <>
+struct WTraits<WT_F32> {
+  static constexpr int VEC = 4, SPC = 4, EB = 4, XB = 4;
+};
+template <>
+struct WTraits<WT_BF16> {
+  static constexpr int VEC = 8, SPC = 4, EB = 2, XB = 2;
+};
+template <>
+struct WTraits<WT_FP8> {
+  static constexpr int VEC = 16, SPC = 2, EB = 1, XB = 2;
+};
+
+// ------------------------------------------------------------ dot products
+// acc += <16 bytes of weights, VEC token elements in LDS>
+template <int WT>
+struct Dot;
+
+template <>
+struct Dot<WT_F32> {
+  struct W {
+    u32x4 v;
+  };
+  static __device__ __forceinline__ W prep(u32x4 v) { return W{v}; }
+  static __device__ __forceinline__ float run(const W& w, const uint8_t* xs, float acc, float) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(xs);
+    acc = fmaf(__uint_as_float(w.v.x), x.x, acc);
+    acc = fmaf(__uint_as_float(w.v.y), x.y, acc);
+    acc = fmaf(__uint_as_float(w.v.z), x.z, acc);
+    acc = fmaf(__uint_as_float(w.v.w), x.w, acc);
+    return acc;
+  }
+};
+
+template <>
+struct Dot<WT_BF16> {
+  struct W {
+    u32x4 v;
+  };
+  static __device__ __forceinline__ W prep(u32x4 v) { return W{v}; }
+  static __device__ __forceinline__ float run(const W& w, const uint8_t* xs, float acc, float) {
+    const u32x4 x = ld16(xs);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.v.x), as_bf16x2(x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.v.y), as_bf16x2(x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.v.z), as_bf16x2(x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.v.w), as_bf16x2(x.w), acc, false);
+    return acc;
+  }
+};
+
+template <>
+struct Dot<WT_FP8> {
+  struct W {
+    bf16x2 p[8];
+  };
+  static __device__ __forceinline__ W prep(u32x4 v) {
+    W w;
+    w.p[0] = fp8x2_to_bf16x2<false>(v.x);
+    w.p[1] = fp8x2_to_bf16x2<true>(v.x);
+    w.p[2] = fp8x2_to_bf16x2<false>(v.y);
+    w.p[3] = fp8x2_to_bf16x2<true>(v.y);
+    w.p[4] = fp8x2_to_bf16x2<false>(v.z);
+    w.p[5] = fp8x2_to_bf16x2<true>(v.z);
+    w.p[6] = fp8x2_to_bf16x2<false>(v.w);
+    w.p[7] = fp8x2_to_bf16x2<true>(v.w);
+    return w;
+  }
+  // the 16 codes of one load lie in one 128-wide block: one scale
+  static __device__ __forceinline__ float run(const W& w, const uint8_t* xs, float acc,
+                                              float scale) {
+    const u32x4 x0 = ld16(xs), x1 = ld16(xs + 16);
+    float t = 0.0f;
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[0], as_bf16x2(x0.x), t, false);
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[1], as_bf16x2(x0.y), t, false);
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[2], as_bf16x2(x0.z), t, false);
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[3], as_bf16x2(x0.w), t, false);
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[4], as_bf16x2(x1.x), t, false);
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[5], as_bf16x2(x1.y), t, false);
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[6], as_bf16x2(x1.z), t, false);
+    t = __builtin_amdgcn_fdot2_f32_bf16(w.p[7], as_bf16x2(x1.w), t, false);
+    return fmaf(scale, t, acc);
+  }
+};
+
+// --------------------------------------------------- wavefront reduction
+// Recursive halving: N partial sums per lane -> every lane holds the total
+// of value index (lane >> (6 - log2 N)).
+template <int N>
+struct Halve {
+  static __device__ __forceinline__ void run(float* v, int lane, int o) {
+    const bool upper = (lane & o) != 0;
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      const float send = upper ? v[k] : v[k + N / 2];
+      const float keep = upper ? v[k + N / 2] : v[k];
+      v[k] = keep + __shfl_xor(send, o);
+    }
+    Halve<N / 2>::run(v, lane, o >> 1);
+  }
+};
+template <>
+struct Halve<1> {
+  static __device__ __forceinline__ void run(float* v, int, int o) {
+    for (; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o);
+  }
+};
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// ------------------------------------------------------------------ groups
+struct Group {
+  int e;       // expert index (routed or shared)
+  int shared;  // 1 for a shared expert
+  int cnt;     // tokens served
+  int first;   // dedup routed: offset into perm; per-slot: slot or shared pair index
+  int s_idx;   // shared expert index (dedup) or (token * S + s) pair (per-slot)
+};
+
+// ------------------------------------------------------ routing metadata
+// The union arrays (dedup) or the slot ids (per-slot) are copied to LDS once
+// per workgroup before the stream starts: loads issued later would complete
+// in order behind the weight prefetch, so reading them from global memory in
+// the loop would drain the prefetch every time.
+constexpr int kMaxSlots = 256;  // n*K <= 32*8
+struct Meta {
+  int a[kMaxSlots + 1];  // dedup: offsets[0..cap]; per-slot: ids[0..nK)
+  int b[kMaxSlots];      // dedup: union_ids[0..cap)
+  int c[kMaxSlots];      // dedup: perm[0..nK)
+};
+
+__device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
+  const int nk = p.n * p.K;
+  if (p.mode == MODE_DEDUP) {
+    for (int i = threadIdx.x; i <= p.ucap; i += kBlock) m.a[i] = p.offsets[i];
+    for (int i = threadIdx.x; i < p.ucap; i += kBlock) m.b[i] = p.union_ids[i];
+    for (int i = threadIdx.x; i < nk; i += kBlock) m.c[i] = p.perm[i];
+  } else {
+    for (int i = threadIdx.x; i < nk; i += kBlock) m.a[i] = p.ids[i];
+  }
+}
+
+// token j of a group: its row in x, its row in H and its output row
+__device__ __forceinline__ void token_of(const FfnParams& p, const Meta& mt, const Group& G, int j,
+                                         int& xrow, int& hrow, float*& yrow) {
+  const int nk = p.n * p.K;
+  if (p.mode == MODE_DEDUP) {
+    if (!G.shared) {
+      const int slot = mt.c[G.first + j];
+      xrow = slot / p.K;
+      hrow = G.first + j;
+      yrow = p.y_slots + static_cast<size_t>(slot) * p.d;
+    } else {
+      xrow = j;
+      hrow = nk + G.s_idx * p.n + j;
+      yrow = p.y_shared + (static_cast<size_t>(j) * p.S + G.s_idx) * p.d;
+    }
+  } else {
+    if (!G.shared) {
+      xrow = G.first / p.K;
+      hrow = G.first;
+      yrow = p.y_slots + static_cast<size_t>(G.first) * p.d;
+    } else {
+      xrow = G.s_idx / p.S;
+      hrow = nk + G.s_idx;
+      yrow = p.y_shared + static_cast<size_t>(G.s_idx) * p.d;
+    }
+  }
+}
+
+// ------------------------------------------------------------ the walk
+// One phase (up: gate/up rows, or down rows) is a list of units: (group g,
+// row block of 4*R rows), groups in order, row blocks in order.  Workgroup b
+// owns the contiguous unit range [b*NU/G, (b+1)*NU/G), so every workgroup
+// streams the same number of bytes and all finish together.  It walks its
+// range chunk by chunk (K split in chunks of SPC load steps): for each group
+// segment, for each token tile of that group, for each unit, for each chunk.
+// The walk is the same for every lane of the workgroup.
+struct Walk {
+  int g, tile, u, kc, done;
+  int ntile, seg_lo, seg_hi;
+  int valid;  // expert id in range
+  Group G;
+};
+
+// group g of a phase: dedup 0..U-1 routed union experts, then the S shared;
+// per-slot 0..n*K-1 slots, then the n*S (token, shared expert) pairs
+__device__ __forceinline__ void group_at(const FfnParams& p, const Meta& mt, int U, int g,
+                                         Group& G) {
+  if (p.mode == MODE_DEDUP) {
+    if (g < U) {
+      G.e = mt.b[g];
+      G.shared = 0;
+      G.first = mt.a[g];
+      G.cnt = mt.a[g + 1] - G.first;
+      G.s_idx = 0;
+    } else {
+      G.e = g - U;
+      G.shared = 1;
+      G.first = 0;
+      G.cnt = p.n;
+      G.s_idx = g - U;
+    }
+    return;
+  }
+  const int nk = p.n * p.K;
+  if (g < nk) {
+    G.e = mt.a[g];
+    G.shared = 0;
+    G.first = g;
+    G.cnt = 1;
+    G.s_idx = 0;
+  } else {
+    const int q = g - nk;
+    G.e = q % p.S;
+    G.shared = 1;
+    G.first = q;
+    G.cnt = 1;
+    G.s_idx = q;
+  }
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int TC>
+__device__ __forceinline__ void walk_group(const FfnParams& p, const Meta& mt, int U, Walk& w,
+                                           int g, long long lo, long long hi, int upg) {
+  // every field is the same in all lanes: keep the walk in scalar registers
+  w.g = uni(g);
+  group_at(p, mt, U, w.g, w.G);
+  w.G.e = uni(w.G.e);
+  w.G.shared = uni(w.G.shared);
+  w.G.cnt = uni(w.G.cnt);
+  w.G.first = uni(w.G.first);
+  w.G.s_idx = uni(w.G.s_idx);
+  w.valid = w.G.shared || (w.G.e >= 0 && w.G.e < p.E);
+  w.ntile = (w.G.cnt + TC - 1) / TC;
+  w.tile = 0;
+  const long long glo = static_cast<long long>(g) * upg;
+  w.seg_lo = uni(static_cast<int>(lo > glo ? lo : glo));
+  w.seg_hi = uni(static_cast<int>(hi < glo + upg ? hi : glo + upg));
+  w.u = w.seg_lo;
+  w.kc = 0;
+}
+
+template <int TC>
+__device__ __forceinline__ void walk_next(const FfnParams& p, const Meta& mt, int U, Walk& w,
+                                          int nchunks, long long lo, long long hi, int upg) {
+  if (++w.kc < nchunks) return;
+  w.kc = 0;
+  if (++w.u < w.seg_hi) return;
+  if (++w.tile < w.ntile) {
+    w.u = w.seg_lo;
+    return;
+  }
+  if (w.seg_hi >= hi) {
+    w.done = 1;
+    return;
+  }
+  walk_group<TC>(p, mt, U, w, w.g + 1, lo, hi, upg);
+}
+
+// ------------------------------------------------------- streaming kernel
+// UP (NMAT = 2): rows j of W_gate and W_up (Kdim = d) -> H[token][j] = silu(a) * v.
+// DOWN (NMAT = 1): rows c of W_down (Kdim = f, tokens read from H) -> y[slot][c].
+// Each wave owns R rows of the current unit; the weights of the next chunk
+// are in flight while the current chunk is multiplied (two register buffers).
+template <int WT, int TC, int R, int NMAT, int SPC>
+struct StreamCfg {
+  using T = WTraits<WT>;
+  static constexpr int STEP = kWave * T::VEC;  // elements per load step
+  static constexpr int CH = SPC * STEP;        // elements per chunk
+  static constexpr int V = NMAT * R * TC;      // partial sums per lane
+  static constexpr int SH = 6 - ilog2(V);
+  static_assert((V & (V - 1)) == 0 && V <= 64, "values per lane must be a power of two <= 64");
+  static_assert(NMAT == 1 || V >= 2, "gate/up pairing needs two values");
+};
+
+// matrix MI's base pointer (0 gate, 1 up, 2 down), routed or shared; the
+// fields are read with constant indices so the argument block stays in
+// scalar registers (a selected address would force a copy to scratch)
+template <int MI>
+__device__ __forceinline__ const uint8_t* wptr(const FfnParams& p, int shared) {
+  const uint8_t* a = p.w[MI];
+  const uint8_t* b = p.shw[MI];
+  return shared ? b : a;
+}
+template <int MI>
+__device__ __forceinline__ const float* sptr(const FfnParams& p, int shared) {
+  const float* a = p.s[MI];
+  const float* b = p.shs[MI];
+  return shared ? b : a;
+}
+
+template <int WT, int TC, int R, int NMAT, int SPC>
+__device__ __forceinline__ void load_chunk(const FfnParams& p, const Group& G, int live, int urel,
+                                           int kc, int rows, int Kdim, int lane, int wave,
+                                           u32x4 (&buf)[NMAT][SPC][R], float (&sc)[NMAT][SPC]) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  using T = typename C::T;
+  // Every lane issues every load, outside any branch, and nothing inspects the
+  // loaded value before the multiply, so the next chunk stays in flight while
+  // the current one is used.  Masked lanes read 16 zero bytes of the
+  // workspace's control block instead of weights.
+  const int r0 = urel * (kBlock / kWave) * R + wave * R;
+  const int rv = live ? max(0, min(R, rows - r0)) : 0;
+  const size_t row_bytes = static_cast<size_t>(Kdim) * T::EB;
+  const size_t mat = static_cast<size_t>(rows) * row_bytes;
+  const int kb = Kdim / 128;
+  const int e = rv > 0 ? G.e : 0;
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    const uint8_t* base = (NMAT == 1 ? wptr<2>(p, G.shared)
+                                     : (m == 0 ? wptr<0>(p, G.shared) : wptr<1>(p, G.shared))) +
+                          static_cast<size_t>(e) * mat + static_cast<size_t>(r0) * row_bytes;
+    const float* sbase = nullptr;
+    if (WT == WT_FP8)
+      sbase = (NMAT == 1 ? sptr<2>(p, G.shared)
+                         : (m == 0 ? sptr<0>(p, G.shared) : sptr<1>(p, G.shared))) +
+              (static_cast<size_t>(e) * (rows / 128) + (rv > 0 ? r0 / 128 : 0)) * kb;
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+      const int k = kc * C::CH + s * C::STEP + lane * T::VEC;
+      const bool kin = k < Kdim;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool ok = kin && r < rv;
+        const uint8_t* a = ok ? base + static_cast<size_t>(r) * row_bytes +
+                                    static_cast<size_t>(k) * T::EB
+                              : p.zeros;
+        // streamed once: non-temporal, so the weights do not evict tokens,
+        // H and routing data from the caches (measured: +13% bandwidth)
+        buf[m][s][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+      }
+      if (WT == WT_FP8) {
+        const bool ok = kin && rv > 0;
+        sc[m][s] = *(ok ? sbase + (k >> 7) : reinterpret_cast<const float*>(p.zeros));
+      }
+    }
+  }
+}
+
+template <int WT, int TC, int R, int NMAT, int SPC, int NT>
+__device__ __forceinline__ void mul_chunk_nt(int kc, int Kpad, int lane, const uint8_t* xs,
+                                             const u32x4 (&buf)[NMAT][SPC][R],
+                                             const float (&sc)[NMAT][SPC], float* acc) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  using T = typename C::T;
+#pragma unroll
+  for (int s = 0; s < SPC; ++s) {
+    const int k = kc * C::CH + s * C::STEP + lane * T::VEC;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const typename Dot<WT>::W wt = Dot<WT>::prep(buf[m][s][r]);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          float& a = acc[(m * R + r) * TC + tt];
+          a = Dot<WT>::run(wt, xs + (static_cast<size_t>(tt) * Kpad + k) * T::XB, a,
+                           WT == WT_FP8 ? sc[m][s] : 0.0f);
+        }
+      }
+    }
+  }
+}
+
+// all TC staged tokens are multiplied: tokens beyond the tile's count are
+// zero in LDS, and a branch on the count would cost the prefetch pipeline
+template <int WT, int TC, int R, int NMAT, int SPC>
+__device__ __forceinline__ void mul_chunk(int kc, int Kpad, int lane, const uint8_t* xs,
+                                          const u32x4 (&buf)[NMAT][SPC][R],
+                                          const float (&sc)[NMAT][SPC], float* acc) {
+  mul_chunk_nt<WT, TC, R, NMAT, SPC, TC>(kc, Kpad, lane, xs, buf, sc, acc);
+}
+
+// tokens of (group, tile) -> LDS [TC][Kpad], zero beyond Kdim and beyond the
+// tile; the H row and output row of every token go to LDS too, so the
+// epilogue issues no global loads
+template <int WT, int TC, bool FROM_H, bool COH>
+__device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt, const Walk& w,
+                                             int Kdim, int Kpad, uint8_t* xs, int* tok_h,
+                                             float** tok_y) {
+  using T = WTraits<WT>;
+  constexpr int EPV = 16 / T::XB;  // elements per 16-byte vector
+  const int vpt = Kpad / EPV;
+  const int nt = min(TC, w.G.cnt - w.tile * TC);
+  if (threadIdx.x < TC) {
+    int xrow = 0, hrow = 0;
+    float* yrow = nullptr;
+    if (static_cast<int>(threadIdx.x) < nt) token_of(p, mt, w.G, w.tile * TC + threadIdx.x, xrow, hrow, yrow);
+    tok_h[threadIdx.x] = hrow;
+    tok_y[threadIdx.x] = yrow;
+  }
+  for (int v = threadIdx.x; v < TC * vpt; v += kBlock) {
+    const int tt = v / vpt;
+    const int k = (v - tt * vpt) * EPV;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (tt < nt && k < Kdim) {
+      int xrow, hrow;
+      float* yrow;
+      token_of(p, mt, w.G, w.tile * TC + tt, xrow, hrow, yrow);
+      if (FROM_H && COH) {
+        // H holds f32 written by other workgroups: read it coherently and
+        // round to the staged type here
+        const size_t off = (static_cast<size_t>(hrow) * Kdim + k) * 4;
+        val = coh_h_to_staged<T::XB>(p.H, off);
+      } else {
+        const uint8_t* src = FROM_H ? p.H + static_cast<size_t>(hrow) * Kdim * T::XB
+                                    : p.x + static_cast<size_t>(xrow) * Kdim * T::XB;
+        val = ld16(src + static_cast<size_t>(k) * T::XB);
+      }
+    }
+    st16(xs + static_cast<size_t>(v) * 16, val);
+  }
+}
+
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
+__device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int urel, int rows,
+                                            int lane, int wave, const int* tok_h,
+                                            float* const* tok_y, float* acc) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  Halve<C::V>::run(acc, lane, 32);
+  const int r0 = urel * (kBlock / kWave) * R + wave * R;
+  const int rv = max(0, min(R, rows - r0));
+  if (NMAT == 2) {
+    const float v = __shfl_xor(acc[0], 32);  // the up value pairs with this gate value
+    if (lane < 32 && (lane & ((1 << C::SH) - 1)) == 0) {
+      const int idx = lane >> C::SH;
+      const int r = idx / TC, tt = idx - (idx / TC) * TC;
+      if (r < rv && tt < nt) {
+        const float a = acc[0];
+        const float h = a / (1.0f + expf(-a)) * v;
+        const size_t off = static_cast<size_t>(tok_h[tt]) * rows + r0 + r;
+        if (COH) {
+          coh_store(reinterpret_cast<float*>(p.H) + off, h);
+        } else if (WTraits<WT>::XB == 4) {
+          reinterpret_cast<float*>(p.H)[off] = h;
+        } else {
+          reinterpret_cast<uint16_t*>(p.H)[off] = f32_to_bf16_bits(h);
+        }
+      }
+    }
+  } else {
+    if ((lane & ((1 << C::SH) - 1)) == 0) {
+      const int idx = lane >> C::SH;
+      const int r = idx / TC, tt = idx - (idx / TC) * TC;
+      if (r < rv && tt < nt) {
+        if (COH) {
+          coh_store(tok_y[tt] + r0 + r, acc[0]);
+        } else {
+          tok_y[tt][r0 + r] = acc[0];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::V; ++i) acc[i] = 0.0f;
+}
+
+// ------------------------------------------------------------ one range
+// Streams units [lo, hi) of one phase.  UP (NMAT = 2) reads W_gate and W_up
+// rows against the tokens x; DOWN (NMAT = 1) reads W_down rows against H.
+// COH: H and the outputs are exchanged between workgroups of one launch
+// (H in f32 with coherent stores and loads, and each DOWN group waits for the
+// flags of the workgroups that own its UP units); otherwise a kernel boundary
+// separates them.
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
+__device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, int U, long long lo,
+                                          long long hi, uint8_t* xs, int* tok_h, float** tok_y,
+                                          const Sync& sy) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  constexpr bool UP = NMAT == 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = UP ? p.f : p.d;
+  const int Kdim = UP ? p.d : p.f;
+  const int nchunks = (Kdim + C::CH - 1) / C::CH;
+  const int Kpad = nchunks * C::CH;
+  const int upg = (rows + (kBlock / kWave) * R - 1) / ((kBlock / kWave) * R);
+
+  u32x4 b0[NMAT][SPC][R], b1[NMAT][SPC][R];
+  float s0[NMAT][SPC], s1[NMAT][SPC];
+  float acc[C::V];
+#pragma unroll
+  for (int i = 0; i < C::V; ++i) acc[i] = 0.0f;
+
+  // Fast path: the range touches at most two groups, each within one token
+  // tile, and LDS has two token slots: stage both up front, then stream with
+  // no load other than the weights (a load that must be waited for would,
+  // with in-order completion, drain the weight prefetch).
+  const int g0 = uni(static_cast<int>(lo / upg));
+  const int g1 = uni(static_cast<int>((hi - 1) / upg));
+  Group G0, G1;
+  group_at(p, mt, U, g0, G0);
+  group_at(p, mt, U, g1, G1);
+  G0.e = uni(G0.e); G0.shared = uni(G0.shared); G0.cnt = uni(G0.cnt);
+  G0.first = uni(G0.first); G0.s_idx = uni(G0.s_idx);
+  G1.e = uni(G1.e); G1.shared = uni(G1.shared); G1.cnt = uni(G1.cnt);
+  G1.first = uni(G1.first); G1.s_idx = uni(G1.s_idx);
+  const bool fast = g1 - g0 <= 1 && G0.cnt <= TC && G1.cnt <= TC && (g1 == g0 || p.lds_slots >= 2);
+  if (fast) {
+    const int v0 = G0.shared || (G0.e >= 0 && G0.e < p.E);
+    const int v1 = G1.shared || (G1.e >= 0 && G1.e < p.E);
+    if (UP && threadIdx.x == 0 && (!v0 || !v1)) atomicOr(p.err, ERRBIT_BAD_IDS);
+    const int base0 = g0 * upg;
+    const int nct = static_cast<int>(hi - lo) * nchunks;  // chunks of this range
+    const size_t slot_bytes = static_cast<size_t>(TC) * Kpad * C::T::XB;
+    uint8_t* xs1 = xs + (g1 != g0 ? slot_bytes : 0);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, G0, v0, static_cast<int>(lo) - base0, 0, rows, Kdim, lane,
+                                     wave, b0, s0);
+    if (COH && !UP) {
+      wait_group_ready(sy, g0);
+      if (g1 != g0) wait_group_ready(sy, g1);
+    }
+    {
+      Walk w;
+      w.G = G0;
+      w.tile = 0;
+      stage_tokens<WT, TC, !UP, COH>(p, mt, w, Kdim, Kpad, xs, tok_h, tok_y);
+      if (g1 != g0) {
+        w.G = G1;
+        stage_tokens<WT, TC, !UP, COH>(p, mt, w, Kdim, Kpad, xs1, tok_h + TC, tok_y + TC);
+      }
+    }
+    __syncthreads();
+    // chunk c: unit lo + c / nchunks, K chunk c % nchunks.  One step
+    // prefetches chunk cc + 1 into one buffer and multiplies chunk cc from
+    // the other.  The loop runs whole pairs of steps, so on every path back
+    // to its head the only loads in flight are the prefetch of the next
+    // chunk (a half-finished pair would leave a buffer that the head
+    // overwrites in flight, and the compiler would wait for every load there).
+    auto step = [&](int cc, u32x4 (&bl)[NMAT][SPC][R], float (&sl)[NMAT][SPC],
+                    const u32x4 (&bm)[NMAT][SPC][R], const float (&sm)[NMAT][SPC],
+                    bool prefetch) {
+      if (prefetch) {
+        const int un = static_cast<int>(lo) + (cc + 1) / nchunks;  // unit of the next chunk
+        const int kn = (cc + 1) - ((cc + 1) / nchunks) * nchunks;
+        const int sn = un - base0 >= upg;  // next chunk in the second group
+        load_chunk<WT, TC, R, NMAT, SPC>(p, sn ? G1 : G0, (cc + 1 < nct) && (sn ? v1 : v0),
+                                         un - base0 - (sn ? upg : 0), kn, rows, Kdim, lane, wave,
+                                         bl, sl);
+#ifdef MOE_TUNE_SCHED
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+      }
+      const int uc = static_cast<int>(lo) + cc / nchunks;
+      const int kcc = cc - (cc / nchunks) * nchunks;
+      const int sc_ = uc - base0 >= upg;
+      mul_chunk<WT, TC, R, NMAT, SPC>(kcc, Kpad, lane, sc_ ? xs1 : xs, bm, sm, acc);
+      if (kcc == nchunks - 1)
+        finish_unit<WT, TC, R, NMAT, SPC, COH>(p, sc_ ? G1.cnt : G0.cnt, uc - base0 - (sc_ ? upg : 0),
+                                          rows, lane, wave, tok_h + (sc_ ? TC : 0),
+                                          tok_y + (sc_ ? TC : 0), acc);
+    };
+    int c = 0;
+    for (; c + 2 <= nct; c += 2) {
+      step(c, b1, s1, b0, s0, true);
+      step(c + 1, b0, s0, b1, s1, true);
+    }
+    if (c < nct) step(c, b1, s1, b0, s0, false);  // odd count: the last chunk is in b0
+    return;
+  }
+
+  // General path: restage tokens at every (group, token tile) change.
+  Walk cur;
+  cur.done = 0;
+  walk_group<TC>(p, mt, U, cur, g0, lo, hi, upg);
+  if (UP && !cur.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+
+  load_chunk<WT, TC, R, NMAT, SPC>(p, cur.G, cur.valid, cur.u - cur.g * upg, cur.kc, rows, Kdim,
+                                   lane, wave, b0, s0);
+  if (COH && !UP) wait_group_ready(sy, g0);
+  stage_tokens<WT, TC, !UP, COH>(p, mt, cur, Kdim, Kpad, xs, tok_h, tok_y);
+  __syncthreads();
+
+  Walk nxt = cur;
+  walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
+  // two chunks per trip so the register buffers keep fixed names
+  while (true) {
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, nxt.valid && !nxt.done, nxt.u - nxt.g * upg, nxt.kc,
+                                     rows, Kdim, lane, wave, b1, s1);
+    mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b0, s0, acc);
+    if (cur.kc == nchunks - 1)
+      finish_unit<WT, TC, R, NMAT, SPC, COH>(p, min(TC, cur.G.cnt - cur.tile * TC), cur.u - cur.g * upg,
+                                        rows, lane, wave, tok_h, tok_y, acc);
+    if (nxt.done) break;
+    if (nxt.g != cur.g || nxt.tile != cur.tile) {
+      if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+      __syncthreads();
+      if (COH && !UP && nxt.g != cur.g) wait_group_ready(sy, nxt.g);
+      stage_tokens<WT, TC, !UP, COH>(p, mt, nxt, Kdim, Kpad, xs, tok_h, tok_y);
+      __syncthreads();
+    }
+    cur = nxt;
+    walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
+
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, nxt.valid && !nxt.done, nxt.u - nxt.g * upg, nxt.kc,
+                                     rows, Kdim, lane, wave, b0, s0);
+    mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b1, s1, acc);
+    if (cur.kc == nchunks - 1)
+      finish_unit<WT, TC, R, NMAT, SPC, COH>(p, min(TC, cur.G.cnt - cur.tile * TC), cur.u - cur.g * upg,
+                                        rows, lane, wave, tok_h, tok_y, acc);
+    if (nxt.done) break;
+    if (nxt.g != cur.g || nxt.tile != cur.tile) {
+      if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
+      __syncthreads();
+      if (COH && !UP && nxt.g != cur.g) wait_group_ready(sy, nxt.g);
+      stage_tokens<WT, TC, !UP, COH>(p, mt, nxt, Kdim, Kpad, xs, tok_h, tok_y);
+      __syncthreads();
+    }
+    cur = nxt;
+    walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
+  }
+}
+
+}  // namespace moe

@@ -92,3 +92,18 @@ def verify_pass(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor, logits:
         L.moe_expert_ffn_perslot(layer.shape, layer.weights, x, n, buf.ids, buf.y_slots, ysh,
                                  buf.bytes, buf.ws, buf.ws_bytes, stream)
     L.moe_combine(buf.y_slots, buf.gates, ysh, n, K, S, d, buf.out, buf.out_dtype, stream)
+
+
+def verify_layer(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor, logits: torch.Tensor,
+                 n: int, mode: int = L.MOE_MODE_DEDUP, stream=None, keep: bool = True) -> None:
+    """The same pass in one launch (moe_verify_layer).  keep=False leaves the
+    routing, union and slot outputs to the workspace and writes only out."""
+    ysh = buf.y_shared if layer.S > 0 else None
+    if keep:
+        L.moe_verify_layer(layer.shape, layer.weights, logits, x, n, mode, buf.out, buf.out_dtype,
+                           buf.ids, buf.gates, buf.U, buf.union_ids, buf.offsets, buf.perm,
+                           buf.slot_rank, buf.y_slots, ysh, buf.bytes, buf.ws, buf.ws_bytes,
+                           stream)
+    else:
+        L.moe_verify_layer(layer.shape, layer.weights, logits, x, n, mode, buf.out, buf.out_dtype,
+                           ws=buf.ws, ws_bytes=buf.ws_bytes, stream=stream)

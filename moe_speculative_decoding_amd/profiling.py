@@ -1,7 +1,7 @@
-"""Summaries of rocprofv3 output for the expert-FFN kernels (host-side text tools).
+"""Summaries of rocprofv3 output for the verify-pass kernels (host-side text tools).
 
     python -m moe_speculative_decoding_amd.profiling traffic FETCH_DIR WRITE_DIR MANIFEST
-        HBM traffic per deduplicating-FFN call from two `rocprofv3 --pmc FETCH_SIZE`
+        HBM traffic per deduplicating call from two `rocprofv3 --pmc FETCH_SIZE`
         and `--pmc WRITE_SIZE` runs of `bench.py --counters MANIFEST`.  Each counter is
         scaled by what it reads for a plain 1 GiB device copy in the same run (the
         calibration factor = copy bytes / counted bytes).
@@ -49,19 +49,21 @@ def traffic(fetch_dir: str, write_dir: str, manifest_path: str) -> dict:
     out = {}
     for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = per_dispatch(d, counter)
-        # the counted block is the last 2 * ops FFN dispatches; the three
-        # calibration copies are the last non-library dispatches before it
-        ffn_idx = [i for i, (_, n, _) in enumerate(rows) if "ffn_stream_kernel" in n]
-        need = 2 * len(man["ops"])
+        # the counted block is the last per_op * ops dispatches of the counted
+        # kernel; the three calibration copies are the last non-library
+        # dispatches before it
+        kname, k = man.get("kernel", "ffn_stream_kernel"), man.get("per_op", 2)
+        ffn_idx = [i for i, (_, n, _) in enumerate(rows) if kname in n]
+        need = k * len(man["ops"])
         if len(ffn_idx) < need:
-            raise ValueError("expected %d FFN dispatches, found %d" % (need, len(ffn_idx)))
+            raise ValueError("expected %d %s dispatches, found %d" % (need, kname, len(ffn_idx)))
         first = ffn_idx[-need]
         ffn = [(rows[i][1], rows[i][2]) for i in ffn_idx[-need:]]
         others = [v for (_, n, v) in rows[:first] if "moe::" not in n]
         copies = others[-man["copies"]:]
         # a copy reads copy_bytes and writes copy_bytes
         factor = man["copy_bytes"] / (sum(copies) / len(copies)) if copies else float("nan")
-        per_op = [factor * (ffn[2 * i][1] + ffn[2 * i + 1][1]) for i in range(len(man["ops"]))]
+        per_op = [factor * sum(v for _, v in ffn[k * i:k * (i + 1)]) for i in range(len(man["ops"]))]
         out[label] = {"factor": factor, "per_op": per_op, "copies_counted": copies}
     ops = man["ops"]
     by_n = defaultdict(lambda: [0.0, 0.0, 0.0, 0])

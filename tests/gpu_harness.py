@@ -4,6 +4,9 @@ through the C ABI, and compare with the oracle.
 Tolerances
 - ids, union, permutation, byte counts: bit-exact.
 - gates: fp32 softmax against float64: |err| <= 1e-6 + 1e-5 |ref|.
+- the one-launch pass (moe_verify_layer) against the chain of entry points:
+  bit-exact in every output (same arithmetic in the same order), on two
+  calls in a row on one workspace (the first leaves its counters zero).
 - expert outputs, relative L2 per slot (and over the whole output):
   the contractual bound of the layer (1e-5 f32, 1e-2 bf16, 3e-2 fp8) and a
   derived bound: the HIP path rounds the intermediate h = silu(a) * v to
@@ -21,7 +24,8 @@ import torch
 
 import oracle
 from moe_speculative_decoding_amd import _lib as L
-from moe_speculative_decoding_amd.layer import DeviceLayer, VerifyBuffers, to_device, verify_pass
+from moe_speculative_decoding_amd.layer import (DeviceLayer, VerifyBuffers, to_device, verify_layer,
+                                                verify_pass)
 
 DEV = "cuda:0"
 
@@ -66,7 +70,8 @@ def check_vectors(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> fl
     return worst
 
 
-def run_case(case, modes=("dedup", "perslot"), ref=None, experts=None) -> Dict[str, object]:
+def run_case(case, modes=("dedup", "perslot"), ref=None, experts=None,
+             fused: bool = True) -> Dict[str, object]:
     """Run the whole pass on the GPU in each mode and compare with the oracle."""
     cfg = case.cfg
     n = case.n
@@ -109,4 +114,45 @@ def run_case(case, modes=("dedup", "perslot"), ref=None, experts=None) -> Dict[s
         out = buf.out[:n].float().cpu().numpy()
         check_vectors(out, ref["out"], tight, mode + " out")
         report[mode] = w
+        if fused:
+            check_fused_matches(layer, buf, x, logits, n, m, mode)
     return report
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return t.cpu().numpy().view(np.uint8)
+
+
+def check_fused_matches(layer: DeviceLayer, chain: VerifyBuffers, x, logits, n: int, m: int,
+                        mode: str) -> None:
+    """moe_verify_layer reproduces the chain's outputs bit for bit, twice."""
+    K, S = layer.K, layer.S
+    buf = VerifyBuffers(layer, n, DEV, out_dtype=chain.out_dtype)
+    for call in range(2):
+        print("  fused call %d mode=%s" % (call, mode), flush=True)
+        buf.out.zero_()
+        buf.y_slots.zero_()
+        verify_layer(layer, buf, x, logits, n, m)
+        torch.cuda.synchronize()
+        assert L.moe_get_error(buf.ws) == L.MOE_OK, "fused: device error"
+        pairs = [("ids", buf.ids[:n], chain.ids[:n]), ("gates", buf.gates[:n], chain.gates[:n]),
+                 ("bytes", buf.bytes, chain.bytes), ("y_slots", buf.y_slots[:n], chain.y_slots[:n]),
+                 ("out", buf.out[:n], chain.out[:n])]
+        if S:
+            pairs.append(("y_shared", buf.y_shared[:n, :S], chain.y_shared[:n, :S]))
+        if mode == "dedup":
+            pairs += [("U", buf.U, chain.U), ("union_ids", buf.union_ids, chain.union_ids),
+                      ("offsets", buf.offsets, chain.offsets),
+                      ("perm", buf.perm[:n * K], chain.perm[:n * K]),
+                      ("slot_rank", buf.slot_rank[:n * K], chain.slot_rank[:n * K])]
+        for name, a, b in pairs:
+            assert np.array_equal(_bits(a), _bits(b)), "fused %s call %d: %s differs" % (mode, call, name)
+    # outputs kept in the workspace: the same layer output
+    buf.out.zero_()
+    verify_layer(layer, buf, x, logits, n, m, keep=False)
+    torch.cuda.synchronize()
+    assert L.moe_get_error(buf.ws) == L.MOE_OK
+    assert np.array_equal(_bits(buf.out[:n]), _bits(chain.out[:n])), "fused (workspace outputs)"

@@ -91,6 +91,7 @@ def test_ffn_validation_before_launch():
     s = shape()
     w = _weights()
     ws_need = L.moe_workspace_size(s, 8, L.MOE_MODE_DEDUP)
+    ffn_need = 33024 + 8 * s.K * s.f * 2   # control block, hand-over flags, bf16 H
     dd = L.lib.moe_expert_ffn_dedup
     args = [C.byref(s), C.byref(w), FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
             ws_need, None]
@@ -100,7 +101,7 @@ def test_ffn_validation_before_launch():
     assert dd(*bad) == L.MOE_ERR_ARG
     bad = list(args); bad[2] = FAKE + 4   # misaligned x
     assert dd(*bad) == L.MOE_ERR_ARG
-    bad = list(args); bad[12] = ws_need - 1
+    bad = list(args); bad[12] = ffn_need - 1
     assert dd(*bad) == L.MOE_ERR_WORKSPACE
     bad = list(args); bad[11] = FAKE + 64  # workspace not 256-aligned
     assert dd(*bad) == L.MOE_ERR_WORKSPACE
@@ -121,6 +122,35 @@ def test_ffn_validation_before_launch():
     ps = L.lib.moe_expert_ffn_perslot
     assert ps(C.byref(s), C.byref(w), FAKE, 8, None, FAKE, None, None, FAKE, ws_need, None) \
         == L.MOE_ERR_ARG                                           # ids missing
+
+
+def test_layer_validation_before_launch():
+    s = shape()
+    w = _weights()
+    need = L.moe_workspace_size(s, 8, L.MOE_MODE_DEDUP)
+    vl = L.lib.moe_verify_layer
+    base = [C.byref(s), C.byref(w), FAKE, FAKE, 8, L.MOE_MODE_DEDUP, FAKE, L.MOE_F32,
+            None, None, None, None, None, None, None, None, None, None, FAKE, need, None]
+    def call(**chg):
+        a = list(base)
+        for k, v in chg.items():
+            a[int(k[1:])] = v
+        return vl(*a)
+    assert call(a4=0) == L.MOE_ERR_ARG                    # n = 0
+    assert call(a4=33) == L.MOE_ERR_ARG                   # n > 32
+    assert call(a5=7) == L.MOE_ERR_ARG                    # mode
+    assert call(a2=None) == L.MOE_ERR_ARG                 # logits
+    assert call(a3=FAKE + 8) == L.MOE_ERR_ARG             # misaligned x
+    assert call(a6=FAKE + 4) == L.MOE_ERR_ARG             # misaligned out
+    assert call(a7=L.MOE_FP8_E4M3) == L.MOE_ERR_UNSUPPORTED
+    assert call(a10=FAKE) == L.MOE_ERR_ARG                # union outputs: all or none
+    assert call(a15=FAKE + 4) == L.MOE_ERR_ARG            # misaligned y_slots
+    assert call(a19=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(a18=FAKE + 64) == L.MOE_ERR_WORKSPACE     # workspace not 256-aligned
+    # keeping the slot outputs outside the workspace shrinks the need
+    r = lambda b: (b + 255) // 256 * 256
+    own = need - r(8 * s.K * s.d * 4)
+    assert call(a15=FAKE, a19=own - 1) == L.MOE_ERR_WORKSPACE
 
 
 def test_routing_and_combine_validation():
@@ -152,7 +182,9 @@ def test_byte_counts_match_oracle(cfg):
                 cfg.d, cfg.f, cfg.w_dtype, cfg.K, cfg.S, n, U)
         with pytest.raises(L.MoeError):
             L.moe_byte_counts(s, n, cap + 1)
-    tb = 4 if cfg.w_dtype == "f32" else 2
-    need = 256 + 32 * (cfg.K + cfg.S) * cfg.f * tb
-    got = L.moe_workspace_size(s, 32, L.MOE_MODE_DEDUP)
-    assert need <= got < need + 256 and got % 256 == 0
+    # control block, hand-over flags, H in f32, slot outputs (one-launch pass)
+    r = lambda b: (b + 255) // 256 * 256
+    need = (33024 + r(32 * (cfg.K + cfg.S) * cfg.f * 4) + r(32 * cfg.K * cfg.d * 4)
+            + r(32 * cfg.S * cfg.d * 4))
+    assert L.moe_workspace_size(s, 32, L.MOE_MODE_DEDUP) == need
+    assert L.moe_workspace_size(s, 32, L.MOE_MODE_PERSLOT) == need

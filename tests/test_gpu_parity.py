@@ -265,3 +265,28 @@ def test_combine_matches_oracle_f32_and_bf16():
     L.moe_combine(dev(y), dev(gates), dev(ysh), n, K, S, d, outb, L.MOE_BF16)
     gotb = outb.float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(gotb - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+# ------------------------------------------- one-launch pass, one workspace
+def test_layer_one_workspace_across_pass_sizes():
+    """moe_verify_layer on one workspace for passes of different sizes (and so
+    different grids and tiles) in a row: every call matches the chain of entry
+    points bit for bit (the hand-over flags of one call never satisfy the
+    next call's waits)."""
+    from moe_speculative_decoding_amd.layer import VerifyBuffers, to_device, verify_layer, verify_pass
+    from gpu_harness import _bits, upload_layer
+    cfg = RAGGED_BF16
+    layer = upload_layer(make_case(cfg, 8, None, seed=9))  # every expert of the layer
+    shared = VerifyBuffers(layer, 8, DEV)
+    for step, n in enumerate((8, 1, 5, 2, 8, 1)):
+        case = make_case(cfg, n, None, seed=20 + step)
+        x, logits = to_device(case.x, DEV), to_device(case.logits, DEV)
+        for mode in (L.MOE_MODE_DEDUP, L.MOE_MODE_PERSLOT):
+            print("step %d n=%d mode=%d" % (step, n, mode), flush=True)
+            chain = VerifyBuffers(layer, n, DEV)
+            verify_pass(layer, chain, x, logits, n, mode)
+            shared.out.zero_()
+            verify_layer(layer, shared, x, logits, n, mode)
+            torch.cuda.synchronize()
+            assert L.moe_get_error(shared.ws) == L.MOE_OK
+            assert np.array_equal(_bits(shared.out[:n]), _bits(chain.out[:n])), (step, n, mode)
