@@ -52,11 +52,29 @@ def parse():
     ap.add_argument("--cold", action="store_true", help="also time operations after a scrub")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="replay only the one-launch step graph (for a kernel trace whose "
+                         "per-template averages are the deduplicating launches at n=1,2,4,8)")
     ap.add_argument("--counters", metavar="MANIFEST",
                     help="counter-collection mode: eager launches of every operation's route+union "
                          "and deduplicating FFN plus three 1 GiB calibration copies; writes the "
                          "launch order to MANIFEST (JSON) and no benchmark line")
     return ap.parse_args()
+
+
+def measured_traffic():
+    """HBM bytes per deduplicating launch (FETCH_SIZE + WRITE_SIZE, calibrated)
+    from the committed counter summary, or None once the kernel sources have
+    changed since the counters were taken."""
+    from moe_speculative_decoding_amd.profiling import kernel_source_hash
+    path = os.path.join(ROOT, "profiles", "layer_kernel_olmoe_bf16_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return round(rec["traffic_bytes_per_call"])
 
 
 def log(msg):
@@ -68,27 +86,28 @@ def cpu_baseline(cfg, p, budget_s):
     import oracle
     from synth import make_case
     from threadpoolctl import threadpool_limits
-    total_bytes, total_s, done = 0, 0.0, []
+    cases = []
+    for n in (1, 2, 4, 8):  # the step's operations of layer 0
+        case = make_case(cfg, n, "markov:%s" % p, seed=0, window=0, layer=0)
+        ids, _ = oracle.route_topk(case.logits, cfg.K)
+        for e in set(int(v) for v in ids.reshape(-1)):
+            case.expert(e)  # generate inputs before the clock starts
+        cases.append(case)
+    total_bytes, total_s, rounds = 0, 0.0, 0
     with threadpool_limits(limits=1):
-        for n in (1, 2, 4, 8):
-            case = make_case(cfg, n, "markov:%s" % p, seed=0, window=0, layer=0)
-            ids, _ = oracle.route_topk(case.logits, cfg.K)
-            for e in set(int(v) for v in ids.reshape(-1)):
-                case.expert(e)  # generate inputs before the clock starts
-            t0 = time.perf_counter()
-            r = oracle.verify_op(case, "dedup")
-            dt = time.perf_counter() - t0
-            total_bytes += r["union_bytes"]
-            total_s += dt
-            done.append(n)
-            log("cpu oracle n=%d: %.3f s" % (n, dt))
-            if total_s > budget_s:
-                break
+        while total_s < budget_s:  # whole rounds of the four operations until the budget is spent
+            for case in cases:
+                t0 = time.perf_counter()
+                r = oracle.verify_op(case, "dedup")
+                total_s += time.perf_counter() - t0
+                total_bytes += r["union_bytes"]
+            rounds += 1
+    log("cpu oracle: %d rounds of n=1,2,4,8 in %.1f s" % (rounds, total_s))
     return {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": "float64 numpy oracle, dedup mode, one OLMoE-shaped layer, Markov p=%s, "
-                      "n in %s (route+union+FFN+combine incl. weight decode), one thread"
-                      % (p, done)}
+            "sample": "float64 numpy oracle, dedup mode, one OLMoE-shaped layer, Markov p=%s: "
+                      "the operations at n=1,2,4,8 (route+union+FFN+combine incl. weight "
+                      "decode), %d rounds, %.1f s on one thread" % (p, rounds, total_s)}
 
 
 def main():
@@ -140,28 +159,35 @@ def main():
         b = op["buf_layer"] if mode == DEDUP else op["buf_layer_slot"]
         verify_layer(layers[op["layer"]], b, op["x"], op["logits"], op["n"], mode)
 
+    # (profile-step mode: the deduplicating one-launch pass only, so that the
+    # kernel trace holds nothing but the launches the step times)
+    full = not args.profile_step
     for op in ops:
-        verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"], op["n"], DEDUP)
-        verify_pass(layers[op["layer"]], op["buf_slot"], op["x"], op["logits"], op["n"], SLOT)
+        if full:
+            verify_pass(layers[op["layer"]], op["buf"], op["x"], op["logits"], op["n"], DEDUP)
+            verify_pass(layers[op["layer"]], op["buf_slot"], op["x"], op["logits"], op["n"], SLOT)
+            layer_call(op, SLOT)
         layer_call(op, DEDUP)
-        layer_call(op, SLOT)
     torch.cuda.synchronize()
     for op in ops:
-        for b in (op["buf"], op["buf_slot"], op["buf_layer"], op["buf_layer_slot"]):
+        bufs = (op["buf"], op["buf_slot"], op["buf_layer"], op["buf_layer_slot"]) if full \
+            else (op["buf_layer"],)
+        for b in bufs:
             if L.moe_get_error(b.ws) != L.MOE_OK:
                 raise RuntimeError("device error word set")
         n = op["n"]
-        if not (torch.equal(op["buf_layer"].out[:n], op["buf"].out[:n]) and
-                torch.equal(op["buf_layer_slot"].out[:n], op["buf_slot"].out[:n])):
+        if full and not (torch.equal(op["buf_layer"].out[:n], op["buf"].out[:n]) and
+                         torch.equal(op["buf_layer_slot"].out[:n], op["buf_slot"].out[:n])):
             raise RuntimeError("one-launch and chained passes differ")
-        b = op["buf"].bytes.cpu().tolist()
-        op["U"] = int(op["buf"].U.item())
+        b = op["buf_layer"].bytes.cpu().tolist()
+        op["U"] = int(op["buf_layer"].U.item())
         op["union_bytes"], op["requested_bytes"] = int(b[0]), int(b[1])
-        op["out_eager"] = op["buf"].out[:op["n"]].clone()
-        slot = op["buf_slot"].out[:op["n"]]
-        rel = float((slot - op["out_eager"]).norm() / op["out_eager"].norm())
-        if not rel < 1e-5:
-            raise RuntimeError("dedup and per-slot outputs differ (rel %.2e)" % rel)
+        op["out_eager"] = op["buf_layer"].out[:op["n"]].clone()
+        if full:
+            slot = op["buf_slot"].out[:op["n"]]
+            rel = float((slot - op["out_eager"]).norm() / op["out_eager"].norm())
+            if not rel < 1e-5:
+                raise RuntimeError("dedup and per-slot outputs differ (rel %.2e)" % rel)
     step_union_bytes = sum(op["union_bytes"] for op in ops)
 
     if args.counters:
@@ -233,6 +259,10 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = step_union_bytes / (ms_per_step * 1e-3) / 1e9
     log("step: %.3f ms, %.1f GB/s on union bytes" % (ms_per_step, value))
+    if args.profile_step:
+        log("profile-step mode: %d replays of %d launches, nothing else timed"
+            % (args.steps + args.warmup + 3, len(ops)))
+        return
 
     # -------------------------------------------- FFN alone, per n and mode
     def time_graph(g, calls):
@@ -313,9 +343,11 @@ def main():
     tot_t = sum(per_n[n]["t_layer_dedup"] for n in ns)
     achieved = tot_b / tot_t / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "layer_kernel (moe_verify_layer, deduplicating), launches of n=1,2,4,8",
-                "bytes_per_launch": "(U + S) * 3*d*f*2 B (union expert bytes)"}
+                "bytes_per_launch": "(U + S) * 3*d*f*2 B (union expert bytes), mean %.0f"
+                                    % (tot_b / len(ns)),
+                "launch_us": {"n=%d" % n: round(1e6 * per_n[n]["t_layer_dedup"], 2) for n in ns}}
 
     cold = None
     if args.cold:

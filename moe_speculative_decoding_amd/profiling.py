@@ -6,6 +6,9 @@
         scaled by what it reads for a plain 1 GiB device copy in the same run (the
         calibration factor = copy bytes / counted bytes).
 
+    python -m moe_speculative_decoding_amd.profiling traffic FETCH_DIR WRITE_DIR MANIFEST --out JSON
+        the same, written with the sha256 of the kernel sources it was taken with
+
     python -m moe_speculative_decoding_amd.profiling stats TRACE_DIR
         kernel-duration table from a `rocprofv3 --kernel-trace --stats` run.
 """
@@ -13,10 +16,25 @@ from __future__ import annotations
 
 import csv
 import glob
+import hashlib
 import json
 import os
 import sys
 from collections import defaultdict
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over every kernel source (name and contents): a counter summary
+    is valid only for the sources it was taken with."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
 
 
 def _counter_rows(d: str):
@@ -105,7 +123,12 @@ def stats(trace_dir: str) -> str:
 
 def main(argv):
     if len(argv) >= 4 and argv[0] == "traffic":
-        print(json.dumps(traffic(argv[1], argv[2], argv[3]), indent=1))
+        rec = traffic(argv[1], argv[2], argv[3])
+        if len(argv) >= 6 and argv[4] == "--out":
+            rec["kernel_source_sha256"] = kernel_source_hash()
+            with open(argv[5], "w") as fh:
+                json.dump(rec, fh, indent=1)
+        print(json.dumps(rec, indent=1))
     elif len(argv) >= 2 and argv[0] == "stats":
         print(stats(argv[1]))
     else:
