@@ -123,7 +123,7 @@ def main():
     from moe_speculative_decoding_amd import _lib as L
     from moe_speculative_decoding_amd import costmodel as cm
     from moe_speculative_decoding_amd.layer import (DeviceLayer, VerifyBuffers, to_device,
-                                                    verify_layer, verify_pass)
+                                                    verify_layer, verify_layer_auto, verify_pass)
     from synth import make_case
     from synth.configs import OLMOE
     from synth.gen import device_layer_weights
@@ -339,6 +339,73 @@ def main():
     fit["crossover_n"] = cm.crossover(ns, [per_n[n]["t_slot"] - per_n[n]["t_dedup"] for n in ns])
     fit["ms_per_step_chained"] = round(ms_chain, 4)
 
+    # ---- mode dispatch and best draft length (expert-bytes page: Eq. (7),
+    # the appendix symbols, Table 2) from the one-launch pass at n = 1..8
+    model = {n: {"t_dedup": per_n[n]["t_layer_dedup"], "t_slot": per_n[n]["t_layer_slot"],
+                 "union_bytes": per_n[n]["union_bytes"],
+                 "requested_bytes": per_n[n]["requested_bytes"]} for n in ns}
+    for n in range(1, 9):
+        if n in model:
+            continue
+        sel = []
+        for l in range(args.layers):
+            case = make_case(cfg, n, routing, seed=0, window=l, layer=l)
+            sel.append({"n": n, "layer": l, "x": to_device(case.x, dev),
+                        "logits": to_device(case.logits, dev),
+                        "buf_layer": VerifyBuffers(layers[l], n, dev),
+                        "buf_layer_slot": VerifyBuffers(layers[l], n, dev)})
+        for op in sel:
+            layer_call(op, DEDUP)
+        torch.cuda.synchronize()
+        byt = [op["buf_layer"].bytes.cpu().tolist() for op in sel]
+        t = {}
+        for mode in (DEDUP, SLOT):
+            g = capture(lambda: [layer_call(op, mode) for op in sel])
+            t[mode] = time_graph(g, len(sel))
+            del g
+        model[n] = {"t_dedup": t[DEDUP], "t_slot": t[SLOT],
+                    "union_bytes": sum(b[0] for b in byt) / len(byt),
+                    "requested_bytes": sum(b[1] for b in byt) / len(byt)}
+        del sel
+    for n in model:
+        a = cm.aggregate([model[n]])
+        model[n].update(u=a["u"], r=a["r"])
+        model[n]["mode"] = "dedup" if cm.dedup_faster(a["u"], a["r"]) else "per-slot"
+        model[n]["t_best"] = model[n]["t_dedup"] if model[n]["mode"] == "dedup" else model[n]["t_slot"]
+    # the step with the mode chosen on the device per pass from each n's measured r
+    mode_out = torch.zeros(len(ops), dtype=torch.int32, device=dev)
+
+    def auto_call(i, op):
+        verify_layer_auto(layers[op["layer"]], op["buf_layer"], op["x"], op["logits"], op["n"],
+                          model[op["n"]]["r"], mode_out[i:i + 1])
+
+    g_auto = capture(lambda: [auto_call(i, op) for i, op in enumerate(ops)])
+    ms_auto = time_graph(g_auto, 1) * 1e3
+    del g_auto
+    picked = mode_out.cpu().tolist()
+    V = [model[k + 1]["t_best"] for k in range(8)]  # V(k) = tau(k + 1)
+    steps = cm.step_points(V)
+    dispatch = {
+        "rule": "dedup iff u(n) < r(n), decided on the device from each pass's union",
+        "ms_per_step_auto": round(ms_auto, 4),
+        "dedup_passes": sum(1 for m in picked if m == DEDUP), "passes": len(picked),
+        "per_n": {"n=%d" % n: {"u": round(model[n]["u"], 4), "r": round(model[n]["r"], 4),
+                               "mode": model[n]["mode"],
+                               "us_dedup": round(1e6 * model[n]["t_dedup"], 2),
+                               "us_perslot": round(1e6 * model[n]["t_slot"], 2)}
+                  for n in sorted(model)},
+    }
+    draft = {
+        "V_us": [round(1e6 * v, 2) for v in V],
+        "a0": round(cm.a0(V), 4),
+        "step_points": [[round(a, 4), k] for a, k in steps],
+        "k_star": {"a=%.1f" % a: cm.best_draft_length(V, a) for a in (0.3, 0.5, 0.7, 0.8, 0.9)},
+        "reading": "V(k) = time of one MoE layer op at n = k+1 in the mode Eq. (7) picks; "
+                   "geometric acceptance, T_a(k) = sum_{j<=k} a^j / V(k)",
+    }
+    log("dispatch: %s" % json.dumps(dispatch))
+    log("draft length: %s" % json.dumps(draft))
+
     tot_b = sum(per_n[n]["union_bytes"] for n in ns)
     tot_t = sum(per_n[n]["t_layer_dedup"] for n in ns)
     achieved = tot_b / tot_t / 1e9
@@ -382,6 +449,7 @@ def main():
                                % (args.p, args.layers),
                    "global_batch": sum(ns) * args.layers, "seq_len": 1, "parallelism": "none"},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fit": fit,
+        "dispatch": dispatch, "draft_length": draft,
     }
     if cold is not None:
         line["cold"] = cold

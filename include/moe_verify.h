@@ -196,6 +196,25 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
                             float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
                             moe_stream_t stream);
 
+/* moe_verify_layer with the mode chosen on the device for each pass: the
+ * pass deduplicates iff its byte share (U + S) / (n (K + S)) is below r, the
+ * ratio beta_dedup / beta_slot of the two kernels' effective bandwidths
+ * measured at this n (the expert-bytes page, Eq. (7) and Table 1: r and u as
+ * ratios of sums).  U is the pass's own union, counted on the device, so no
+ * host round trip decides the mode.  r = 0 always runs per-slot, r > 1 always
+ * deduplicates (u <= 1).
+ *   mode_out  (device, optional) int32 [1]: the moe_mode the pass ran
+ *   bytes     (device, optional) uint64 [2]: [0] bytes the chosen mode
+ *             streamed, [1] n (K + S) b
+ * Other arguments as moe_verify_layer (no routing or union outputs; the slot
+ * outputs stay in the workspace).  Errors: MOE_ERR_ARG for r negative or not
+ * finite, otherwise as moe_verify_layer. */
+moe_status moe_verify_layer_auto(const moe_shape* shape, const moe_weights* w,
+                                 const float* logits, const void* x, int32_t n, float r,
+                                 void* out, int32_t out_dtype, int32_t* mode_out,
+                                 uint64_t* bytes, void* ws, size_t ws_bytes,
+                                 moe_stream_t stream);
+
 /* Bytes of workspace any FFN or layer call needs for passes of up to n_max
  * tokens (0 for an invalid shape). */
 size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode);

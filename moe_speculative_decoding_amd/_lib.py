@@ -67,6 +67,8 @@ _SIG = {
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]),
     "moe_verify_layer": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I, _I, _P,
                               _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_verify_layer_auto": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I,
+                                   C.c_float, _P, _I, _P, _P, _P, C.c_size_t, _P]),
     "moe_workspace_size": (C.c_size_t, [C.POINTER(moe_shape), _I, _I]),
     "moe_workspace_init": (_I, [_P, C.c_size_t, _P]),
     "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
@@ -170,6 +172,13 @@ def moe_verify_layer(shape: moe_shape, w: moe_weights, logits, x, n, mode, out, 
                                 ptr(offsets), ptr(perm), ptr(slot_rank), ptr(y_slots),
                                 ptr(y_shared), ptr(bytes_), ptr(ws), ws_bytes, _stream(stream)),
            "moe_verify_layer")
+
+
+def moe_verify_layer_auto(shape: moe_shape, w: moe_weights, logits, x, n, r, out, out_dtype,
+                          mode_out=None, bytes_=None, ws=None, ws_bytes=0, stream=None) -> None:
+    _check(lib.moe_verify_layer_auto(C.byref(shape), C.byref(w), ptr(logits), ptr(x), n, float(r),
+                                     ptr(out), out_dtype, ptr(mode_out), ptr(bytes_), ptr(ws),
+                                     ws_bytes, _stream(stream)), "moe_verify_layer_auto")
 
 
 def moe_workspace_size(shape: moe_shape, n_max: int, mode: int) -> int:

@@ -150,6 +150,56 @@ int wt_of(int w_dtype) {
   return w_dtype == MOE_F32 ? moe::WT_F32 : (w_dtype == MOE_BF16 ? moe::WT_BF16 : moe::WT_FP8);
 }
 
+
+// argument checks of the one-launch pass shared by its fixed-mode and
+// automatic-mode entry points
+moe_status moe_verify_layer_check(const moe_shape* shape, const moe_weights* w,
+                                  const float* logits, const void* x, int n, int mode, void* out,
+                                  int out_dtype, const float* y_slots, const float* y_shared,
+                                  const uint64_t* bytes, const void* ws, size_t ws_bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (n < 1 || n > kMaxN) return MOE_ERR_ARG;
+  if (mode != MOE_MODE_DEDUP && mode != MOE_MODE_PERSLOT) return MOE_ERR_ARG;
+  st = check_weights(shape, w);
+  if (st != MOE_OK) return st;
+  if (logits == nullptr || !aligned(logits, 4)) return MOE_ERR_ARG;
+  if (x == nullptr || !aligned(x, 16) || out == nullptr || !aligned(out, 16)) return MOE_ERR_ARG;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((y_slots != nullptr && !aligned(y_slots, 16)) ||
+      (y_shared != nullptr && !aligned(y_shared, 16)))
+    return MOE_ERR_ARG;
+  if (bytes != nullptr && !aligned(bytes, 8)) return MOE_ERR_ARG;
+  if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  const size_t need = kHOffset + layer_h_bytes(shape, n) +
+                      (y_slots == nullptr ? layer_ys_bytes(shape, n) : 0) +
+                      (y_shared == nullptr ? layer_ysh_bytes(shape, n) : 0);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// launch parameters of the one-launch pass (arguments already checked)
+moe::LayerParams layer_params(const moe_shape* shape, const moe_weights* w, const float* logits,
+                              const void* x, int n, int mode, void* out, int out_dtype,
+                              float* y_slots, float* y_shared, uint64_t* bytes, void* ws) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* next = base + kHOffset + layer_h_bytes(shape, n);
+  if (y_slots == nullptr) {
+    y_slots = reinterpret_cast<float*>(next);
+    next += layer_ys_bytes(shape, n);
+  }
+  if (y_shared == nullptr) y_shared = reinterpret_cast<float*>(next);
+  moe::LayerParams lp{};
+  lp.f = make_params(shape, w, x, n, y_slots, y_shared, bytes, ws);
+  lp.f.mode = mode;
+  lp.logits = logits;
+  lp.out = out;
+  lp.out_bf16 = out_dtype == MOE_BF16;
+  lp.epoch = reinterpret_cast<unsigned*>(base + moe::kEpochOffset);
+  lp.up_flags = reinterpret_cast<unsigned*>(base + moe::kFlagsOffset);
+  lp.down_flags = lp.up_flags + moe::kMaxGrid;
+  return lp;
+}
 }  // namespace
 
 extern "C" {
@@ -263,15 +313,10 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
                             int32_t* offsets, int32_t* perm, int32_t* slot_rank, float* y_slots,
                             float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
                             moe_stream_t stream) {
-  moe_status st = check_shape(shape);
-  if (st != MOE_OK) return st;
-  if (n < 1 || n > kMaxN) return MOE_ERR_ARG;
   if (mode != MOE_MODE_DEDUP && mode != MOE_MODE_PERSLOT) return MOE_ERR_ARG;
-  st = check_weights(shape, w);
+  moe_status st = moe_verify_layer_check(shape, w, logits, x, n, mode, out, out_dtype, y_slots,
+                                         y_shared, bytes, ws, ws_bytes);
   if (st != MOE_OK) return st;
-  if (logits == nullptr || !aligned(logits, 4)) return MOE_ERR_ARG;
-  if (x == nullptr || !aligned(x, 16) || out == nullptr || !aligned(out, 16)) return MOE_ERR_ARG;
-  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if ((ids != nullptr && !aligned(ids, 4)) || (gates != nullptr && !aligned(gates, 4)))
     return MOE_ERR_ARG;
   const void* uni[5] = {U, union_ids, offsets, perm, slot_rank};
@@ -281,27 +326,9 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
     given += p != nullptr;
   }
   if (given != 0 && given != 5) return MOE_ERR_ARG;
-  if ((y_slots != nullptr && !aligned(y_slots, 16)) ||
-      (y_shared != nullptr && !aligned(y_shared, 16)))
-    return MOE_ERR_ARG;
-  if (bytes != nullptr && !aligned(bytes, 8)) return MOE_ERR_ARG;
-  if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
-  const size_t need = kHOffset + layer_h_bytes(shape, n) +
-                      (y_slots == nullptr ? layer_ys_bytes(shape, n) : 0) +
-                      (y_shared == nullptr ? layer_ysh_bytes(shape, n) : 0);
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  uint8_t* next = base + kHOffset + layer_h_bytes(shape, n);
-  if (y_slots == nullptr) {
-    y_slots = reinterpret_cast<float*>(next);
-    next += layer_ys_bytes(shape, n);
-  }
-  if (y_shared == nullptr) y_shared = reinterpret_cast<float*>(next);
-  moe::LayerParams lp{};
-  lp.f = make_params(shape, w, x, n, y_slots, y_shared, bytes, ws);
-  lp.f.mode = mode == MOE_MODE_DEDUP ? moe::MODE_DEDUP : moe::MODE_PERSLOT;
-  lp.logits = logits;
+  moe::LayerParams lp = layer_params(
+      shape, w, logits, x, n, mode == MOE_MODE_DEDUP ? moe::MODE_DEDUP : moe::MODE_PERSLOT, out,
+      out_dtype, y_slots, y_shared, bytes, ws);
   lp.ids = ids;
   lp.gates = gates;
   if (mode == MOE_MODE_DEDUP && given == 5) {
@@ -311,11 +338,25 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
     lp.perm = perm;
     lp.slot_rank = slot_rank;
   }
-  lp.out = out;
-  lp.out_bf16 = out_dtype == MOE_BF16;
-  lp.epoch = reinterpret_cast<unsigned*>(base + moe::kEpochOffset);
-  lp.up_flags = reinterpret_cast<unsigned*>(base + moe::kFlagsOffset);
-  lp.down_flags = lp.up_flags + moe::kMaxGrid;
+  return hip_status(moe::launch_layer(lp, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_verify_layer_auto(const moe_shape* shape, const moe_weights* w,
+                                 const float* logits, const void* x, int32_t n, float r,
+                                 void* out, int32_t out_dtype, int32_t* mode_out,
+                                 uint64_t* bytes, void* ws, size_t ws_bytes,
+                                 moe_stream_t stream) {
+  if (!(r >= 0.0f) || r > 1e30f) return MOE_ERR_ARG;  // rejects NaN and infinities
+  if (mode_out != nullptr && !aligned(mode_out, 4)) return MOE_ERR_ARG;
+  // validate and lay out exactly as the fixed-mode call (deduplicating shape
+  // of the arguments; the workspace need is the same for both modes)
+  moe_status st = moe_verify_layer_check(shape, w, logits, x, n, MOE_MODE_DEDUP, out, out_dtype,
+                                         nullptr, nullptr, bytes, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  moe::LayerParams lp = layer_params(shape, w, logits, x, n, moe::MODE_AUTO, out, out_dtype,
+                                     nullptr, nullptr, bytes, ws);
+  lp.r_auto = r;
+  lp.mode_out = mode_out;
   return hip_status(moe::launch_layer(lp, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
 }
 

@@ -17,7 +17,7 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;  // 4 waves
 
 enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
-enum { MODE_DEDUP = 0, MODE_PERSLOT = 1 };
+enum { MODE_DEDUP = 0, MODE_PERSLOT = 1, MODE_AUTO = 2 };  // AUTO: the one-launch pass decides
 enum : uint32_t { ERRBIT_BAD_IDS = 1u, ERRBIT_TIMEOUT = 2u };
 
 // Workspace: [0, kCtrlBytes) control words (error word first, the epoch of
@@ -104,6 +104,8 @@ struct LayerParams {
   int32_t* slot_rank;
   void* out;              // [n][d]
   int out_bf16;
+  float r_auto;           // MODE_AUTO: deduplicate iff (U+S) < r_auto * n*(K+S)
+  int32_t* mode_out;      // optional: the mode a MODE_AUTO pass ran
   unsigned* epoch;        // call counter of the workspace
   unsigned* up_flags;     // [kMaxGrid] UP range done (tag of the call)
   unsigned* down_flags;   // [kMaxGrid] DOWN range done

@@ -102,20 +102,29 @@ void layer_kernel(LayerParams lp) {
   }
   __syncthreads();
   int U = 0;
-  if (p.mode == MODE_DEDUP) {
+  int mode = p.mode;
+  if (mode != MODE_PERSLOT) {
     build_union_256(ids_l, n, K, E, &U_l, mt.b, mt.a, mt.c, rl.slot_rank, rl.ul);
     __syncthreads();
     U = uni(U_l);
-  } else {
-    for (int i = tid; i < nk; i += kBlock) mt.a[i] = ids_l[i];
-    __syncthreads();
   }
+  if (mode == MODE_AUTO) {
+    // the expert-bytes page's Eq. (7): deduplicate iff its byte share
+    // (U+S)/(n(K+S)) is below the measured bandwidth ratio r (every
+    // workgroup decides alike: it saw the same U)
+    mode = static_cast<float>(U + S) < lp.r_auto * static_cast<float>(n * (K + S)) ? MODE_DEDUP
+                                                                                    : MODE_PERSLOT;
+  }
+  if (mode == MODE_PERSLOT)
+    for (int i = tid; i < nk; i += kBlock) mt.a[i] = ids_l[i];
+  if (tid == 0) mt.mode = mode;
+  __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = tid; i < nk; i += kBlock) {
       if (lp.ids != nullptr) lp.ids[i] = ids_l[i];
       if (lp.gates != nullptr) lp.gates[i] = gates_l[i];
     }
-    if (p.mode == MODE_DEDUP && lp.U != nullptr) {
+    if (mode == MODE_DEDUP && lp.U != nullptr) {
       const int cap = p.ucap;
       for (int i = tid; i < nk; i += kBlock) {
         lp.perm[i] = mt.c[i];
@@ -128,10 +137,11 @@ void layer_kernel(LayerParams lp) {
     if (tid == 0 && p.bytes != nullptr) {
       const unsigned long long req =
           static_cast<unsigned long long>(n) * (K + S) * p.expert_bytes;
-      p.bytes[0] = p.mode == MODE_DEDUP ? static_cast<unsigned long long>(U + S) * p.expert_bytes
+      p.bytes[0] = mode == MODE_DEDUP ? static_cast<unsigned long long>(U + S) * p.expert_bytes
                                         : req;
       p.bytes[1] = req;
     }
+    if (tid == 0 && lp.mode_out != nullptr) *lp.mode_out = mode;
   }
   __syncthreads();  // the routing scratch in xs is dead from here
 
@@ -140,7 +150,7 @@ void layer_kernel(LayerParams lp) {
   if (tid == 0) tag_l = coh_load_u32(lp.epoch) + 1u;
   __syncthreads();
   const unsigned tag = tag_l;
-  const int NG = p.mode == MODE_DEDUP ? U + S : n * (K + S);
+  const int NG = mode == MODE_DEDUP ? U + S : n * (K + S);
   const int upg_u = (p.f + (kBlock / kWave) * RU - 1) / ((kBlock / kWave) * RU);
   const int upg_d = (p.d + (kBlock / kWave) * RD - 1) / ((kBlock / kWave) * RD);
   const long long NUu = static_cast<long long>(NG) * upg_u;

@@ -233,10 +233,12 @@ struct Meta {
   int a[kMaxSlots + 1];  // dedup: offsets[0..cap]; per-slot: ids[0..nK)
   int b[kMaxSlots];      // dedup: union_ids[0..cap)
   int c[kMaxSlots];      // dedup: perm[0..nK)
+  int mode;              // MODE_DEDUP or MODE_PERSLOT: how a, b, c are read
 };
 
 __device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
   const int nk = p.n * p.K;
+  if (threadIdx.x == 0) m.mode = p.mode;
   if (p.mode == MODE_DEDUP) {
     for (int i = threadIdx.x; i <= p.ucap; i += kBlock) m.a[i] = p.offsets[i];
     for (int i = threadIdx.x; i < p.ucap; i += kBlock) m.b[i] = p.union_ids[i];
@@ -250,7 +252,7 @@ __device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
 __device__ __forceinline__ void token_of(const FfnParams& p, const Meta& mt, const Group& G, int j,
                                          int& xrow, int& hrow, float*& yrow) {
   const int nk = p.n * p.K;
-  if (p.mode == MODE_DEDUP) {
+  if (mt.mode == MODE_DEDUP) {
     if (!G.shared) {
       const int slot = mt.c[G.first + j];
       xrow = slot / p.K;
@@ -274,6 +276,9 @@ __device__ __forceinline__ void token_of(const FfnParams& p, const Meta& mt, con
   }
 }
 
+// a value every lane holds the same, kept in a scalar register
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // ------------------------------------------------------------ the walk
 // One phase (up: gate/up rows, or down rows) is a list of units: (group g,
 // row block of 4*R rows), groups in order, row blocks in order.  Workgroup b
@@ -293,7 +298,7 @@ struct Walk {
 // per-slot 0..n*K-1 slots, then the n*S (token, shared expert) pairs
 __device__ __forceinline__ void group_at(const FfnParams& p, const Meta& mt, int U, int g,
                                          Group& G) {
-  if (p.mode == MODE_DEDUP) {
+  if (uni(mt.mode) == MODE_DEDUP) {
     if (g < U) {
       G.e = mt.b[g];
       G.shared = 0;
@@ -326,7 +331,6 @@ __device__ __forceinline__ void group_at(const FfnParams& p, const Meta& mt, int
   }
 }
 
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <int TC>
 __device__ __forceinline__ void walk_group(const FfnParams& p, const Meta& mt, int U, Walk& w,

@@ -107,3 +107,12 @@ def verify_layer(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor, logits
     else:
         L.moe_verify_layer(layer.shape, layer.weights, logits, x, n, mode, buf.out, buf.out_dtype,
                            ws=buf.ws, ws_bytes=buf.ws_bytes, stream=stream)
+
+
+def verify_layer_auto(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor,
+                      logits: torch.Tensor, n: int, r: float, mode_out: torch.Tensor,
+                      stream=None) -> None:
+    """The one-launch pass with the mode chosen on the device from the pass's
+    own union and the measured bandwidth ratio r (moe_verify_layer_auto)."""
+    L.moe_verify_layer_auto(layer.shape, layer.weights, logits, x, n, r, buf.out, buf.out_dtype,
+                            mode_out, buf.bytes, buf.ws, buf.ws_bytes, stream)

@@ -153,6 +153,28 @@ def test_layer_validation_before_launch():
     assert call(a15=FAKE, a19=own - 1) == L.MOE_ERR_WORKSPACE
 
 
+def test_layer_auto_validation_before_launch():
+    s = shape()
+    w = _weights()
+    need = L.moe_workspace_size(s, 8, L.MOE_MODE_DEDUP)
+    va = L.lib.moe_verify_layer_auto
+    base = [C.byref(s), C.byref(w), FAKE, FAKE, 8, 0.8, FAKE, L.MOE_F32, None, None, FAKE, need,
+            None]
+    def call(**chg):
+        a = list(base)
+        for k, v in chg.items():
+            a[int(k[1:])] = v
+        return va(*a)
+    assert call(a5=-0.1) == L.MOE_ERR_ARG
+    assert call(a5=float("nan")) == L.MOE_ERR_ARG
+    assert call(a5=float("inf")) == L.MOE_ERR_ARG
+    assert call(a4=0) == L.MOE_ERR_ARG
+    assert call(a8=FAKE + 2) == L.MOE_ERR_ARG            # misaligned mode_out
+    assert call(a9=FAKE + 4) == L.MOE_ERR_ARG            # misaligned bytes
+    assert call(a11=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(a7=L.MOE_FP8_E4M3) == L.MOE_ERR_UNSUPPORTED
+
+
 def test_routing_and_combine_validation():
     rt = L.lib.moe_route_topk
     assert rt(FAKE, 0, 8, 2, FAKE, FAKE, None) == L.MOE_ERR_ARG

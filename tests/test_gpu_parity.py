@@ -290,3 +290,36 @@ def test_layer_one_workspace_across_pass_sizes():
             torch.cuda.synchronize()
             assert L.moe_get_error(shared.ws) == L.MOE_OK
             assert np.array_equal(_bits(shared.out[:n]), _bits(chain.out[:n])), (step, n, mode)
+
+
+# ------------------------------------ one-launch pass, mode chosen on device
+@pytest.mark.parametrize("cfg,n", [(RAGGED_BF16, 5), (TINY, 4), (RAGGED_F32, 11)])
+def test_layer_auto_mode_follows_eq7(cfg, n):
+    """moe_verify_layer_auto picks deduplication iff (U+S)/(n(K+S)) < r, from
+    the union it counts itself, and then matches that mode's chain bit for bit."""
+    from moe_speculative_decoding_amd.layer import (VerifyBuffers, to_device, verify_layer_auto,
+                                                    verify_pass)
+    from gpu_harness import _bits, upload_layer
+    case = make_case(cfg, n, None, seed=31)
+    layer = upload_layer(case)
+    x, logits = to_device(case.x, DEV), to_device(case.logits, DEV)
+    chains = {}
+    for mode in (L.MOE_MODE_DEDUP, L.MOE_MODE_PERSLOT):
+        chains[mode] = VerifyBuffers(layer, n, DEV)
+        verify_pass(layer, chains[mode], x, logits, n, mode)
+    torch.cuda.synchronize()
+    U = int(chains[L.MOE_MODE_DEDUP].U.item())
+    u = (U + cfg.S) / (n * (cfg.K + cfg.S))
+    buf = VerifyBuffers(layer, n, DEV)
+    mode_out = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    for r in (0.0, u * 0.999, u * 1.001, 2.0):
+        expect = L.MOE_MODE_DEDUP if u < r else L.MOE_MODE_PERSLOT
+        print("n=%d U=%d u=%.4f r=%.4f expect=%d" % (n, U, u, r, expect), flush=True)
+        buf.out.zero_()
+        verify_layer_auto(layer, buf, x, logits, n, r, mode_out)
+        torch.cuda.synchronize()
+        assert L.moe_get_error(buf.ws) == L.MOE_OK
+        assert int(mode_out.item()) == expect
+        ref = chains[expect]
+        assert np.array_equal(_bits(buf.out[:n]), _bits(ref.out[:n])), r
+        assert np.array_equal(_bits(buf.bytes), _bits(ref.bytes)), r
