@@ -9,3 +9,4 @@ from .moe_ref import (  # noqa: F401
     decode_matrix, decode_x, distinct_share, expert_bytes, ffn_dedup, ffn_perslot,
     reuse_last, route_topk, silu, swiglu, union_size, verify_op,
 )
+from .evict_ref import evict_select, is_ancestor_closed, path_scores, rank_nodes  # noqa: F401,E402
