@@ -70,7 +70,8 @@ typedef enum {
   MOE_ERR_WORKSPACE = 3,    /* workspace too small or misaligned */
   MOE_ERR_HIP = 4,          /* the HIP runtime refused a launch or copy */
   MOE_ERR_BAD_IDS = 5,      /* (device) an expert id outside [0, E) was seen */
-  MOE_ERR_TIMEOUT = 6       /* (device) a bounded wait gave up */
+  MOE_ERR_TIMEOUT = 6,      /* (device) a bounded wait gave up */
+  MOE_ERR_BAD_TREE = 7      /* (device) a draft tree or its probabilities out of range */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -215,6 +216,29 @@ moe_status moe_verify_layer_auto(const moe_shape* shape, const moe_weights* w,
                                  uint64_t* bytes, void* ws, size_t ws_bytes,
                                  moe_stream_t stream);
 
+/* EVICT utility-guided truncation of a draft tree, ahead of its verify pass
+ * ("Making Every Verified Token Count: Adaptive Verification for MoE
+ * Speculative Decoding", Sec. 3.1-3.2, Eqs. (7)-(10)).
+ *   parent   (device) int32 [N]: parent node of v, parent[v] < v (breadth-first
+ *            order); -1 for a child of the root token
+ *   q        (device) f32 [N]: draft probability of v given its parent, in [0, 1]
+ *   cost     (device) f32 [N]: cost[k-1] = C(k), the profiled latency of a step
+ *            that verifies k nodes, > 0
+ *   order    (device) int32 [N]: nodes by path score, descending (equal scores:
+ *            lower index first); T_k = order[0..k) is ancestor-closed
+ *   scores   (device, optional) f64 [N]: Score(v), the float64 product of q over
+ *            the path, taken from the root outward
+ *   expected (device, optional) f64 [N]: expected[k-1] = E_hat(T_k), prefix sums
+ *            of the sorted scores
+ *   k_best   (device) int32 [1]: k* = argmax_k E_hat(T_k) / C(k), the smallest k
+ *            on equal utility; 0 when the tree is invalid
+ *   ws       workspace (>= 256 bytes, 256-aligned) for the error word.
+ * 1 <= N <= 1024.  Errors: MOE_ERR_ARG on the host; a parent outside [-1, v),
+ * q outside [0, 1] or cost <= 0 records MOE_ERR_BAD_TREE (moe_get_error). */
+moe_status moe_evict_select(const int32_t* parent, const float* q, const float* cost, int32_t N,
+                            int32_t* order, double* scores, double* expected, int32_t* k_best,
+                            void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* Bytes of workspace any FFN or layer call needs for passes of up to n_max
  * tokens (0 for an invalid shape). */
 size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode);
@@ -229,7 +253,8 @@ moe_status moe_byte_counts(const moe_shape* shape, int32_t n, int32_t U,
                            uint64_t* union_bytes, uint64_t* requested_bytes);
 
 /* Synchronizes `stream`, then returns and clears the device error word kept
- * at the start of `ws`: MOE_OK, MOE_ERR_BAD_IDS or MOE_ERR_TIMEOUT. */
+ * at the start of `ws`: MOE_OK, MOE_ERR_BAD_IDS, MOE_ERR_BAD_TREE or
+ * MOE_ERR_TIMEOUT. */
 moe_status moe_get_error(void* ws, moe_stream_t stream);
 
 /* Diagnostic: decode `count` E4M3FN codes (device) to f32 (device) with the

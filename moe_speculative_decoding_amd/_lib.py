@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_VERIFY_LIB") or os.path.join(_HERE, "libmoe_verify.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, 1, 2, 3
-MOE_ERR_HIP, MOE_ERR_BAD_IDS, MOE_ERR_TIMEOUT = 4, 5, 6
+MOE_ERR_HIP, MOE_ERR_BAD_IDS, MOE_ERR_TIMEOUT, MOE_ERR_BAD_TREE = 4, 5, 6, 7
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_MODE_DEDUP, MOE_MODE_PERSLOT = 0, 1
 
@@ -69,6 +69,7 @@ _SIG = {
                               _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_verify_layer_auto": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I,
                                    C.c_float, _P, _I, _P, _P, _P, C.c_size_t, _P]),
+    "moe_evict_select": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_workspace_size": (C.c_size_t, [C.POINTER(moe_shape), _I, _I]),
     "moe_workspace_init": (_I, [_P, C.c_size_t, _P]),
     "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
@@ -179,6 +180,13 @@ def moe_verify_layer_auto(shape: moe_shape, w: moe_weights, logits, x, n, r, out
     _check(lib.moe_verify_layer_auto(C.byref(shape), C.byref(w), ptr(logits), ptr(x), n, float(r),
                                      ptr(out), out_dtype, ptr(mode_out), ptr(bytes_), ptr(ws),
                                      ws_bytes, _stream(stream)), "moe_verify_layer_auto")
+
+
+def moe_evict_select(parent, q, cost, N, order, scores, expected, k_best, ws, ws_bytes,
+                     stream=None) -> None:
+    _check(lib.moe_evict_select(ptr(parent), ptr(q), ptr(cost), N, ptr(order), ptr(scores),
+                                ptr(expected), ptr(k_best), ptr(ws), ws_bytes, _stream(stream)),
+           "moe_evict_select")
 
 
 def moe_workspace_size(shape: moe_shape, n_max: int, mode: int) -> int:

@@ -12,6 +12,7 @@ using moe::kCtrlBytes;
 using moe::kHOffset;
 
 constexpr int kMaxN = 32, kMaxK = 8, kMaxE = 256, kMaxS = 4, kMaxDim = 65536;
+constexpr int kMaxTreeNodes = 1024;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -215,6 +216,7 @@ const char* moe_status_str(int32_t s) {
     case MOE_ERR_HIP: return "HIP runtime error";
     case MOE_ERR_BAD_IDS: return "expert id outside [0, E)";
     case MOE_ERR_TIMEOUT: return "bounded device wait gave up";
+    case MOE_ERR_BAD_TREE: return "draft tree or probabilities out of range";
     default: return "unknown status";
   }
 }
@@ -360,6 +362,20 @@ moe_status moe_verify_layer_auto(const moe_shape* shape, const moe_weights* w,
   return hip_status(moe::launch_layer(lp, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_evict_select(const int32_t* parent, const float* q, const float* cost, int32_t N,
+                            int32_t* order, double* scores, double* expected, int32_t* k_best,
+                            void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (N < 1 || N > kMaxTreeNodes) return MOE_ERR_ARG;
+  const void* need4[5] = {parent, q, cost, order, k_best};
+  for (const void* p : need4)
+    if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+  if ((scores != nullptr && !aligned(scores, 8)) || (expected != nullptr && !aligned(expected, 8)))
+    return MOE_ERR_ARG;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_evict(parent, q, cost, N, order, scores, expected, k_best,
+                                      static_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
@@ -395,6 +411,7 @@ moe_status moe_get_error(void* ws, moe_stream_t stream) {
   st = hip_status(hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice));
   if (st != MOE_OK) return st;
   if (word & moe::ERRBIT_BAD_IDS) return MOE_ERR_BAD_IDS;
+  if (word & moe::ERRBIT_BAD_TREE) return MOE_ERR_BAD_TREE;
   return MOE_ERR_TIMEOUT;
 }
 

@@ -18,7 +18,7 @@ constexpr int kBlock = 256;  // 4 waves
 
 enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
 enum { MODE_DEDUP = 0, MODE_PERSLOT = 1, MODE_AUTO = 2 };  // AUTO: the one-launch pass decides
-enum : uint32_t { ERRBIT_BAD_IDS = 1u, ERRBIT_TIMEOUT = 2u };
+enum : uint32_t { ERRBIT_BAD_IDS = 1u, ERRBIT_TIMEOUT = 2u, ERRBIT_BAD_TREE = 4u };
 
 // Workspace: [0, kCtrlBytes) control words (error word first, the epoch of
 // the one-launch pass at kEpochOffset; bytes [kZeroOffset, kZeroOffset + 16)
@@ -152,6 +152,9 @@ hipError_t launch_layer(const LayerParams& lp, int w_dtype, hipStream_t s);
 hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
                           int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_evict(const int32_t* parent, const float* q, const float* cost, int N,
+                        int32_t* order, double* scores, double* expected, int32_t* k_best,
+                        uint32_t* err, hipStream_t s);
 hipError_t launch_decode_fp8(const uint8_t* codes, float* out, long long count, hipStream_t s);
 
 }  // namespace moe

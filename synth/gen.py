@@ -284,3 +284,44 @@ def device_layer_weights(cfg: LayerConfig, seed: int, layer: int, device, count:
             out[name] = w
         del w
     return out
+
+
+# ---------------------------------------------------------- draft trees
+def draft_tree(nodes: int, seed: int, width: int = 8, fanout: int = 4,
+               p_one: float = 0.0):
+    """A draft tree of `nodes` nodes in breadth-first order (parent(v) < v;
+    -1 = a child of the root token), built level by level with at most
+    `width` nodes per level and `fanout` children per node, plus each node's
+    draft probability given its parent: the children of one node share a
+    random split of at most probability 1 (the rest stays with tokens not
+    drafted).  With p_one > 0 that share of edges gets probability exactly 1
+    (equal scores of parent and child).  Returns (parent int32, q float32)."""
+    g = np.random.default_rng([seed, 7001, nodes])
+    parent = []
+    prev = [-1]
+    while len(parent) < nodes:
+        level = []
+        slots = [p for p in prev for _ in range(fanout if p >= 0 else width)]
+        g.shuffle(slots)
+        for p in sorted(slots[:min(width, nodes - len(parent))]):
+            level.append(len(parent))
+            parent.append(p)
+        prev = level
+    parent = np.asarray(parent, dtype=np.int32)
+    q = np.zeros(nodes, dtype=np.float32)
+    for p in np.unique(parent):
+        kids = np.flatnonzero(parent == p)
+        share = g.dirichlet(np.ones(len(kids) + 1))[:len(kids)]
+        q[kids] = np.sort(share)[::-1].astype(np.float32)
+    if p_one > 0:
+        q[g.random(nodes) < p_one] = 1.0
+    return parent, q
+
+
+def step_costs(k_max: int, seed: int):
+    """An increasing cost table C(1..k_max) (profiled step latency, arbitrary
+    unit): a fixed part plus a concave rise, with small noise."""
+    g = np.random.default_rng([seed, 7002, k_max])
+    k = np.arange(1, k_max + 1, dtype=np.float64)
+    c = 10.0 + 1.5 * k ** 0.8 + g.uniform(0.0, 0.05, k_max)
+    return np.maximum.accumulate(c).astype(np.float32)

@@ -55,7 +55,7 @@ def test_binding_signatures_match_header():
 
 def test_abi_version_and_status_strings():
     assert L.moe_abi_version() == 1
-    for s in range(7):
+    for s in range(8):
         assert L.status_str(s) and L.status_str(s) != "unknown status"
     assert L.status_str(99) == "unknown status"
 
@@ -173,6 +173,24 @@ def test_layer_auto_validation_before_launch():
     assert call(a9=FAKE + 4) == L.MOE_ERR_ARG            # misaligned bytes
     assert call(a11=need - 1) == L.MOE_ERR_WORKSPACE
     assert call(a7=L.MOE_FP8_E4M3) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_evict_validation_before_launch():
+    ev = L.lib.moe_evict_select
+    base = [FAKE, FAKE, FAKE, 16, FAKE, None, None, FAKE, FAKE, 256, None]
+    def call(**chg):
+        a = list(base)
+        for k, v in chg.items():
+            a[int(k[1:])] = v
+        return ev(*a)
+    assert call(a3=0) == L.MOE_ERR_ARG
+    assert call(a3=1025) == L.MOE_ERR_ARG
+    assert call(a0=None) == L.MOE_ERR_ARG
+    assert call(a4=FAKE + 2) == L.MOE_ERR_ARG
+    assert call(a5=FAKE + 4) == L.MOE_ERR_ARG          # scores must be 8-aligned
+    assert call(a7=None) == L.MOE_ERR_ARG
+    assert call(a9=255) == L.MOE_ERR_WORKSPACE
+    assert call(a8=FAKE + 128) == L.MOE_ERR_WORKSPACE
 
 
 def test_routing_and_combine_validation():
