@@ -239,6 +239,29 @@ moe_status moe_evict_select(const int32_t* parent, const float* q, const float* 
                             int32_t* order, double* scores, double* expected, int32_t* k_best,
                             void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* EcoSpec cost-aware draft selection ("Less Experts, Faster Decoding:
+ * Cost-Aware Speculative Decoding for Mixture-of-Experts", Sec. 4.2, Eqs.
+ * (7)-(9), Algorithm 1): gamma times, score every unselected node by
+ * P / (|path footprint \ B| + eps), select the best and add its path
+ * footprint to the buffer B.
+ *   parent, q  (device) as moe_evict_select (P = float64 product of q over the
+ *              path, from the root out; q in [0, 1])
+ *   pred       (device) uint64 [N][W]: predicted (layer, expert) set of each
+ *              node as a bitset, bit l*E + e in word (l*E + e) / 64
+ *   buffer0    (device, optional) uint64 [W]: experts already resident; NULL =
+ *              empty
+ *   selected   (device) int32 [gamma]: nodes in selection order (equal scores:
+ *              the lower index, so every prefix is ancestor-closed)
+ *   buffer_out (device, optional) uint64 [W]: the final buffer
+ *   ws         workspace (>= 256 bytes, 256-aligned) for the error word.
+ * 1 <= gamma <= N <= 1024, 1 <= W <= 256, N * W <= 8192, eps > 0.
+ * Errors: MOE_ERR_ARG / _UNSUPPORTED (N * W) on the host; an invalid tree or
+ * probability records MOE_ERR_BAD_TREE. */
+moe_status moe_ecospec_select(const int32_t* parent, const float* q, const uint64_t* pred,
+                              const uint64_t* buffer0, int32_t N, int32_t W, int32_t gamma,
+                              double eps, int32_t* selected, uint64_t* buffer_out, void* ws,
+                              size_t ws_bytes, moe_stream_t stream);
+
 /* Bytes of workspace any FFN or layer call needs for passes of up to n_max
  * tokens (0 for an invalid shape). */
 size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode);

@@ -70,6 +70,8 @@ _SIG = {
     "moe_verify_layer_auto": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I,
                                    C.c_float, _P, _I, _P, _P, _P, C.c_size_t, _P]),
     "moe_evict_select": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_ecospec_select": (_I, [_P, _P, _P, _P, _I, _I, _I, C.c_double, _P, _P, _P, C.c_size_t,
+                                _P]),
     "moe_workspace_size": (C.c_size_t, [C.POINTER(moe_shape), _I, _I]),
     "moe_workspace_init": (_I, [_P, C.c_size_t, _P]),
     "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
@@ -187,6 +189,13 @@ def moe_evict_select(parent, q, cost, N, order, scores, expected, k_best, ws, ws
     _check(lib.moe_evict_select(ptr(parent), ptr(q), ptr(cost), N, ptr(order), ptr(scores),
                                 ptr(expected), ptr(k_best), ptr(ws), ws_bytes, _stream(stream)),
            "moe_evict_select")
+
+
+def moe_ecospec_select(parent, q, pred, buffer0, N, W, gamma, eps, selected, buffer_out, ws,
+                       ws_bytes, stream=None) -> None:
+    _check(lib.moe_ecospec_select(ptr(parent), ptr(q), ptr(pred), ptr(buffer0), N, W, gamma,
+                                  float(eps), ptr(selected), ptr(buffer_out), ptr(ws), ws_bytes,
+                                  _stream(stream)), "moe_ecospec_select")
 
 
 def moe_workspace_size(shape: moe_shape, n_max: int, mode: int) -> int:

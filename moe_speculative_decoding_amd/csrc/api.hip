@@ -13,6 +13,8 @@ using moe::kHOffset;
 
 constexpr int kMaxN = 32, kMaxK = 8, kMaxE = 256, kMaxS = 4, kMaxDim = 65536;
 constexpr int kMaxTreeNodes = 1024;
+constexpr int kMaxSetWords = 256;          // 64-bit words of one (layer, expert) set
+constexpr int kMaxTreeSetWords = 8192;     // N * W: the footprints fit 64 KB of LDS
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -374,6 +376,27 @@ moe_status moe_evict_select(const int32_t* parent, const float* q, const float* 
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_evict(parent, q, cost, N, order, scores, expected, k_best,
                                       static_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_ecospec_select(const int32_t* parent, const float* q, const uint64_t* pred,
+                              const uint64_t* buffer0, int32_t N, int32_t W, int32_t gamma,
+                              double eps, int32_t* selected, uint64_t* buffer_out, void* ws,
+                              size_t ws_bytes, moe_stream_t stream) {
+  if (N < 1 || N > kMaxTreeNodes || W < 1 || W > kMaxSetWords || gamma < 1 || gamma > N)
+    return MOE_ERR_ARG;
+  if (static_cast<long long>(N) * W > kMaxTreeSetWords) return MOE_ERR_UNSUPPORTED;
+  if (!(eps > 0.0) || eps > 1e300) return MOE_ERR_ARG;
+  const void* need4[3] = {parent, q, selected};
+  for (const void* p : need4)
+    if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+  if (pred == nullptr || !aligned(pred, 8)) return MOE_ERR_ARG;
+  if ((buffer0 != nullptr && !aligned(buffer0, 8)) ||
+      (buffer_out != nullptr && !aligned(buffer_out, 8)))
+    return MOE_ERR_ARG;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_ecospec(parent, q, pred, buffer0, N, W, gamma, eps, selected,
+                                        buffer_out, static_cast<uint32_t*>(ws),
+                                        static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, moe_stream_t stream) {

@@ -152,6 +152,9 @@ hipError_t launch_layer(const LayerParams& lp, int w_dtype, hipStream_t s);
 hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
                           int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t* pred,
+                          const uint64_t* buffer0, int N, int W, int gamma, double eps,
+                          int32_t* selected, uint64_t* buffer_out, uint32_t* err, hipStream_t s);
 hipError_t launch_evict(const int32_t* parent, const float* q, const float* cost, int N,
                         int32_t* order, double* scores, double* expected, int32_t* k_best,
                         uint32_t* err, hipStream_t s);

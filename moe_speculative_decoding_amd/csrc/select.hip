@@ -143,4 +143,136 @@ hipError_t launch_evict(const int32_t* parent, const float* q, const float* cost
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ EcoSpec
+// EcoSpec ("Less Experts, Faster Decoding: Cost-Aware Speculative Decoding for
+// Mixture-of-Experts", Sec. 4.2, Algorithm 1): each node's path footprint is
+// the union of the predicted (layer, expert) sets on its root path (Eq. (7));
+// gamma times, every unselected node is scored P / (|footprint \ B| + eps)
+// (Eqs. (8)-(9)), the best is selected and its footprint joins the buffer B.
+//
+// The footprints are bitsets of W 64-bit words held in LDS; a step's costs are
+// popcounts of (footprint AND NOT B) summed per node with LDS atomics (an
+// integer sum, so the order does not matter); scores are float64 divisions of
+// the same operands on every side; equal scores select the lower index.
+constexpr int kMaxSetWordsPerNode = 256;
+
+__global__ __launch_bounds__(kSelectBlock) void ecospec_kernel(
+    const int32_t* __restrict__ parent, const float* __restrict__ q,
+    const uint64_t* __restrict__ pred, const uint64_t* __restrict__ buffer0, int N, int W,
+    int gamma, double eps, int32_t* __restrict__ selected, uint64_t* __restrict__ buffer_out,
+    uint32_t* __restrict__ err) {
+  extern __shared__ __attribute__((aligned(16))) uint64_t traj[];  // [N][W]
+  __shared__ int par[kSelectBlock];
+  __shared__ double P[kSelectBlock];
+  __shared__ int cost[kSelectBlock];
+  __shared__ unsigned char ready[2][kSelectBlock];
+  __shared__ unsigned char taken[kSelectBlock];
+  __shared__ uint64_t B[kMaxSetWordsPerNode];
+  __shared__ double best_s[kSelectBlock / kWave];
+  __shared__ int best_t[kSelectBlock / kWave];
+  __shared__ int pick, bad;
+  const int v = threadIdx.x;
+  const bool mine = v < N;
+  if (v == 0) bad = 0;
+  __syncthreads();
+  float qv = 0.0f;
+  if (mine) {
+    const int p = parent[v];
+    qv = q[v];
+    par[v] = p;
+    if (p < -1 || p >= v || !(qv >= 0.0f && qv <= 1.0f)) atomicOr(&bad, 1);
+  }
+  ready[0][v] = 0;
+  taken[v] = 0;
+  for (int i = v; i < N * W; i += kSelectBlock) traj[i] = pred[i];
+  for (int w = v; w < W; w += kSelectBlock) B[w] = buffer0 != nullptr ? buffer0[w] : 0ull;
+  __syncthreads();
+  if (bad) {  // uniform
+    if (v == 0) atomicOr(err, ERRBIT_BAD_TREE);
+    return;
+  }
+
+  // P and footprints, one tree level per round (Eq. (7); P from the root out)
+  int cur = 0;
+  bool done = !mine;
+  while (__syncthreads_or(!done)) {
+    unsigned char r = ready[cur][v];
+    if (!done) {
+      const int p = par[v];
+      if (p < 0 || ready[cur][p]) {
+        P[v] = (p < 0 ? 1.0 : P[p]) * static_cast<double>(qv);
+        if (p >= 0)
+          for (int w = 0; w < W; ++w) traj[v * W + w] |= traj[p * W + w];
+        r = 1;
+        done = true;
+      }
+    }
+    ready[cur ^ 1][v] = r;
+    cur ^= 1;
+  }
+  __syncthreads();
+
+  for (int it = 0; it < gamma; ++it) {
+    if (mine) cost[v] = 0;
+    __syncthreads();
+    // Eq. (8): new experts of every unselected node's footprint
+    for (int i = v; i < N * W; i += kSelectBlock) {
+      const int t = i / W;
+      if (!taken[t]) {
+        const int c = __popcll(traj[i] & ~B[i - t * W]);
+        if (c) atomicAdd(&cost[t], c);
+      }
+    }
+    __syncthreads();
+    // Eq. (9) and the argmax (equal scores: the lower index)
+    double sc = -1.0;
+    int t = N;
+    if (mine && !taken[v]) {
+      sc = P[v] / (static_cast<double>(cost[v]) + eps);
+      t = v;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+      const double s2 = __shfl_xor(sc, o);
+      const int t2 = __shfl_xor(t, o);
+      if (s2 > sc || (s2 == sc && t2 < t)) {
+        sc = s2;
+        t = t2;
+      }
+    }
+    if ((v & (kWave - 1)) == 0) {
+      best_s[v / kWave] = sc;
+      best_t[v / kWave] = t;
+    }
+    __syncthreads();
+    if (v == 0) {
+      double bs = best_s[0];
+      int bt = best_t[0];
+      for (int i = 1; i < kSelectBlock / kWave; ++i) {
+        if (best_s[i] > bs || (best_s[i] == bs && best_t[i] < bt)) {
+          bs = best_s[i];
+          bt = best_t[i];
+        }
+      }
+      pick = bt;
+      taken[bt] = 1;
+      selected[it] = bt;
+    }
+    __syncthreads();
+    const int pk = pick;
+    for (int w = v; w < W; w += kSelectBlock) B[w] |= traj[pk * W + w];  // buffer update
+    __syncthreads();
+  }
+  if (buffer_out != nullptr)
+    for (int w = v; w < W; w += kSelectBlock) buffer_out[w] = B[w];
+}
+
+hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t* pred,
+                          const uint64_t* buffer0, int N, int W, int gamma, double eps,
+                          int32_t* selected, uint64_t* buffer_out, uint32_t* err, hipStream_t s) {
+  const size_t smem = static_cast<size_t>(N) * W * sizeof(uint64_t);
+  hipLaunchKernelGGL(ecospec_kernel, dim3(1), dim3(kSelectBlock), smem, s, parent, q, pred,
+                     buffer0, N, W, gamma, eps, selected, buffer_out, err);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -11,5 +11,5 @@ from .moe_ref import (  # noqa: F401
 )
 from .evict_ref import evict_select, is_ancestor_closed, path_scores, rank_nodes  # noqa: F401,E402
 from .ecospec_ref import (  # noqa: F401,E402
-    cumulative_probability, ecospec_select, path_footprints, to_bitsets,
+    cumulative_probability, ecospec_select, path_footprints,
 )

@@ -18,7 +18,7 @@ Readings: the tree is given by parent indices with parent(t) < t (-1 for the
 root token(s)); P is the float64 product of the draft probabilities from the
 root outward; equal scores select the lower node index (a parent before its
 child, so the selection stays prefix-closed, Sec. 4.2 "Prefix Consistency");
-(layer, expert) sets are bitsets of W 64-bit words.
+(layer, expert) sets are Python sets of pairs here.
 """
 from __future__ import annotations
 
@@ -66,15 +66,3 @@ def ecospec_select(parent: Sequence[int], q: Sequence[float], pred: Sequence[set
         selected.append(best)
         B |= traj[best]
     return {"selected": selected, "P": P, "steps": steps, "buffer": B}
-
-
-def to_bitsets(sets: Sequence[set], layers: int, experts: int) -> np.ndarray:
-    """(layer, expert) sets -> uint64 [len][W], bit l*experts + e."""
-    bits = layers * experts
-    W = (bits + 63) // 64
-    out = np.zeros((len(sets), W), dtype=np.uint64)
-    for i, s in enumerate(sets):
-        for (l, e) in s:
-            b = l * experts + e
-            out[i, b // 64] |= np.uint64(1) << np.uint64(b % 64)
-    return out

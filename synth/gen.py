@@ -325,3 +325,36 @@ def step_costs(k_max: int, seed: int):
     k = np.arange(1, k_max + 1, dtype=np.float64)
     c = 10.0 + 1.5 * k ** 0.8 + g.uniform(0.0, 0.05, k_max)
     return np.maximum.accumulate(c).astype(np.float32)
+
+
+def expert_bitsets(sets, layers: int, experts: int) -> np.ndarray:
+    """(layer, expert) sets -> uint64 [len(sets)][W]: bit l*experts + e in word
+    (l*experts + e) // 64 (the layout of the selection kernels' footprints)."""
+    bits = layers * experts
+    W = (bits + 63) // 64
+    out = np.zeros((len(sets), W), dtype=np.uint64)
+    for i, s in enumerate(sets):
+        for (l, e) in s:
+            b = l * experts + e
+            out[i, b // 64] |= np.uint64(1) << np.uint64(b % 64)
+    return out
+
+
+def predicted_sets(nodes: int, layers: int, experts: int, k: int, seed: int, parent=None,
+                   p_keep: float = 0.6):
+    """Predicted (layer, expert) sets of draft nodes: per layer k experts; a
+    node keeps each of its parent's experts with probability p_keep and fills
+    the rest uniformly (Markov reuse along tree edges, as the routing recipe)."""
+    g = np.random.default_rng([seed, 7003, nodes, layers, experts])
+    out = []
+    for v in range(nodes):
+        p = -1 if parent is None else int(parent[v])
+        s = set()
+        for l in range(layers):
+            prev = sorted(e for (ll, e) in out[p] if ll == l) if p >= 0 else []
+            keep = [e for e in prev if g.random() < p_keep]
+            rest = [e for e in range(experts) if e not in keep]
+            fill = g.choice(rest, size=k - len(keep), replace=False).tolist() if k > len(keep) else []
+            s.update((l, int(e)) for e in keep + fill)
+        out.append(s)
+    return out

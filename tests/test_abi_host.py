@@ -193,6 +193,26 @@ def test_evict_validation_before_launch():
     assert call(a8=FAKE + 128) == L.MOE_ERR_WORKSPACE
 
 
+def test_ecospec_validation_before_launch():
+    ec = L.lib.moe_ecospec_select
+    base = [FAKE, FAKE, FAKE, None, 16, 4, 4, 0.1, FAKE, None, FAKE, 256, None]
+    def call(**chg):
+        a = list(base)
+        for k, v in chg.items():
+            a[int(k[1:])] = v
+        return ec(*a)
+    assert call(a4=0) == L.MOE_ERR_ARG                 # N
+    assert call(a5=257) == L.MOE_ERR_ARG               # W
+    assert call(a6=17) == L.MOE_ERR_ARG                # gamma > N
+    assert call(a6=0) == L.MOE_ERR_ARG
+    assert call(a4=1024, a5=9, a6=4) == L.MOE_ERR_UNSUPPORTED  # N*W beyond 64 KB of LDS
+    assert call(a7=0.0) == L.MOE_ERR_ARG               # eps
+    assert call(a7=float("nan")) == L.MOE_ERR_ARG
+    assert call(a2=FAKE + 4) == L.MOE_ERR_ARG          # pred must be 8-aligned
+    assert call(a8=None) == L.MOE_ERR_ARG
+    assert call(a11=100) == L.MOE_ERR_WORKSPACE
+
+
 def test_routing_and_combine_validation():
     rt = L.lib.moe_route_topk
     assert rt(FAKE, 0, 8, 2, FAKE, FAKE, None) == L.MOE_ERR_ARG

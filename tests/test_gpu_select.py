@@ -107,3 +107,72 @@ def test_evict_rejects_invalid_trees_on_device(bad):
         cost[4] = 0.0
     _, _, _, k, err = run_evict(parent, q, cost)
     assert err == L.MOE_ERR_BAD_TREE and k == 0
+
+
+# ------------------------------------------------------------------ EcoSpec
+import json  # noqa: E402
+import os  # noqa: E402
+
+from synth.gen import expert_bitsets, predicted_sets  # noqa: E402
+
+
+def run_ecospec(parent, q, bits, gamma, eps, buffer0=None):
+    N, W = bits.shape
+    d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=dt))).to(DEV)
+    d_par, d_q = d(parent, np.int32), d(q, np.float32)
+    d_pred = d(bits.view(np.int64), np.int64)
+    d_b0 = d(np.asarray(buffer0, dtype=np.uint64).view(np.int64), np.int64) if buffer0 is not None else None
+    sel = torch.full((gamma,), -1, dtype=torch.int32, device=DEV)
+    bout = torch.zeros(W, dtype=torch.int64, device=DEV)
+    ws = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    L.moe_ecospec_select(d_par, d_q, d_pred, d_b0, N, W, gamma, eps, sel, bout, ws, 256)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy().tolist(), bout.cpu().numpy().view(np.uint64), L.moe_get_error(ws)
+
+
+def check_ecospec(parent, q, sets, layers, experts, gamma, eps, buffer0=None):
+    print("ecospec N=%d L=%d E=%d gamma=%d" % (len(parent), layers, experts, gamma), flush=True)
+    bits = expert_bitsets(sets, layers, experts)
+    b0 = expert_bitsets([buffer0], layers, experts)[0] if buffer0 is not None else None
+    ref = oracle.ecospec_select(parent, q, sets, gamma, eps, buffer0=buffer0)
+    sel, bout, err = run_ecospec(parent, q, bits, gamma, eps, b0)
+    assert err == L.MOE_OK
+    assert sel == ref["selected"]
+    assert np.array_equal(bout, expert_bitsets([ref["buffer"]], layers, experts)[0])
+    return sel
+
+
+def test_ecospec_figure3_on_device():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "ecospec_fig3.json")))
+    rd = g["reading"]
+    sets = [set((0, e) for e in es) for es in rd["pred_experts"]]
+    sel = check_ecospec(rd["parent"], rd["q"], sets, 1, 8, 2, rd["eps"])
+    assert ["t%d" % t for t in sel] == g["stated"]["final_selected"]
+
+
+@pytest.mark.parametrize("N,L_,E,k,gamma,seed", [
+    (1, 1, 8, 2, 1, 0), (14, 16, 64, 8, 4, 1), (32, 48, 128, 8, 8, 2), (64, 16, 64, 8, 32, 3),
+    (120, 4, 64, 6, 60, 4), (1024, 2, 64, 4, 16, 5), (35, 58, 256, 8, 12, 6),
+])
+def test_ecospec_matches_oracle(N, L_, E, k, gamma, seed):
+    parent, q = draft_tree(N, seed, p_one=0.1)
+    sets = predicted_sets(N, L_, E, k, seed, parent)
+    check_ecospec(parent, q, sets, L_, E, gamma, 0.1)
+
+
+def test_ecospec_initial_buffer_and_empty_footprints():
+    parent, q = draft_tree(40, 21)
+    sets = predicted_sets(40, 8, 32, 4, 21, parent)
+    check_ecospec(parent, q, sets, 8, 32, 10, 0.05, buffer0=sets[3] | sets[7])
+    empty = [set() for _ in range(40)]
+    sel = check_ecospec(parent, q, empty, 8, 32, 10, 0.5)
+    assert sel == oracle.evict_select(parent, q, [1.0] * 40)["order"][:10]
+
+
+def test_ecospec_rejects_invalid_tree_on_device():
+    parent, q = draft_tree(16, 22)
+    parent = parent.copy()
+    parent[4] = 10
+    bits = expert_bitsets(predicted_sets(16, 2, 16, 2, 22), 2, 16)
+    _, _, err = run_ecospec(parent, q, bits, 4, 0.1)
+    assert err == L.MOE_ERR_BAD_TREE

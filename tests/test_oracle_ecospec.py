@@ -90,9 +90,10 @@ def test_initial_buffer_makes_covered_experts_free():
     assert oracle.ecospec_select(parent, q, pred, 1, 0.1, buffer0={(0, 1), (0, 2)})["selected"] == [0]
 
 
-def test_bitset_layout():
+def test_bitset_layout_of_the_input_generator():
+    from synth.gen import expert_bitsets
     # bit l*experts + e: (1, 3) -> 43 in word 0, (1, 30) -> 70 = word 1, bit 6
-    bits = oracle.to_bitsets([{(0, 0), (1, 3), (1, 30)}, set()], layers=2, experts=40)
+    bits = expert_bitsets([{(0, 0), (1, 3), (1, 30)}, set()], layers=2, experts=40)
     assert bits.shape == (2, 2)
     assert int(bits[0, 0]) == 1 | (1 << 43) and int(bits[0, 1]) == 1 << 6
     assert not bits[1].any()
