@@ -406,6 +406,40 @@ def main():
     log("dispatch: %s" % json.dumps(dispatch))
     log("draft length: %s" % json.dumps(draft))
 
+    # ---- draft-tree selection ahead of the verify pass: EVICT truncation
+    # (cost table = the measured per-op times above) and EcoSpec selection
+    from synth.gen import draft_tree, expert_bitsets, predicted_sets
+    sel_ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+    selection = {}
+    for N in (32, 64, 1024):
+        parent, q = draft_tree(N, 0)
+        k = np.arange(1, N + 1)
+        cost = np.interp(k + 1, np.arange(1, 9), [1e6 * model[n]["t_best"] for n in range(1, 9)])
+        d_par = torch.from_numpy(parent).to(dev)
+        d_q = torch.from_numpy(q).to(dev)
+        d_c = torch.from_numpy(cost.astype(np.float32)).to(dev)
+        order = torch.empty(N, dtype=torch.int32, device=dev)
+        kb = torch.empty(1, dtype=torch.int32, device=dev)
+        g = capture(lambda: [L.moe_evict_select(d_par, d_q, d_c, N, order, None, None, kb, sel_ws,
+                                                256) for _ in range(8)])
+        selection["evict_N%d_us" % N] = round(1e6 * time_graph(g, 8), 2)
+        del g
+    for N, nl, ne, kk, gamma in ((14, 16, 64, 8, 4), (64, 48, 128, 8, 16)):
+        parent, q = draft_tree(N, 1)
+        bits = expert_bitsets(predicted_sets(N, nl, ne, kk, 1, parent), nl, ne)
+        d_par = torch.from_numpy(parent).to(dev)
+        d_q = torch.from_numpy(q).to(dev)
+        d_pred = torch.from_numpy(bits.view(np.int64)).to(dev)
+        selv = torch.empty(gamma, dtype=torch.int32, device=dev)
+        g = capture(lambda: [L.moe_ecospec_select(d_par, d_q, d_pred, None, N, bits.shape[1], gamma,
+                                                  0.1, selv, None, sel_ws, 256)
+                             for _ in range(8)])
+        selection["ecospec_N%d_L%d_E%d_g%d_us" % (N, nl, ne, gamma)] = round(1e6 * time_graph(g, 8), 2)
+        del g
+    if L.moe_get_error(sel_ws) != L.MOE_OK:
+        raise RuntimeError("selection kernels set the error word")
+    log("selection: %s" % json.dumps(selection))
+
     tot_b = sum(per_n[n]["union_bytes"] for n in ns)
     tot_t = sum(per_n[n]["t_layer_dedup"] for n in ns)
     achieved = tot_b / tot_t / 1e9
@@ -449,7 +483,7 @@ def main():
                                % (args.p, args.layers),
                    "global_batch": sum(ns) * args.layers, "seq_len": 1, "parallelism": "none"},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fit": fit,
-        "dispatch": dispatch, "draft_length": draft,
+        "dispatch": dispatch, "draft_length": draft, "selection": selection,
     }
     if cold is not None:
         line["cold"] = cold

@@ -8,7 +8,9 @@
 // with C the profiled step latency (Eqs. (9)-(10)), computed as prefix sums of
 // the sorted scores, a division by the cost table and an argmax (Sec. 3.2.3).
 //
-// One workgroup holds the whole tree in LDS (N <= 1024 nodes, parent(v) < v).
+// One workgroup holds the whole tree in LDS (N <= 1024 nodes, parent(v) < v);
+// its size follows N (one wavefront for the trees of 64 nodes or fewer that
+// draft steps produce), so the barriers cost little.
 // Scores are float64 products taken from the root outward, one tree level per
 // step, so every score has the same value as the plain path product; nodes
 // are ranked by counting the nodes ahead of them (equal scores: the lower
@@ -17,19 +19,63 @@
 
 namespace moe {
 
-constexpr int kSelectBlock = 1024;
+constexpr int kSelectMax = 1024;          // largest tree / workgroup
+constexpr int kSelectWaves = kSelectMax / kWave;
 
-__global__ __launch_bounds__(kSelectBlock) void evict_kernel(
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// first maximum of (value, index) over the workgroup: equal values give the
+// lower index.  Every thread calls it; thread 0 returns the index.
+__device__ __forceinline__ int block_argmax(double u, int k, double* best_u, int* best_k) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double u2 = __shfl_xor(u, o);
+    const int k2 = __shfl_xor(k, o);
+    if (u2 > u || (u2 == u && k2 < k)) {
+      u = u2;
+      k = k2;
+    }
+  }
+  const int nw = static_cast<int>(blockDim.x) / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    best_u[threadIdx.x / kWave] = u;
+    best_k[threadIdx.x / kWave] = k;
+  }
+  __syncthreads();
+  int bk = best_k[0];
+  if (threadIdx.x == 0) {
+    double bu = best_u[0];
+    for (int i = 1; i < nw; ++i) {
+      if (best_u[i] > bu || (best_u[i] == bu && best_k[i] < bk)) {
+        bu = best_u[i];
+        bk = best_k[i];
+      }
+    }
+  }
+  return bk;
+}
+
+// the selection kernels' workgroup: threads >= nodes (tree level steps run a
+// thread per node), a multiple of a wavefront
+static int select_threads(int nodes, int want) {
+  int t = nodes > want ? nodes : want;
+  t = (t + kWave - 1) / kWave * kWave;
+  return t > kSelectMax ? kSelectMax : t;
+}
+
+__global__ __launch_bounds__(kSelectMax) void evict_kernel(
     const int32_t* __restrict__ parent, const float* __restrict__ q,
     const float* __restrict__ cost, int N, int32_t* __restrict__ order,
     double* __restrict__ scores_out, double* __restrict__ expected_out,
     int32_t* __restrict__ k_best, uint32_t* __restrict__ err) {
-  __shared__ int par[kSelectBlock];
-  __shared__ double s[kSelectBlock];
-  __shared__ double scan[2][kSelectBlock];
-  __shared__ unsigned char ready[2][kSelectBlock];
-  __shared__ double best_u[kSelectBlock / kWave];
-  __shared__ int best_k[kSelectBlock / kWave];
+  __shared__ int par[kSelectMax];
+  __shared__ double s[kSelectMax];
+  __shared__ double scan[2][kSelectMax];
+  __shared__ unsigned char ready[2][kSelectMax];
+  __shared__ double best_u[kSelectWaves];
+  __shared__ int best_k[kSelectWaves];
   __shared__ int bad;
   const int v = threadIdx.x;
   const bool mine = v < N;
@@ -102,44 +148,20 @@ __global__ __launch_bounds__(kSelectBlock) void evict_kernel(
 
   // Eq. (10): the first maximum of E_hat(T_k) / C(k), k = v + 1
   double u = -1.0;
-  int k = N + 1;
   if (mine) {
     const double e = scan[src][v];
     if (expected_out != nullptr) expected_out[v] = e;
     u = e / static_cast<double>(cost[v]);
-    k = v + 1;
   }
-  for (int o = 32; o >= 1; o >>= 1) {
-    const double u2 = __shfl_xor(u, o);
-    const int k2 = __shfl_xor(k, o);
-    if (u2 > u || (u2 == u && k2 < k)) {
-      u = u2;
-      k = k2;
-    }
-  }
-  if ((v & (kWave - 1)) == 0) {
-    best_u[v / kWave] = u;
-    best_k[v / kWave] = k;
-  }
-  __syncthreads();
-  if (v == 0) {
-    double bu = best_u[0];
-    int bk = best_k[0];
-    for (int i = 1; i < kSelectBlock / kWave; ++i) {
-      if (best_u[i] > bu || (best_u[i] == bu && best_k[i] < bk)) {
-        bu = best_u[i];
-        bk = best_k[i];
-      }
-    }
-    *k_best = bk;
-  }
+  const int kb = block_argmax(u, mine ? v + 1 : N + 1, best_u, best_k);
+  if (v == 0) *k_best = kb;
 }
 
 hipError_t launch_evict(const int32_t* parent, const float* q, const float* cost, int N,
                         int32_t* order, double* scores, double* expected, int32_t* k_best,
                         uint32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(evict_kernel, dim3(1), dim3(kSelectBlock), 0, s, parent, q, cost, N, order,
-                     scores, expected, k_best, err);
+  hipLaunchKernelGGL(evict_kernel, dim3(1), dim3(select_threads(N, kWave)), 0, s, parent, q, cost,
+                     N, order, scores, expected, k_best, err);
   return hipGetLastError();
 }
 
@@ -150,28 +172,31 @@ hipError_t launch_evict(const int32_t* parent, const float* q, const float* cost
 // gamma times, every unselected node is scored P / (|footprint \ B| + eps)
 // (Eqs. (8)-(9)), the best is selected and its footprint joins the buffer B.
 //
-// The footprints are bitsets of W 64-bit words held in LDS; a step's costs are
-// popcounts of (footprint AND NOT B) summed per node with LDS atomics (an
-// integer sum, so the order does not matter); scores are float64 divisions of
-// the same operands on every side; equal scores select the lower index.
+// The footprints are bitsets of W 64-bit words held in LDS; a step's cost of
+// a node is the popcount of (footprint AND NOT B) summed by one wavefront
+// (an integer sum, so the order does not matter); scores are float64
+// divisions of the same operands on every side; equal scores select the
+// lower index.
 constexpr int kMaxSetWordsPerNode = 256;
 
-__global__ __launch_bounds__(kSelectBlock) void ecospec_kernel(
+__global__ __launch_bounds__(kSelectMax) void ecospec_kernel(
     const int32_t* __restrict__ parent, const float* __restrict__ q,
     const uint64_t* __restrict__ pred, const uint64_t* __restrict__ buffer0, int N, int W,
     int gamma, double eps, int32_t* __restrict__ selected, uint64_t* __restrict__ buffer_out,
     uint32_t* __restrict__ err) {
   extern __shared__ __attribute__((aligned(16))) uint64_t traj[];  // [N][W]
-  __shared__ int par[kSelectBlock];
-  __shared__ double P[kSelectBlock];
-  __shared__ int cost[kSelectBlock];
-  __shared__ unsigned char ready[2][kSelectBlock];
-  __shared__ unsigned char taken[kSelectBlock];
+  __shared__ int par[kSelectMax];
+  __shared__ double P[kSelectMax];
+  __shared__ int cost[kSelectMax];
+  __shared__ unsigned char ready[2][kSelectMax];
+  __shared__ unsigned char fresh[kSelectMax];
+  __shared__ unsigned char taken[kSelectMax];
   __shared__ uint64_t B[kMaxSetWordsPerNode];
-  __shared__ double best_s[kSelectBlock / kWave];
-  __shared__ int best_t[kSelectBlock / kWave];
+  __shared__ double best_s[kSelectWaves];
+  __shared__ int best_t[kSelectWaves];
   __shared__ int pick, bad;
-  const int v = threadIdx.x;
+  const int v = threadIdx.x, nthr = blockDim.x;
+  const int wave = v / kWave, lane = v & (kWave - 1), nwaves = nthr / kWave;
   const bool mine = v < N;
   if (v == 0) bad = 0;
   __syncthreads();
@@ -184,94 +209,77 @@ __global__ __launch_bounds__(kSelectBlock) void ecospec_kernel(
   }
   ready[0][v] = 0;
   taken[v] = 0;
-  for (int i = v; i < N * W; i += kSelectBlock) traj[i] = pred[i];
-  for (int w = v; w < W; w += kSelectBlock) B[w] = buffer0 != nullptr ? buffer0[w] : 0ull;
+  for (int i = v; i < N * W; i += nthr) traj[i] = pred[i];
+  for (int w = v; w < W; w += nthr) B[w] = buffer0 != nullptr ? buffer0[w] : 0ull;
   __syncthreads();
   if (bad) {  // uniform
     if (v == 0) atomicOr(err, ERRBIT_BAD_TREE);
     return;
   }
 
-  // P and footprints, one tree level per round (Eq. (7); P from the root out)
+  // P and footprints, one tree level per round (Eq. (7); P from the root out):
+  // a node whose parent is complete takes its P, then every thread ORs the
+  // parent's words into the fresh nodes' footprints
   int cur = 0;
   bool done = !mine;
   while (__syncthreads_or(!done)) {
-    unsigned char r = ready[cur][v];
+    unsigned char f = 0;
     if (!done) {
       const int p = par[v];
       if (p < 0 || ready[cur][p]) {
         P[v] = (p < 0 ? 1.0 : P[p]) * static_cast<double>(qv);
-        if (p >= 0)
-          for (int w = 0; w < W; ++w) traj[v * W + w] |= traj[p * W + w];
-        r = 1;
+        f = 1;
         done = true;
       }
     }
-    ready[cur ^ 1][v] = r;
+    fresh[v] = f;
+    __syncthreads();
+    for (int i = v; i < N * W; i += nthr) {
+      const int t = i / W;
+      if (fresh[t] && par[t] >= 0) traj[i] |= traj[par[t] * W + (i - t * W)];
+    }
+    ready[cur ^ 1][v] = ready[cur][v] | f;
     cur ^= 1;
   }
   __syncthreads();
 
   for (int it = 0; it < gamma; ++it) {
-    if (mine) cost[v] = 0;
-    __syncthreads();
-    // Eq. (8): new experts of every unselected node's footprint
-    for (int i = v; i < N * W; i += kSelectBlock) {
-      const int t = i / W;
-      if (!taken[t]) {
-        const int c = __popcll(traj[i] & ~B[i - t * W]);
-        if (c) atomicAdd(&cost[t], c);
-      }
+    // Eq. (8): new experts of every unselected node's footprint, a wavefront
+    // per node
+    for (int t = wave; t < N; t += nwaves) {
+      if (taken[t]) continue;  // uniform in the wavefront
+      int c = 0;
+      for (int w = lane; w < W; w += kWave) c += __popcll(traj[t * W + w] & ~B[w]);
+      c = wave_sum_i32(c);
+      if (lane == 0) cost[t] = c;
     }
     __syncthreads();
     // Eq. (9) and the argmax (equal scores: the lower index)
     double sc = -1.0;
-    int t = N;
-    if (mine && !taken[v]) {
-      sc = P[v] / (static_cast<double>(cost[v]) + eps);
-      t = v;
-    }
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double s2 = __shfl_xor(sc, o);
-      const int t2 = __shfl_xor(t, o);
-      if (s2 > sc || (s2 == sc && t2 < t)) {
-        sc = s2;
-        t = t2;
-      }
-    }
-    if ((v & (kWave - 1)) == 0) {
-      best_s[v / kWave] = sc;
-      best_t[v / kWave] = t;
-    }
-    __syncthreads();
+    if (mine && !taken[v]) sc = P[v] / (static_cast<double>(cost[v]) + eps);
+    const int bt = block_argmax(sc, mine && !taken[v] ? v : N, best_s, best_t);
     if (v == 0) {
-      double bs = best_s[0];
-      int bt = best_t[0];
-      for (int i = 1; i < kSelectBlock / kWave; ++i) {
-        if (best_s[i] > bs || (best_s[i] == bs && best_t[i] < bt)) {
-          bs = best_s[i];
-          bt = best_t[i];
-        }
-      }
       pick = bt;
       taken[bt] = 1;
       selected[it] = bt;
     }
     __syncthreads();
     const int pk = pick;
-    for (int w = v; w < W; w += kSelectBlock) B[w] |= traj[pk * W + w];  // buffer update
+    for (int w = v; w < W; w += nthr) B[w] |= traj[pk * W + w];  // the buffer update
     __syncthreads();
   }
   if (buffer_out != nullptr)
-    for (int w = v; w < W; w += kSelectBlock) buffer_out[w] = B[w];
+    for (int w = v; w < W; w += nthr) buffer_out[w] = B[w];
 }
 
 hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t* pred,
                           const uint64_t* buffer0, int N, int W, int gamma, double eps,
                           int32_t* selected, uint64_t* buffer_out, uint32_t* err, hipStream_t s) {
   const size_t smem = static_cast<size_t>(N) * W * sizeof(uint64_t);
-  hipLaunchKernelGGL(ecospec_kernel, dim3(1), dim3(kSelectBlock), smem, s, parent, q, pred,
-                     buffer0, N, W, gamma, eps, selected, buffer_out, err);
+  // a wavefront per node for the cost sums, up to 16
+  const int threads = select_threads(N, kWave * (N < kSelectWaves ? N : kSelectWaves));
+  hipLaunchKernelGGL(ecospec_kernel, dim3(1), dim3(threads), smem, s, parent, q, pred, buffer0, N,
+                     W, gamma, eps, selected, buffer_out, err);
   return hipGetLastError();
 }
 
