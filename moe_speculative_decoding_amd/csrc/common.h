@@ -15,6 +15,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;  // 4 waves
+// The streaming kernels (expert FFN, one-launch pass) run one workgroup per
+// CU whose wavefronts share the CU's work through an LDS counter: sixteen
+// when the kernel fits 128 VGPRs (four per SIMD), else twelve (168 VGPRs).
+constexpr int kMaxStreamWaves = 16;
+#ifndef MOE_TUNE_NW16
+#define MOE_TUNE_NW16 0
+#endif
 
 enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
 enum { MODE_DEDUP = 0, MODE_PERSLOT = 1, MODE_AUTO = 2 };  // AUTO: the one-launch pass decides
@@ -136,8 +143,8 @@ inline int token_tile(int mode, int n) {
   return n >= 5 ? 8 : (n >= 3 ? 4 : (n == 2 ? 2 : 1));
 }
 
-// resident workgroups of a kernel of kBlock threads on the current device
-int resident_blocks(const void* fn, size_t smem);
+// resident workgroups of a kernel of `block` threads on the current device
+int resident_blocks(const void* fn, size_t smem, int block);
 
 hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* ids,
                              float* gates, hipStream_t s);

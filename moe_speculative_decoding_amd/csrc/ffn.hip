@@ -18,15 +18,18 @@
 
 namespace moe {
 
-template <int WT, int TC, int R, int NMAT, int SPC>
-__global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
+// one workgroup of NW wavefronts per CU (NW / 4 per SIMD)
+template <int WT, int TC, int R, int NMAT, int SPC, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+void ffn_stream_kernel(FfnParams p) {
   constexpr bool UP = NMAT == 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   __shared__ int tok_h[2 * TC];
   __shared__ float* tok_y[2 * TC];
   __shared__ Meta mt;
+  __shared__ int claim;
   const int rows = UP ? p.f : p.d;
-  const int upg = (rows + (kBlock / kWave) * R - 1) / ((kBlock / kWave) * R);
+  const int upg = units_per_group(rows, R);
 
   if (!UP && blockIdx.x == 0 && threadIdx.x == 0 && p.bytes != nullptr) {
     const unsigned long long req =
@@ -58,33 +61,35 @@ __global__ __launch_bounds__(kBlock) void ffn_stream_kernel(FfnParams p) {
 
   load_meta(p, mt);
   __syncthreads();
-  run_range<WT, TC, R, NMAT, SPC, false>(p, mt, U, lo, hi, xs, tok_h, tok_y, Sync{});
+  run_range<WT, TC, R, NMAT, SPC, false>(p, mt, U, lo, hi, xs, tok_h, tok_y, &claim, Sync{});
 }
 
 // ------------------------------------------------------------------ launch
 struct OccKey {
   const void* fn;
   size_t smem;
+  int block;
   int dev;
   bool operator<(const OccKey& o) const {
     if (fn != o.fn) return fn < o.fn;
     if (smem != o.smem) return smem < o.smem;
+    if (block != o.block) return block < o.block;
     return dev < o.dev;
   }
 };
 
 // resident workgroups of a kernel on the whole device (cached per process)
-int resident_blocks(const void* fn, size_t smem) {
+int resident_blocks(const void* fn, size_t smem, int block) {
   static std::mutex mu;
   static std::map<OccKey, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   std::lock_guard<std::mutex> g(mu);
-  const OccKey key{fn, smem, dev};
+  const OccKey key{fn, smem, block, dev};
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, smem) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, smem) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   const int total = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
@@ -96,48 +101,45 @@ template <int WT, int TC, int R, int NMAT, int SPC>
 static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   constexpr bool UP = NMAT == 2;
+  constexpr int NW = (MOE_TUNE_NW16 && TC <= 2 && WT != WT_FP8) ? 16 : 12;
+  constexpr int kStreamBlock = NW * kWave;
   const int rows = UP ? p.f : p.d;
   const int Kdim = UP ? p.d : p.f;
   const int Kpad = (Kdim + C::CH - 1) / C::CH * C::CH;
-  const void* fn = reinterpret_cast<const void*>(&ffn_stream_kernel<WT, TC, R, NMAT, SPC>);
+  const void* fn = reinterpret_cast<const void*>(&ffn_stream_kernel<WT, TC, R, NMAT, SPC, NW>);
   // A second token slot lets ranges that cross a group boundary take the
   // fast path; it is used only when it costs no resident workgroups.
   const size_t slot = static_cast<size_t>(TC) * Kpad * C::T::XB;
 #ifndef MOE_TUNE_SLOTS
   const int slots =
-      2 * slot <= 65536 && resident_blocks(fn, 2 * slot) >= resident_blocks(fn, slot) ? 2 : 1;
+      2 * slot <= 65536 && resident_blocks(fn, 2 * slot, kStreamBlock) >= resident_blocks(fn, slot, kStreamBlock) ? 2 : 1;
 #else
   const int slots = MOE_TUNE_SLOTS;
 #endif
   const size_t smem = slots * slot;
   FfnParams q = p;
   q.lds_slots = slots;
-  const int upg = (rows + (kBlock / kWave) * R - 1) / ((kBlock / kWave) * R);
+  const int upg = units_per_group(rows, R);
   const int groups_max = p.mode == MODE_DEDUP ? p.ucap + p.S : p.n * (p.K + p.S);
   const long long units_max = static_cast<long long>(groups_max) * upg;
-  long long grid = resident_blocks(fn, smem);
+  long long grid = resident_blocks(fn, smem, kStreamBlock);
   if (grid <= 0) return hipErrorInvalidConfiguration;
 #ifdef MOE_TUNE_MAXBPC
   if (grid > 256LL * MOE_TUNE_MAXBPC) grid = 256LL * MOE_TUNE_MAXBPC;
 #endif
   if (grid > units_max) grid = units_max;
-  hipLaunchKernelGGL((ffn_stream_kernel<WT, TC, R, NMAT, SPC>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kBlock), smem, s, q);
+  hipLaunchKernelGGL((ffn_stream_kernel<WT, TC, R, NMAT, SPC, NW>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kStreamBlock), smem, s, q);
   return hipGetLastError();
 }
 
 template <int WT, int TC>
 static hipError_t launch_pair(const FfnParams& p, hipStream_t s) {
-  // up: R rows of W_gate and W_up per wave; down: R rows of W_down per wave.
-  // fp8 (d = 7168): the up phase stages at most 4 tokens (56 KB of LDS)
-  constexpr int RU = WT == WT_FP8 ? 4 : kTuneRU;
-  constexpr int SPCU = WT == WT_FP8 ? 1 : kTuneSPCU;
-  constexpr int RD = kTuneRD;
-  constexpr int SPCD = WT == WT_FP8 ? 1 : kTuneSPCD;
-  constexpr int TCU = (WT == WT_FP8 && TC > 4) ? 4 : TC;
-  hipError_t e = launch_phase<WT, TCU, RU, 2, SPCU>(p, s);
+  // up: R rows of W_gate and W_up per wave; down: R rows of W_down per wave
+  using Tl = Tiles<WT, TC>;
+  hipError_t e = launch_phase<WT, Tl::TCU, Tl::RU, 2, Tl::SPCU>(p, s);
   if (e != hipSuccess) return e;
-  return launch_phase<WT, TC, RD, 1, SPCD>(p, s);
+  return launch_phase<WT, TC, Tl::RD, 1, Tl::SPCD>(p, s);
 }
 
 template <int WT>

@@ -34,6 +34,7 @@
 // The grid is the device's resident capacity for the kernel, so every
 // workgroup runs at once; each wait is bounded besides and records a
 // time-out in the error word instead of hanging.
+#include <algorithm>
 #include <map>
 #include <mutex>
 
@@ -50,17 +51,51 @@ struct RouteLds {
   int slot_rank[kMaxSlots];
 };
 constexpr size_t kRouteTopkOffset = (sizeof(RouteLds) + 15) / 16 * 16;
-constexpr size_t kRouteLogitsOffset = kRouteTopkOffset + (kBlock / kWave) * sizeof(TopkLds);
+constexpr size_t kRouteLogitsOffset = kRouteTopkOffset + kMaxStreamWaves * sizeof(TopkLds);
 
-// at most 168 VGPRs, so three workgroups fit on a CU (the streaming needs
-// the bytes in flight of three)
-template <int WT, int TCU, int RU, int SPCU, int TCD, int RD, int SPCD>
-#ifndef MOE_TUNE_WPE
-#define MOE_TUNE_WPE 3
-#endif
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MOE_TUNE_WPE)))
+// UP range b, then DOWN range b, with the tile shapes of token tile TC (the
+// two-kernel FFN's shapes for the same tile, so both run the same arithmetic)
+template <int WT, int TC>
+__device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt, int U, int NG,
+                                           uint8_t* xs, int* tok_h, float** tok_y, int* claim,
+                                           unsigned tag) {
+  using Tl = Tiles<WT, TC>;
+  const FfnParams& p = lp.f;
+  const int upg_u = units_per_group(p.f, Tl::RU);
+  const int upg_d = units_per_group(p.d, Tl::RD);
+  const long long NUu = static_cast<long long>(NG) * upg_u;
+  const long long NUd = static_cast<long long>(NG) * upg_d;
+  const int G = gridDim.x, b = blockIdx.x;
+  const Sync sy{lp.up_flags, tag, NUu, G, upg_u, p.err};
+  {
+    const long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
+    if (lo < hi)
+      run_range<WT, Tl::TCU, Tl::RU, 2, Tl::SPCU, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, claim,
+                                                         sy);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(lp.up_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  {
+    const long long lo = NUd * b / G, hi = NUd * (b + 1) / G;
+    if (lo < hi)
+      run_range<WT, TC, Tl::RD, 1, Tl::SPCD, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, claim, sy);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(lp.down_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// one workgroup of NW wavefronts per CU (NW / 4 per SIMD).  AUTO: the mode is
+// chosen per pass on the device; a per-slot pass then runs the per-slot tile
+// (one token), so it reproduces moe_expert_ffn_perslot bit for bit.
+template <int WT, int TC, int NW, bool AUTO>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void layer_kernel(LayerParams lp) {
-  constexpr int TCM = TCU > TCD ? TCU : TCD;
+  constexpr int kStreamWaves = NW, kStreamBlock = NW * kWave;
+  constexpr int TCM = TC;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   __shared__ int tok_h[2 * TCM];
   __shared__ float* tok_y[2 * TCM];
@@ -68,6 +103,7 @@ void layer_kernel(LayerParams lp) {
   __shared__ int ids_l[kMaxSlots];
   __shared__ float gates_l[kMaxSlots];
   __shared__ int U_l;
+  __shared__ int claim;  // next unit of the running phase (stream.h)
   const FfnParams& p = lp.f;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = p.n, K = p.K, E = p.E, S = p.S, nk = n * K;
@@ -80,18 +116,18 @@ void layer_kernel(LayerParams lp) {
     // eight loads per lane in flight at once (clamped in bounds), then the stores
     constexpr int kPer = 8;
     const int words = n * E;
-    for (int base = 0; base < words; base += kBlock * kPer) {
+    for (int base = 0; base < words; base += kStreamBlock * kPer) {
       float v[kPer];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) v[i] = lp.logits[min(base + i * kBlock + tid, words - 1)];
+      for (int i = 0; i < kPer; ++i) v[i] = lp.logits[min(base + i * kStreamBlock + tid, words - 1)];
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        if (base + i * kBlock + tid < words) lg[base + i * kBlock + tid] = v[i];
+        if (base + i * kStreamBlock + tid < words) lg[base + i * kStreamBlock + tid] = v[i];
     }
   }
   __syncthreads();
   TopkLds* tk = reinterpret_cast<TopkLds*>(xs + kRouteTopkOffset);
-  for (int t = wave; t < n; t += kBlock / kWave) {
+  for (int t = wave; t < n; t += kStreamWaves) {
     int id;
     float g;
     route_token(lg + t * E, E, K, lane, tk[wave], id, g);
@@ -116,22 +152,22 @@ void layer_kernel(LayerParams lp) {
                                                                                     : MODE_PERSLOT;
   }
   if (mode == MODE_PERSLOT)
-    for (int i = tid; i < nk; i += kBlock) mt.a[i] = ids_l[i];
+    for (int i = tid; i < nk; i += kStreamBlock) mt.a[i] = ids_l[i];
   if (tid == 0) mt.mode = mode;
   __syncthreads();
   if (blockIdx.x == 0) {
-    for (int i = tid; i < nk; i += kBlock) {
+    for (int i = tid; i < nk; i += kStreamBlock) {
       if (lp.ids != nullptr) lp.ids[i] = ids_l[i];
       if (lp.gates != nullptr) lp.gates[i] = gates_l[i];
     }
     if (mode == MODE_DEDUP && lp.U != nullptr) {
       const int cap = p.ucap;
-      for (int i = tid; i < nk; i += kBlock) {
+      for (int i = tid; i < nk; i += kStreamBlock) {
         lp.perm[i] = mt.c[i];
         lp.slot_rank[i] = rl.slot_rank[i];
       }
-      for (int i = tid; i < cap; i += kBlock) lp.union_ids[i] = mt.b[i];
-      for (int i = tid; i <= cap; i += kBlock) lp.offsets[i] = mt.a[i];
+      for (int i = tid; i < cap; i += kStreamBlock) lp.union_ids[i] = mt.b[i];
+      for (int i = tid; i <= cap; i += kStreamBlock) lp.offsets[i] = mt.a[i];
       if (tid == 0) *lp.U = U;
     }
     if (tid == 0 && p.bytes != nullptr) {
@@ -151,38 +187,22 @@ void layer_kernel(LayerParams lp) {
   __syncthreads();
   const unsigned tag = tag_l;
   const int NG = mode == MODE_DEDUP ? U + S : n * (K + S);
-  const int upg_u = (p.f + (kBlock / kWave) * RU - 1) / ((kBlock / kWave) * RU);
-  const int upg_d = (p.d + (kBlock / kWave) * RD - 1) / ((kBlock / kWave) * RD);
-  const long long NUu = static_cast<long long>(NG) * upg_u;
-  const long long NUd = static_cast<long long>(NG) * upg_d;
   const int G = gridDim.x, b = blockIdx.x;
-  const Sync sy{lp.up_flags, tag, NUu, G, upg_u, p.err};
-  {
-    const long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
-    if (lo < hi) run_range<WT, TCU, RU, 2, SPCU, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, sy);
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(lp.up_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  {
-    const long long lo = NUd * b / G, hi = NUd * (b + 1) / G;
-    if (lo < hi) run_range<WT, TCD, RD, 1, SPCD, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, sy);
-    wait_stores();
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(lp.down_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (AUTO && TC > 1 && mode == MODE_PERSLOT)
+    run_phases<WT, 1>(lp, mt, U, NG, xs, tok_h, tok_y, &claim, tag);
+  else
+    run_phases<WT, TC>(lp, mt, U, NG, xs, tok_h, tok_y, &claim, tag);
 
   // ---- combine: one lane per (token, 4 columns), first workgroups only
   const int quads = p.d / 4;
   const int tasks = n * quads;
-  if (b * kBlock >= tasks) return;
+  if (b * kStreamBlock >= tasks) return;
   wait_flags(lp.down_flags, 0, G - 1, tag, p.err);
   if (b == 0 && tid == 0)  // every workgroup has read the epoch: retire this call's flags
     __hip_atomic_store(lp.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const unsigned ys_size = static_cast<unsigned>(static_cast<size_t>(nk) * p.d * 4);
   const unsigned sh_size = static_cast<unsigned>(static_cast<size_t>(n) * S * p.d * 4);
-  for (int task = b * kBlock + tid; task < tasks; task += G * kBlock) {
+  for (int task = b * kStreamBlock + tid; task < tasks; task += G * kStreamBlock) {
     const int t = task / quads;
     const int c = (task - t * quads) * 4;
     u32x4 yv[8], sv[4];
@@ -237,46 +257,50 @@ void layer_kernel(LayerParams lp) {
 }
 
 // ------------------------------------------------------------------ launch
-template <int WT, int TCU, int RU, int SPCU, int TCD, int RD, int SPCD>
+// LDS bytes of one token slot (the larger of the UP and DOWN phases) of tile TC
+template <int WT, int TC>
+static size_t slot_bytes(const FfnParams& p) {
+  using Tl = Tiles<WT, TC>;
+  using CU = StreamCfg<WT, Tl::TCU, Tl::RU, 2, Tl::SPCU>;
+  using CD = StreamCfg<WT, TC, Tl::RD, 1, Tl::SPCD>;
+  const size_t su = static_cast<size_t>(Tl::TCU) * ((p.d + CU::CH - 1) / CU::CH * CU::CH) * CU::T::XB;
+  const size_t sd = static_cast<size_t>(TC) * ((p.f + CD::CH - 1) / CD::CH * CD::CH) * CD::T::XB;
+  return su > sd ? su : sd;
+}
+
+template <int WT, int TC, bool AUTO>
 static hipError_t launch_layer_t(const LayerParams& lp0, hipStream_t s) {
-  using CU = StreamCfg<WT, TCU, RU, 2, SPCU>;
-  using CD = StreamCfg<WT, TCD, RD, 1, SPCD>;
+  // sixteen wavefronts when the token tiles are small (the kernel then fits
+  // 128 VGPRs), else twelve
+  constexpr int NW = (MOE_TUNE_NW16 && TC <= 2 && WT != WT_FP8) ? 16 : 12;
+  constexpr int kStreamBlock = NW * kWave;
   const FfnParams& p = lp0.f;
-  const void* fn =
-      reinterpret_cast<const void*>(&layer_kernel<WT, TCU, RU, SPCU, TCD, RD, SPCD>);
-  const size_t slot_u = static_cast<size_t>(TCU) * ((p.d + CU::CH - 1) / CU::CH * CU::CH) * CU::T::XB;
-  const size_t slot_d = static_cast<size_t>(TCD) * ((p.f + CD::CH - 1) / CD::CH * CD::CH) * CD::T::XB;
-  const size_t slot = slot_u > slot_d ? slot_u : slot_d;
+  const void* fn = reinterpret_cast<const void*>(&layer_kernel<WT, TC, NW, AUTO>);
+  size_t slot = slot_bytes<WT, TC>(p);
+  if (AUTO) slot = std::max(slot, slot_bytes<WT, 1>(p));
   const size_t floor_bytes = kRouteLogitsOffset + static_cast<size_t>(p.n) * p.E * 4;
   auto need = [&](int slots) {
     const size_t b = slots * slot;
     return b > floor_bytes ? b : floor_bytes;
   };
-  const int slots =
-      2 * slot <= 65536 && resident_blocks(fn, need(2)) >= resident_blocks(fn, need(1)) ? 2 : 1;
+  const int slots = 2 * slot <= 65536 && resident_blocks(fn, need(2), kStreamBlock) >=
+                                              resident_blocks(fn, need(1), kStreamBlock)
+                        ? 2
+                        : 1;
   const size_t smem = need(slots);
   LayerParams lp = lp0;
   lp.f.lds_slots = slots;
-  int grid = resident_blocks(fn, smem);
+  int grid = resident_blocks(fn, smem, kStreamBlock);
   if (grid <= 0) return hipErrorInvalidConfiguration;
-#ifdef MOE_TUNE_MAXBPC
-  if (grid > 256 * MOE_TUNE_MAXBPC) grid = 256 * MOE_TUNE_MAXBPC;
-#endif
   if (grid > kMaxGrid) grid = kMaxGrid;
-  hipLaunchKernelGGL((layer_kernel<WT, TCU, RU, SPCU, TCD, RD, SPCD>), dim3(grid), dim3(kBlock),
-                     smem, s, lp);
+  hipLaunchKernelGGL((layer_kernel<WT, TC, NW, AUTO>), dim3(grid), dim3(kStreamBlock), smem, s, lp);
   return hipGetLastError();
 }
 
 template <int WT, int TC>
 static hipError_t launch_layer_tc(const LayerParams& lp, hipStream_t s) {
-  // the tile shapes of the two-kernel FFN
-  constexpr int RU = WT == WT_FP8 ? 4 : kTuneRU;
-  constexpr int SPCU = WT == WT_FP8 ? 1 : kTuneSPCU;
-  constexpr int RD = kTuneRD;
-  constexpr int SPCD = WT == WT_FP8 ? 1 : kTuneSPCD;
-  constexpr int TCU = (WT == WT_FP8 && TC > 4) ? 4 : TC;
-  return launch_layer_t<WT, TCU, RU, SPCU, TC, RD, SPCD>(lp, s);
+  return lp.f.mode == MODE_AUTO ? launch_layer_t<WT, TC, true>(lp, s)
+                                : launch_layer_t<WT, TC, false>(lp, s);
 }
 
 template <int WT>

@@ -78,7 +78,7 @@ struct Sync {
 // a wait that gives up records a time-out in the error word and goes on)
 __device__ __forceinline__ void wait_flags(const unsigned* flags, int c_lo, int c_hi, unsigned tag,
                                            uint32_t* err) {
-  for (int c = c_lo + static_cast<int>(threadIdx.x); c <= c_hi; c += kBlock) {
+  for (int c = c_lo + static_cast<int>(threadIdx.x); c <= c_hi; c += static_cast<int>(blockDim.x)) {
     int spins = 0;
     while (coh_load_u32(flags + c) != tag) {
       if (++spins > kSpinLimit) {
@@ -240,11 +240,11 @@ __device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
   const int nk = p.n * p.K;
   if (threadIdx.x == 0) m.mode = p.mode;
   if (p.mode == MODE_DEDUP) {
-    for (int i = threadIdx.x; i <= p.ucap; i += kBlock) m.a[i] = p.offsets[i];
-    for (int i = threadIdx.x; i < p.ucap; i += kBlock) m.b[i] = p.union_ids[i];
-    for (int i = threadIdx.x; i < nk; i += kBlock) m.c[i] = p.perm[i];
+    for (int i = threadIdx.x; i <= p.ucap; i += blockDim.x) m.a[i] = p.offsets[i];
+    for (int i = threadIdx.x; i < p.ucap; i += blockDim.x) m.b[i] = p.union_ids[i];
+    for (int i = threadIdx.x; i < nk; i += blockDim.x) m.c[i] = p.perm[i];
   } else {
-    for (int i = threadIdx.x; i < nk; i += kBlock) m.a[i] = p.ids[i];
+    for (int i = threadIdx.x; i < nk; i += blockDim.x) m.a[i] = p.ids[i];
   }
 }
 
@@ -281,16 +281,23 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 
 // ------------------------------------------------------------ the walk
 // One phase (up: gate/up rows, or down rows) is a list of units: (group g,
-// row block of 4*R rows), groups in order, row blocks in order.  Workgroup b
-// owns the contiguous unit range [b*NU/G, (b+1)*NU/G), so every workgroup
-// streams the same number of bytes and all finish together.  It walks its
-// range chunk by chunk (K split in chunks of SPC load steps): for each group
-// segment, for each token tile of that group, for each unit, for each chunk.
-// The walk is the same for every lane of the workgroup.
+// block of R rows), groups in order, row blocks in order.  Workgroup b owns
+// the contiguous unit range [b*NU/G, (b+1)*NU/G), so every workgroup streams
+// the same bytes to within one unit of R rows (a unit per wavefront, not per
+// workgroup: coarser units left workgroups with one or two of them, and the
+// ones with two set the phase's time).  Inside a group segment of the range
+// the four wavefronts take consecutive units, one step of four units at a
+// time; the walk goes chunk by chunk (K split in chunks of SPC load steps):
+// for each group segment, for each token tile of that group, for each step,
+// for each chunk.  The walk is the same for every lane of the workgroup.
+
+// units (blocks of R rows) of one group
+__host__ __device__ constexpr int units_per_group(int rows, int R) { return (rows + R - 1) / R; }
+
 struct Walk {
-  int g, tile, u, kc, done;
-  int ntile, seg_lo, seg_hi;
-  int valid;  // expert id in range
+  int g, tile, s, kc, done;
+  int ntile, ua, ub, nsteps;  // the segment's units [ua, ub) of group g, in steps of four
+  int valid;                  // expert id in range
   Group G;
 };
 
@@ -347,9 +354,11 @@ __device__ __forceinline__ void walk_group(const FfnParams& p, const Meta& mt, i
   w.ntile = (w.G.cnt + TC - 1) / TC;
   w.tile = 0;
   const long long glo = static_cast<long long>(g) * upg;
-  w.seg_lo = uni(static_cast<int>(lo > glo ? lo : glo));
-  w.seg_hi = uni(static_cast<int>(hi < glo + upg ? hi : glo + upg));
-  w.u = w.seg_lo;
+  w.ua = uni(static_cast<int>((lo > glo ? lo : glo) - glo));
+  w.ub = uni(static_cast<int>((hi < glo + upg ? hi : glo + upg) - glo));
+  const int nw = static_cast<int>(blockDim.x) >> 6;
+  w.nsteps = (w.ub - w.ua + nw - 1) / nw;
+  w.s = 0;
   w.kc = 0;
 }
 
@@ -358,16 +367,26 @@ __device__ __forceinline__ void walk_next(const FfnParams& p, const Meta& mt, in
                                           int nchunks, long long lo, long long hi, int upg) {
   if (++w.kc < nchunks) return;
   w.kc = 0;
-  if (++w.u < w.seg_hi) return;
+  if (++w.s < w.nsteps) return;
   if (++w.tile < w.ntile) {
-    w.u = w.seg_lo;
+    w.s = 0;
     return;
   }
-  if (w.seg_hi >= hi) {
+  if (static_cast<long long>(w.g + 1) * upg >= hi) {
     w.done = 1;
     return;
   }
   walk_group<TC>(p, mt, U, w, w.g + 1, lo, hi, upg);
+}
+
+// the unit a wavefront streams in step s of a segment [ua, ub): its first
+// row r0 (relative to the group) and its valid rows rv (0 beyond the segment)
+template <int R>
+__device__ __forceinline__ void wave_unit(int ua, int ub, int s, int wave, int rows, int& r0,
+                                          int& rv) {
+  const int unit = ua + s * (static_cast<int>(blockDim.x) >> 6) + wave;
+  r0 = unit * R;
+  rv = unit < ub ? min(R, rows - r0) : 0;
 }
 
 // ------------------------------------------------------- streaming kernel
@@ -375,15 +394,51 @@ __device__ __forceinline__ void walk_next(const FfnParams& p, const Meta& mt, in
 // DOWN (NMAT = 1): rows c of W_down (Kdim = f, tokens read from H) -> y[slot][c].
 // Each wave owns R rows of the current unit; the weights of the next chunk
 // are in flight while the current chunk is multiplied (two register buffers).
+// Matrix cores for tiles of four or more tokens (bf16 and fp8 weights): the
+// dot-product path spends about 8*TC VALU operations per 16 weight bytes,
+// which at eight tokens approaches the memory time; one 4x4x4 MFMA block
+// product covers four rows, four tokens and four K elements per lane.
+#ifndef MOE_TUNE_MFMA
+#define MOE_TUNE_MFMA 1
+#endif
+constexpr bool use_mfma(int WT, int TC, int R) {
+  return MOE_TUNE_MFMA && WT != WT_F32 && TC >= 4 && R == 4;
+}
+
+// Tile shapes shared by the two-kernel FFN and the one-launch pass (both must
+// run the same arithmetic): rows per wavefront R and load steps per chunk SPC
+// of the UP and DOWN phases, and the UP token tile (fp8, d = 7168: at most 4
+// tokens, 56 KB of LDS).  The matrix-core path takes four rows and keeps the
+// bytes per chunk of the dot-product path.
+template <int WT, int TC>
+struct Tiles {
+  static constexpr int TCU = (WT == WT_FP8 && TC > 4) ? 4 : TC;
+  static constexpr int RU0 = WT == WT_FP8 ? 4 : kTuneRU;
+  static constexpr int SPCU0 = WT == WT_FP8 ? 1 : kTuneSPCU;
+  static constexpr int RD0 = kTuneRD;
+  static constexpr int SPCD0 = WT == WT_FP8 ? 1 : kTuneSPCD;
+  static constexpr bool MFU = use_mfma(WT, TCU, 4), MFD = use_mfma(WT, TC, 4);
+  static constexpr int RU = MFU ? 4 : RU0;
+  static constexpr int SPCU = MFU ? SPCU0 * RU0 : SPCU0;
+  static constexpr int RD = MFD ? 4 : RD0;
+  static constexpr int SPCD = MFD ? SPCD0 * RD0 : SPCD0;
+};
+
 template <int WT, int TC, int R, int NMAT, int SPC>
 struct StreamCfg {
   using T = WTraits<WT>;
-  static constexpr int STEP = kWave * T::VEC;  // elements per load step
+  // MF: the products run on the matrix cores (4x4x4 bf16 blocks, see
+  // mul_chunk_mf); one load per matrix and step then covers the R = 4 rows.
+  static constexpr bool MF = use_mfma(WT, TC, R);
+  static constexpr int LR = MF ? 1 : R;                            // loads per matrix and step
+  static constexpr int STEP = MF ? kWave * T::VEC / 4 : kWave * T::VEC;  // elements of a row per step
   static constexpr int CH = SPC * STEP;        // elements per chunk
-  static constexpr int V = NMAT * R * TC;      // partial sums per lane
+  static constexpr int V = NMAT * R * TC;      // partial sums per lane (dot products)
+  static constexpr int NACC = MF ? NMAT * TC : V;  // accumulators per lane
   static constexpr int SH = 6 - ilog2(V);
-  static_assert((V & (V - 1)) == 0 && V <= 64, "values per lane must be a power of two <= 64");
-  static_assert(NMAT == 1 || V >= 2, "gate/up pairing needs two values");
+  static_assert(MF || ((V & (V - 1)) == 0 && V <= 64), "values per lane must be a power of two <= 64");
+  static_assert(MF || NMAT == 1 || V >= 2, "gate/up pairing needs two values");
+  static_assert(!MF || (R == 4 && TC % 4 == 0), "matrix-core path: four rows, tokens in fours");
 };
 
 // matrix MI's base pointer (0 gate, 1 up, 2 down), routed or shared; the
@@ -403,17 +458,49 @@ __device__ __forceinline__ const float* sptr(const FfnParams& p, int shared) {
 }
 
 template <int WT, int TC, int R, int NMAT, int SPC>
-__device__ __forceinline__ void load_chunk(const FfnParams& p, const Group& G, int live, int urel,
-                                           int kc, int rows, int Kdim, int lane, int wave,
-                                           u32x4 (&buf)[NMAT][SPC][R], float (&sc)[NMAT][SPC]) {
+__device__ __forceinline__ void load_chunk(
+    const FfnParams& p, const Group& G, int r0, int rv, int kc, int rows, int Kdim, int lane,
+    u32x4 (&buf)[NMAT][SPC][StreamCfg<WT, TC, R, NMAT, SPC>::LR], float (&sc)[NMAT][SPC]) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   using T = typename C::T;
+  if constexpr (C::MF) {
+    // lane 4b + i reads row r0 + i at K offset b * VEC of the step: a load
+    // covers four rows of STEP elements (16 lanes per row, contiguous), the
+    // A operand layout of the 4x4x4 block products
+    const int i = lane & 3, b = lane >> 2;
+    const size_t row_bytes = static_cast<size_t>(Kdim) * T::EB;
+    const size_t mat = static_cast<size_t>(rows) * row_bytes;
+    const int kb = Kdim / 128;
+    const int e = rv > 0 ? G.e : 0;
+    const bool rok = i < rv;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const uint8_t* base = (NMAT == 1 ? wptr<2>(p, G.shared)
+                                       : (m == 0 ? wptr<0>(p, G.shared) : wptr<1>(p, G.shared))) +
+                            static_cast<size_t>(e) * mat +
+                            static_cast<size_t>(rok ? r0 + i : 0) * row_bytes;
+      const float* sbase = nullptr;
+      if (WT == WT_FP8)
+        sbase = (NMAT == 1 ? sptr<2>(p, G.shared)
+                           : (m == 0 ? sptr<0>(p, G.shared) : sptr<1>(p, G.shared))) +
+                (static_cast<size_t>(e) * (rows / 128) + (rv > 0 ? r0 / 128 : 0)) * kb;
+#pragma unroll
+      for (int s = 0; s < SPC; ++s) {
+        const int k = kc * C::CH + s * C::STEP + b * T::VEC;
+        const bool ok = rok && k < Kdim;
+        const uint8_t* a = ok ? base + static_cast<size_t>(k) * T::EB : p.zeros;
+        buf[m][s][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+        if (WT == WT_FP8)
+          sc[m][s] = *(ok ? sbase + (k >> 7) : reinterpret_cast<const float*>(p.zeros));
+      }
+    }
+    return;
+  }
   // Every lane issues every load, outside any branch, and nothing inspects the
   // loaded value before the multiply, so the next chunk stays in flight while
   // the current one is used.  Masked lanes read 16 zero bytes of the
-  // workspace's control block instead of weights.
-  const int r0 = urel * (kBlock / kWave) * R + wave * R;
-  const int rv = live ? max(0, min(R, rows - r0)) : 0;
+  // workspace's control block instead of weights.  rv = 0 masks the whole
+  // unit (beyond the range, or an expert id out of range).
   const size_t row_bytes = static_cast<size_t>(Kdim) * T::EB;
   const size_t mat = static_cast<size_t>(rows) * row_bytes;
   const int kb = Kdim / 128;
@@ -452,7 +539,7 @@ __device__ __forceinline__ void load_chunk(const FfnParams& p, const Group& G, i
 
 template <int WT, int TC, int R, int NMAT, int SPC, int NT>
 __device__ __forceinline__ void mul_chunk_nt(int kc, int Kpad, int lane, const uint8_t* xs,
-                                             const u32x4 (&buf)[NMAT][SPC][R],
+                                             const u32x4 (&buf)[NMAT][SPC][StreamCfg<WT, TC, R, NMAT, SPC>::LR],
                                              const float (&sc)[NMAT][SPC], float* acc) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   using T = typename C::T;
@@ -475,15 +562,6 @@ __device__ __forceinline__ void mul_chunk_nt(int kc, int Kpad, int lane, const u
   }
 }
 
-// all TC staged tokens are multiplied: tokens beyond the tile's count are
-// zero in LDS, and a branch on the count would cost the prefetch pipeline
-template <int WT, int TC, int R, int NMAT, int SPC>
-__device__ __forceinline__ void mul_chunk(int kc, int Kpad, int lane, const uint8_t* xs,
-                                          const u32x4 (&buf)[NMAT][SPC][R],
-                                          const float (&sc)[NMAT][SPC], float* acc) {
-  mul_chunk_nt<WT, TC, R, NMAT, SPC, TC>(kc, Kpad, lane, xs, buf, sc, acc);
-}
-
 // tokens of (group, tile) -> LDS [TC][Kpad], zero beyond Kdim and beyond the
 // tile; the H row and output row of every token go to LDS too, so the
 // epilogue issues no global loads
@@ -502,7 +580,7 @@ __device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt,
     tok_h[threadIdx.x] = hrow;
     tok_y[threadIdx.x] = yrow;
   }
-  for (int v = threadIdx.x; v < TC * vpt; v += kBlock) {
+  for (int v = threadIdx.x; v < TC * vpt; v += blockDim.x) {
     const int tt = v / vpt;
     const int k = (v - tt * vpt) * EPV;
     u32x4 val = {0u, 0u, 0u, 0u};
@@ -525,22 +603,35 @@ __device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt,
   }
 }
 
-template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
-__device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int urel, int rows,
-                                            int lane, int wave, const int* tok_h,
-                                            float* const* tok_y, float* acc) {
-  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
-  Halve<C::V>::run(acc, lane, 32);
-  const int r0 = urel * (kBlock / kWave) * R + wave * R;
-  const int rv = max(0, min(R, rows - r0));
+// End of a unit whose tile holds at most NT of its TC tokens (the partial
+// sums of tokens NT..TC-1 are zero): the NMAT*R*NT sums of the lane are
+// compacted and reduced across the wavefront; the gate value of (row, token)
+// ends in lane l and the up value in lane l ^ 32.
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH, int NT>
+__device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int r0, int rv, int rows,
+                                            int lane, const int* tok_h, float* const* tok_y,
+                                            float* acc) {
+  constexpr int V = NMAT * R * NT;
+  constexpr int SH = 6 - ilog2(V);
+  static_assert(NT <= TC && (V & (V - 1)) == 0 && V <= 64 && (NMAT == 1 || V >= 2),
+                "values per lane must be a power of two <= 64");
+  float v[V];
+#pragma unroll
+  for (int mr = 0; mr < NMAT * R; ++mr)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      v[mr * NT + tt] = acc[mr * TC + tt];
+      acc[mr * TC + tt] = 0.0f;
+    }
+  Halve<V>::run(v, lane, 32);
   if (NMAT == 2) {
-    const float v = __shfl_xor(acc[0], 32);  // the up value pairs with this gate value
-    if (lane < 32 && (lane & ((1 << C::SH) - 1)) == 0) {
-      const int idx = lane >> C::SH;
-      const int r = idx / TC, tt = idx - (idx / TC) * TC;
+    const float u = __shfl_xor(v[0], 32);  // the up value pairs with this gate value
+    if (lane < 32 && (lane & ((1 << SH) - 1)) == 0) {
+      const int idx = lane >> SH;
+      const int r = idx / NT, tt = idx - (idx / NT) * NT;
       if (r < rv && tt < nt) {
-        const float a = acc[0];
-        const float h = a / (1.0f + expf(-a)) * v;
+        const float a = v[0];
+        const float h = a / (1.0f + expf(-a)) * u;
         const size_t off = static_cast<size_t>(tok_h[tt]) * rows + r0 + r;
         if (COH) {
           coh_store(reinterpret_cast<float*>(p.H) + off, h);
@@ -552,20 +643,168 @@ __device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int urel
       }
     }
   } else {
-    if ((lane & ((1 << C::SH) - 1)) == 0) {
-      const int idx = lane >> C::SH;
-      const int r = idx / TC, tt = idx - (idx / TC) * TC;
+    if ((lane & ((1 << SH) - 1)) == 0) {
+      const int idx = lane >> SH;
+      const int r = idx / NT, tt = idx - (idx / NT) * NT;
       if (r < rv && tt < nt) {
         if (COH) {
-          coh_store(tok_y[tt] + r0 + r, acc[0]);
+          coh_store(tok_y[tt] + r0 + r, v[0]);
         } else {
-          tok_y[tt][r0 + r] = acc[0];
+          tok_y[tt][r0 + r] = v[0];
         }
       }
     }
   }
+}
+
+// ------------------------------------------------- matrix-core products
+// v_mfma_f32_4x4x4_16b_bf16 computes 16 independent 4x4x4 block products:
+// lane 4b + q holds row q of block b's A (4 K elements), column q of its B
+// (token q, the same 4 K elements) and column q of its D (row i in register
+// i; layout checked on the device with one-hot operands).  Here block b
+// of step s is K range [s*STEP + b*VEC, +VEC) of the four rows: every block
+// sums part of the same dot products, and the 16 partial blocks are added
+// across lanes once per unit (finish_unit_mf).  Token group g (tokens 4g..4g+3)
+// has its own D; the tokens come from LDS as bf16.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 as_s16x4(unsigned lo, unsigned hi) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v;
+  v.x = lo;
+  v.y = hi;
+  return __builtin_bit_cast(s16x4, v);
+}
+__device__ __forceinline__ f32x4 mfma4(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int WT, int TC, int R, int NMAT, int SPC>
+__device__ __forceinline__ void mul_chunk_mf(int kc, int Kpad, int lane, const uint8_t* xs,
+                                             const u32x4 (&buf)[NMAT][SPC][1],
+                                             const float (&sc)[NMAT][SPC], float* acc) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  using T = typename C::T;
+  constexpr int TG = TC / 4;
+  const int q = lane & 3, b = lane >> 2;
 #pragma unroll
-  for (int i = 0; i < C::V; ++i) acc[i] = 0.0f;
+  for (int s = 0; s < SPC; ++s) {
+    const int k = kc * C::CH + s * C::STEP + b * T::VEC;
+    // token 4g + q, elements [k, k + VEC): 16 bytes per 8 elements
+    u32x4 xf[TG][T::VEC / 8];
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+      for (int h = 0; h < T::VEC / 8; ++h)
+        xf[g][h] = ld16(xs + (static_cast<size_t>(4 * g + q) * Kpad + k + 8 * h) * 2);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const u32x4 w = buf[m][s][0];
+      if constexpr (WT == WT_BF16) {
+        const s16x4 a0 = as_s16x4(w.x, w.y), a1 = as_s16x4(w.z, w.w);
+#pragma unroll
+        for (int g = 0; g < TG; ++g) {
+          f32x4 d = {acc[(m * TG + g) * 4 + 0], acc[(m * TG + g) * 4 + 1],
+                     acc[(m * TG + g) * 4 + 2], acc[(m * TG + g) * 4 + 3]};
+          d = mfma4(a0, as_s16x4(xf[g][0].x, xf[g][0].y), d);
+          d = mfma4(a1, as_s16x4(xf[g][0].z, xf[g][0].w), d);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[(m * TG + g) * 4 + r] = d[r];
+        }
+      } else {
+        // 16 E4M3FN codes -> bf16 exactly; the block scale of the lane's K
+        // range multiplies the block products of this step
+        const unsigned wd[4] = {w.x, w.y, w.z, w.w};
+        s16x4 a[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          a[h] = as_s16x4(__builtin_bit_cast(unsigned, fp8x2_to_bf16x2<false>(wd[h])),
+                          __builtin_bit_cast(unsigned, fp8x2_to_bf16x2<true>(wd[h])));
+#pragma unroll
+        for (int g = 0; g < TG; ++g) {
+          f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+          t = mfma4(a[0], as_s16x4(xf[g][0].x, xf[g][0].y), t);
+          t = mfma4(a[1], as_s16x4(xf[g][0].z, xf[g][0].w), t);
+          t = mfma4(a[2], as_s16x4(xf[g][1].x, xf[g][1].y), t);
+          t = mfma4(a[3], as_s16x4(xf[g][1].z, xf[g][1].w), t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[(m * TG + g) * 4 + r] = fmaf(sc[m][s], t[r], acc[(m * TG + g) * 4 + r]);
+        }
+      }
+    }
+  }
+}
+
+// End of a matrix-core unit: add the 16 block products of every (matrix,
+// token group) across lanes (bits 5 and 4 by halving, then bits 3 and 2), so
+// lane l with bits 2 and 3 clear holds row 2*bit5 + bit4, token l & 3; the
+// gate and up sums of one (row, token) land in the same lane.
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
+__device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int r0, int rv, int rows,
+                                               int lane, const int* tok_h, float* const* tok_y,
+                                               float* acc) {
+  constexpr int TG = TC / 4;
+  const bool h5 = (lane & 32) != 0, h4 = (lane & 16) != 0;
+  float res[NMAT][TG];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      float* d = acc + (m * TG + g) * 4;
+      float k0 = h5 ? d[2] : d[0], k1 = h5 ? d[3] : d[1];
+      const float s0 = h5 ? d[0] : d[2], s1 = h5 ? d[1] : d[3];
+      k0 += __shfl_xor(s0, 32);
+      k1 += __shfl_xor(s1, 32);
+      float v = h4 ? k1 : k0;
+      v += __shfl_xor(h4 ? k0 : k1, 16);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 4);
+      res[m][g] = v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[r] = 0.0f;
+    }
+  if ((lane & 12) != 0) return;
+  const int r = (h5 ? 2 : 0) + (h4 ? 1 : 0), q = lane & 3;
+  if (r >= rv) return;
+#pragma unroll
+  for (int g = 0; g < TG; ++g) {
+    const int tt = 4 * g + q;
+    if (tt >= nt) continue;
+    if (NMAT == 2) {
+      const float a = res[0][g];
+      const float h = a / (1.0f + expf(-a)) * res[NMAT - 1][g];
+      const size_t off = static_cast<size_t>(tok_h[tt]) * rows + r0 + r;
+      if (COH) {
+        coh_store(reinterpret_cast<float*>(p.H) + off, h);
+      } else {
+        reinterpret_cast<uint16_t*>(p.H)[off] = f32_to_bf16_bits(h);
+      }
+    } else {
+      if (COH) {
+        coh_store(tok_y[tt] + r0 + r, res[0][g]);
+      } else {
+        tok_y[tt][r0 + r] = res[0][g];
+      }
+    }
+  }
+}
+
+// Multiply one chunk, and end the unit after its last chunk: on the matrix
+// cores for token tiles of four or more (bf16, fp8), else as dot products.
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
+__device__ __forceinline__ void mul_finish(int nt, bool last, int kc, int Kpad, int lane,
+                                           const uint8_t* xs,
+                                           const u32x4 (&buf)[NMAT][SPC][StreamCfg<WT, TC, R, NMAT, SPC>::LR],
+                                           const float (&sc)[NMAT][SPC], float* acc,
+                                           const FfnParams& p, int r0, int rv, int rows,
+                                           const int* tok_h, float* const* tok_y) {
+  if constexpr (StreamCfg<WT, TC, R, NMAT, SPC>::MF) {
+    mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, Kpad, lane, xs, buf, sc, acc);
+    if (last) finish_unit_mf<WT, TC, R, NMAT, SPC, COH>(p, nt, r0, rv, rows, lane, tok_h, tok_y, acc);
+  } else {
+    mul_chunk_nt<WT, TC, R, NMAT, SPC, TC>(kc, Kpad, lane, xs, buf, sc, acc);
+    if (last) finish_unit<WT, TC, R, NMAT, SPC, COH, TC>(p, nt, r0, rv, rows, lane, tok_h, tok_y, acc);
+  }
 }
 
 // ------------------------------------------------------------ one range
@@ -578,7 +817,7 @@ __device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int urel
 template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
 __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, int U, long long lo,
                                           long long hi, uint8_t* xs, int* tok_h, float** tok_y,
-                                          const Sync& sy) {
+                                          int* claim, const Sync& sy) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   constexpr bool UP = NMAT == 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -586,13 +825,13 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
   const int Kdim = UP ? p.d : p.f;
   const int nchunks = (Kdim + C::CH - 1) / C::CH;
   const int Kpad = nchunks * C::CH;
-  const int upg = (rows + (kBlock / kWave) * R - 1) / ((kBlock / kWave) * R);
+  const int upg = units_per_group(rows, R);
 
-  u32x4 b0[NMAT][SPC][R], b1[NMAT][SPC][R];
+  u32x4 b0[NMAT][SPC][C::LR], b1[NMAT][SPC][C::LR];
   float s0[NMAT][SPC], s1[NMAT][SPC];
-  float acc[C::V];
+  float acc[C::NACC];
 #pragma unroll
-  for (int i = 0; i < C::V; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < C::NACC; ++i) acc[i] = 0.0f;
 
   // Fast path: the range touches at most two groups, each within one token
   // tile, and LDS has two token slots: stage both up front, then stream with
@@ -612,12 +851,33 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
     const int v0 = G0.shared || (G0.e >= 0 && G0.e < p.E);
     const int v1 = G1.shared || (G1.e >= 0 && G1.e < p.E);
     if (UP && threadIdx.x == 0 && (!v0 || !v1)) atomicOr(p.err, ERRBIT_BAD_IDS);
-    const int base0 = g0 * upg;
-    const int nct = static_cast<int>(hi - lo) * nchunks;  // chunks of this range
+    const int nur = static_cast<int>(hi - lo);  // units of the range, in order
+    const long long g1lo = static_cast<long long>(g0 + 1) * upg;  // first unit of g1
     const size_t slot_bytes = static_cast<size_t>(TC) * Kpad * C::T::XB;
     uint8_t* xs1 = xs + (g1 != g0 ? slot_bytes : 0);
-    load_chunk<WT, TC, R, NMAT, SPC>(p, G0, v0, static_cast<int>(lo) - base0, 0, rows, Kdim, lane,
-                                     wave, b0, s0);
+    // Units are handed out dynamically: wavefront w starts with unit w and
+    // then takes the next unclaimed unit from the workgroup's LDS counter, so
+    // the wavefronts of the CU finish together however the hardware shares
+    // the memory pipeline among them.  Unit u: its group (0: g0, 1: g1), its
+    // first row r0 in that group and its valid rows rv (0 beyond the range).
+    auto unit_info = [&](int u, int& sg, int& r0, int& rv) {
+      const long long gu = lo + u;
+      sg = gu >= g1lo;
+      r0 = static_cast<int>(gu - (sg ? g1lo : g1lo - upg)) * R;
+      rv = u < nur ? min(R, rows - r0) : 0;
+    };
+    auto take = [&]() {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(claim, 1);
+      return uni(v);
+    };
+    int u = wave, kc = 0;
+    {
+      int sg, r0, rv;
+      unit_info(u, sg, r0, rv);
+      load_chunk<WT, TC, R, NMAT, SPC>(p, sg ? G1 : G0, r0, (sg ? v1 : v0) ? rv : 0, 0, rows,
+                                       Kdim, lane, b0, s0);
+    }
     if (COH && !UP) {
       wait_group_ready(sy, g0);
       if (g1 != g0) wait_group_ready(sy, g1);
@@ -632,42 +892,55 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
         stage_tokens<WT, TC, !UP, COH>(p, mt, w, Kdim, Kpad, xs1, tok_h + TC, tok_y + TC);
       }
     }
+    if (threadIdx.x == 0) *claim = static_cast<int>(blockDim.x) >> 6;
     __syncthreads();
-    // chunk c: unit lo + c / nchunks, K chunk c % nchunks.  One step
-    // prefetches chunk cc + 1 into one buffer and multiplies chunk cc from
-    // the other.  The loop runs whole pairs of steps, so on every path back
-    // to its head the only loads in flight are the prefetch of the next
-    // chunk (a half-finished pair would leave a buffer that the head
-    // overwrites in flight, and the compiler would wait for every load there).
-    auto step = [&](int cc, u32x4 (&bl)[NMAT][SPC][R], float (&sl)[NMAT][SPC],
-                    const u32x4 (&bm)[NMAT][SPC][R], const float (&sm)[NMAT][SPC],
-                    bool prefetch) {
-      if (prefetch) {
-        const int un = static_cast<int>(lo) + (cc + 1) / nchunks;  // unit of the next chunk
-        const int kn = (cc + 1) - ((cc + 1) / nchunks) * nchunks;
-        const int sn = un - base0 >= upg;  // next chunk in the second group
-        load_chunk<WT, TC, R, NMAT, SPC>(p, sn ? G1 : G0, (cc + 1 < nct) && (sn ? v1 : v0),
-                                         un - base0 - (sn ? upg : 0), kn, rows, Kdim, lane, wave,
-                                         bl, sl);
+    // One half-step prefetches chunk (un, kn) into one buffer and multiplies
+    // chunk (u, kc) from the other.  The loop runs whole pairs of half-steps,
+    // so on every path back to its head the only loads in flight are the
+    // prefetch of the next chunk (a half-finished pair would leave a buffer
+    // that the head overwrites in flight, and the compiler would wait for
+    // every load there).
+    auto half = [&](int uc, int kcc, int un, int kn, u32x4 (&bl)[NMAT][SPC][C::LR],
+                    float (&sl)[NMAT][SPC], const u32x4 (&bm)[NMAT][SPC][C::LR],
+                    const float (&sm)[NMAT][SPC]) {
+      {
+        int sg, r0, rv;
+        unit_info(un, sg, r0, rv);
+        load_chunk<WT, TC, R, NMAT, SPC>(p, sg ? G1 : G0, r0, (sg ? v1 : v0) ? rv : 0, kn, rows,
+                                         Kdim, lane, bl, sl);
 #ifdef MOE_TUNE_SCHED
         __builtin_amdgcn_sched_barrier(0);
 #endif
       }
-      const int uc = static_cast<int>(lo) + cc / nchunks;
-      const int kcc = cc - (cc / nchunks) * nchunks;
-      const int sc_ = uc - base0 >= upg;
-      mul_chunk<WT, TC, R, NMAT, SPC>(kcc, Kpad, lane, sc_ ? xs1 : xs, bm, sm, acc);
-      if (kcc == nchunks - 1)
-        finish_unit<WT, TC, R, NMAT, SPC, COH>(p, sc_ ? G1.cnt : G0.cnt, uc - base0 - (sc_ ? upg : 0),
-                                          rows, lane, wave, tok_h + (sc_ ? TC : 0),
-                                          tok_y + (sc_ ? TC : 0), acc);
+      int sg, r0, rv;
+      unit_info(uc, sg, r0, rv);
+      mul_finish<WT, TC, R, NMAT, SPC, COH>(sg ? G1.cnt : G0.cnt, kcc == nchunks - 1, kcc, Kpad,
+                                            lane, sg ? xs1 : xs, bm, sm, acc, p, r0, rv, rows,
+                                            tok_h + (sg ? TC : 0), tok_y + (sg ? TC : 0));
     };
-    int c = 0;
-    for (; c + 2 <= nct; c += 2) {
-      step(c, b1, s1, b0, s0, true);
-      step(c + 1, b0, s0, b1, s1, true);
+    int un = u, kn = kc + 1;
+    if (kn == nchunks) {
+      kn = 0;
+      un = take();
     }
-    if (c < nct) step(c, b1, s1, b0, s0, false);  // odd count: the last chunk is in b0
+    while (true) {
+      half(u, kc, un, kn, b1, s1, b0, s0);
+      if (un >= nur) break;
+      u = un;
+      kc = kn;
+      if (++kn == nchunks) {
+        kn = 0;
+        un = take();
+      }
+      half(u, kc, un, kn, b0, s0, b1, s1);
+      if (un >= nur) break;
+      u = un;
+      kc = kn;
+      if (++kn == nchunks) {
+        kn = 0;
+        un = take();
+      }
+    }
     return;
   }
 
@@ -677,8 +950,10 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
   walk_group<TC>(p, mt, U, cur, g0, lo, hi, upg);
   if (UP && !cur.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
 
-  load_chunk<WT, TC, R, NMAT, SPC>(p, cur.G, cur.valid, cur.u - cur.g * upg, cur.kc, rows, Kdim,
-                                   lane, wave, b0, s0);
+  int r0, rv;
+  wave_unit<R>(cur.ua, cur.ub, cur.s, wave, rows, r0, rv);
+  load_chunk<WT, TC, R, NMAT, SPC>(p, cur.G, r0, cur.valid ? rv : 0, cur.kc, rows, Kdim, lane, b0,
+                                   s0);
   if (COH && !UP) wait_group_ready(sy, g0);
   stage_tokens<WT, TC, !UP, COH>(p, mt, cur, Kdim, Kpad, xs, tok_h, tok_y);
   __syncthreads();
@@ -687,12 +962,14 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
   walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
   // two chunks per trip so the register buffers keep fixed names
   while (true) {
-    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, nxt.valid && !nxt.done, nxt.u - nxt.g * upg, nxt.kc,
-                                     rows, Kdim, lane, wave, b1, s1);
-    mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b0, s0, acc);
-    if (cur.kc == nchunks - 1)
-      finish_unit<WT, TC, R, NMAT, SPC, COH>(p, min(TC, cur.G.cnt - cur.tile * TC), cur.u - cur.g * upg,
-                                        rows, lane, wave, tok_h, tok_y, acc);
+    int n0, nv;
+    wave_unit<R>(nxt.ua, nxt.ub, nxt.s, wave, rows, n0, nv);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, n0, (nxt.valid && !nxt.done) ? nv : 0, nxt.kc, rows,
+                                     Kdim, lane, b1, s1);
+    wave_unit<R>(cur.ua, cur.ub, cur.s, wave, rows, r0, rv);
+    mul_finish<WT, TC, R, NMAT, SPC, COH>(min(TC, cur.G.cnt - cur.tile * TC), cur.kc == nchunks - 1,
+                                          cur.kc, Kpad, lane, xs, b0, s0, acc, p, r0, rv, rows,
+                                          tok_h, tok_y);
     if (nxt.done) break;
     if (nxt.g != cur.g || nxt.tile != cur.tile) {
       if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
@@ -704,12 +981,13 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
     cur = nxt;
     walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
 
-    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, nxt.valid && !nxt.done, nxt.u - nxt.g * upg, nxt.kc,
-                                     rows, Kdim, lane, wave, b0, s0);
-    mul_chunk<WT, TC, R, NMAT, SPC>(cur.kc, Kpad, lane, xs, b1, s1, acc);
-    if (cur.kc == nchunks - 1)
-      finish_unit<WT, TC, R, NMAT, SPC, COH>(p, min(TC, cur.G.cnt - cur.tile * TC), cur.u - cur.g * upg,
-                                        rows, lane, wave, tok_h, tok_y, acc);
+    wave_unit<R>(nxt.ua, nxt.ub, nxt.s, wave, rows, n0, nv);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, nxt.G, n0, (nxt.valid && !nxt.done) ? nv : 0, nxt.kc, rows,
+                                     Kdim, lane, b0, s0);
+    wave_unit<R>(cur.ua, cur.ub, cur.s, wave, rows, r0, rv);
+    mul_finish<WT, TC, R, NMAT, SPC, COH>(min(TC, cur.G.cnt - cur.tile * TC), cur.kc == nchunks - 1,
+                                          cur.kc, Kpad, lane, xs, b1, s1, acc, p, r0, rv, rows,
+                                          tok_h, tok_y);
     if (nxt.done) break;
     if (nxt.g != cur.g || nxt.tile != cur.tile) {
       if (UP && nxt.g != cur.g && !nxt.valid && threadIdx.x == 0) atomicOr(p.err, ERRBIT_BAD_IDS);
