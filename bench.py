@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cold", action="store_true", help="also time operations after a scrub")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the Qwen3-, DeepSeek-V2-Lite- and DeepSeek-V3-shaped points")
     ap.add_argument("--profile-step", action="store_true",
                     help="replay only the one-launch step graph (for a kernel trace whose "
                          "per-template averages are the deduplicating launches at n=1,2,4,8)")
@@ -108,6 +110,89 @@ def cpu_baseline(cfg, p, budget_s):
             "sample": "float64 numpy oracle, dedup mode, one OLMoE-shaped layer, Markov p=%s: "
                       "the operations at n=1,2,4,8 (route+union+FFN+combine incl. weight "
                       "decode), %d rounds, %.1f s on one thread" % (p, rounds, total_s)}
+
+
+def shape_sweep(dev, reps=10):
+    """The one-launch pass on the other layer shapes, deduplicating and per-slot:
+    Qwen3-30B-A3B (router logits from AR(1) tokens), DeepSeek-V2-Lite (two shared
+    experts, Markov p = 0.5, a 16-node draft tree) and DeepSeek-V3 (fp8 weights with
+    128x128 block scales; independent and Markov routing, a 32-node tree).  Each point
+    replays a graph of one pass per layer (layers alternate, so no pass finds its
+    experts in the Infinity Cache); GB/s on union bytes (dedup) and on requested
+    bytes (per-slot)."""
+    import torch
+
+    from moe_speculative_decoding_amd import _lib as L
+    from moe_speculative_decoding_amd.layer import DeviceLayer, VerifyBuffers, to_device, verify_layer
+    from synth import make_case
+    from synth.configs import DSV2LITE, DSV3, QWEN3
+    from synth.gen import device_layer_weights
+
+    stream = torch.cuda.current_stream()
+    plan = ((QWEN3, 4, (("logits_ar1", 1, False), ("logits_ar1", 8, False))),
+            (DSV2LITE, 4, (("markov:0.5", 1, False), ("markov:0.5", 8, False),
+                           ("markov:0.5", 16, True))),
+            (DSV3, 2, (("iid", 1, False), ("iid", 8, False), ("markov:0.5", 8, False),
+                       ("markov:0.5", 32, True))))
+    out = {}
+    for cfg, nl, points in plan:
+        layers = []
+        for l in range(nl):
+            w = device_layer_weights(cfg, seed=0, layer=l, device=dev)
+            sh = device_layer_weights(cfg, seed=0, layer=l, device=dev, shared=True) if cfg.S else None
+            layers.append(DeviceLayer(cfg.E, cfg.K, cfg.d, cfg.f, cfg.S, cfg.w_dtype, cfg.x_dtype,
+                                      w, sh))
+        for routing, n, tree in points:
+            ops = []
+            for l in range(nl):
+                case = make_case(cfg, n, routing, seed=0, window=l, layer=l, tree=tree)
+                ops.append((l, to_device(case.x, dev), to_device(case.logits, dev),
+                            VerifyBuffers(layers[l], n, dev)))
+            rec = {}
+            for mode, name in ((L.MOE_MODE_DEDUP, "dedup"), (L.MOE_MODE_PERSLOT, "perslot")):
+                for (l, x, lg, b) in ops:
+                    verify_layer(layers[l], b, x, lg, n, mode)
+                torch.cuda.synchronize()
+                for (_, _, _, b) in ops:
+                    if L.moe_get_error(b.ws) != L.MOE_OK:
+                        raise RuntimeError("device error word set (%s n=%d)" % (cfg.name, n))
+                byt = [b.bytes.cpu().tolist() for (_, _, _, b) in ops]
+                g = torch.cuda.CUDAGraph()
+                st = torch.cuda.Stream()
+                st.wait_stream(stream)
+                with torch.cuda.stream(st):
+                    with torch.cuda.graph(g, stream=st):
+                        for (l, x, lg, b) in ops:
+                            verify_layer(layers[l], b, x, lg, n, mode)
+                stream.wait_stream(st)
+                torch.cuda.synchronize()
+                g.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) * 1e-3 / (reps * nl)
+                del g
+                bytes_ = sum(b[0] for b in byt) / len(byt)
+                rec[name] = (t, bytes_)
+                if mode == L.MOE_MODE_DEDUP:
+                    rec["U"] = sum(int(b.U.item()) for (_, _, _, b) in ops) / len(ops)
+                    rec["requested"] = sum(b[1] for b in byt) / len(byt)
+            (td, ub), (ts, rb) = rec["dedup"], rec["perslot"]
+            key = "%s %s n=%d%s" % (cfg.name, routing, n, " tree" if tree else "")
+            out[key] = {"U_mean": round(rec["U"], 2), "u": round(ub / rec["requested"], 4),
+                        "union_MB": round(ub / 1e6, 1), "us_dedup": round(1e6 * td, 2),
+                        "GBs_dedup_union": round(ub / td / 1e9, 1),
+                        "pct_peak_dedup": round(100 * ub / td / 1e9 / PEAK_GBS, 1),
+                        "us_perslot": round(1e6 * ts, 2),
+                        "GBs_perslot_requested": round(rb / ts / 1e9, 1)}
+            log("shape %s: %s" % (key, json.dumps(out[key])))
+            del ops
+        del layers
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -186,7 +271,10 @@ def main():
         if full:
             slot = op["buf_slot"].out[:op["n"]]
             rel = float((slot - op["out_eager"]).norm() / op["out_eager"].norm())
-            if not rel < 1e-5:
+            # the two modes sum in different orders (matrix-core blocks vs dot
+            # products), so h can round to a neighbouring bf16 value in one mode:
+            # a few elements differ by ~2^-8 relative, far inside the 1e-2 bound
+            if not rel < 1e-3:
                 raise RuntimeError("dedup and per-slot outputs differ (rel %.2e)" % rel)
     step_union_bytes = sum(op["union_bytes"] for op in ops)
 
@@ -470,6 +558,8 @@ def main():
                 cold.setdefault("n=%d" % n, {})[name] = round(float(np.median(v)), 2)
         log("cold (event-timed, includes ~6 us of dispatch): %s" % json.dumps(cold))
 
+    shapes = None if args.no_shapes else shape_sweep(dev)
+
     cpu = None if args.no_cpu else cpu_baseline(cfg, args.p, args.cpu_seconds)
 
     line = {
@@ -484,6 +574,7 @@ def main():
                    "global_batch": sum(ns) * args.layers, "seq_len": 1, "parallelism": "none"},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fit": fit,
         "dispatch": dispatch, "draft_length": draft, "selection": selection,
+        "shapes": shapes,
     }
     if cold is not None:
         line["cold"] = cold

@@ -96,6 +96,7 @@ struct FfnParams {
   int ucap;               // dedup: upper bound of U = min(n*K, E)
   int mode;
   int lds_slots;          // token slots in LDS (set by the launcher)
+  long long lds_bytes;    // dynamic LDS of the launch (set by the launcher)
 };
 
 // One MoE layer of a verify pass in one launch (fused.hip).
@@ -136,15 +137,18 @@ constexpr int kTuneRU = MOE_TUNE_RU, kTuneSPCU = MOE_TUNE_SPCU;
 constexpr int kTuneRD = MOE_TUNE_RD, kTuneSPCD = MOE_TUNE_SPCD;
 
 // token tile: a group serves at most n tokens (a token names an expert once),
-// so the tile is the next power of two of min(n, 8); larger groups (shared
-// experts of a long pass, trees) take several tiles
+// so the tile is the next power of two of n (up to 32); f32 weights take at
+// most 8 and larger groups take several tiles
 inline int token_tile(int mode, int n) {
   if (mode == MODE_PERSLOT) return 1;
-  return n >= 5 ? 8 : (n >= 3 ? 4 : (n == 2 ? 2 : 1));
+  return n >= 17 ? 32 : (n >= 9 ? 16 : (n >= 5 ? 8 : (n >= 3 ? 4 : (n == 2 ? 2 : 1))));
 }
 
 // resident workgroups of a kernel of `block` threads on the current device
 int resident_blocks(const void* fn, size_t smem, int block);
+// dynamic LDS a launch of fn may take on the current device (the device's
+// per-workgroup LDS less fn's static LDS); 0 if the query fails
+size_t lds_budget(const void* fn);
 
 hipError_t launch_route_topk(const float* logits, int n, int E, int K, int32_t* ids,
                              float* gates, hipStream_t s);

@@ -28,6 +28,7 @@ void ffn_stream_kernel(FfnParams p) {
   __shared__ float* tok_y[2 * TC];
   __shared__ Meta mt;
   __shared__ int claim;
+  __shared__ RangeTab rt;
   const int rows = UP ? p.f : p.d;
   const int upg = units_per_group(rows, R);
 
@@ -61,7 +62,7 @@ void ffn_stream_kernel(FfnParams p) {
 
   load_meta(p, mt);
   __syncthreads();
-  run_range<WT, TC, R, NMAT, SPC, false>(p, mt, U, lo, hi, xs, tok_h, tok_y, &claim, Sync{});
+  run_range<WT, TC, R, NMAT, SPC, false>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, &claim, Sync{});
 }
 
 // ------------------------------------------------------------------ launch
@@ -77,6 +78,28 @@ struct OccKey {
     return dev < o.dev;
   }
 };
+
+size_t lds_budget(const void* fn) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> g(mu);
+  const auto key = std::make_pair(fn, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int lim = 0;
+  hipFuncAttributes fa;
+  if (hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      hipFuncGetAttributes(&fa, fn) != hipSuccess || static_cast<size_t>(lim) <= fa.sharedSizeBytes)
+    return 0;
+  const size_t b = static_cast<size_t>(lim) - fa.sharedSizeBytes;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(b)) !=
+      hipSuccess)
+    return 0;
+  cache[key] = b;
+  return b;
+}
 
 // resident workgroups of a kernel on the whole device (cached per process)
 int resident_blocks(const void* fn, size_t smem, int block) {
@@ -107,18 +130,15 @@ static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
   const int Kdim = UP ? p.d : p.f;
   const int Kpad = (Kdim + C::CH - 1) / C::CH * C::CH;
   const void* fn = reinterpret_cast<const void*>(&ffn_stream_kernel<WT, TC, R, NMAT, SPC, NW>);
+  // One workgroup per CU: the launch takes all the LDS a workgroup may have.
   // A second token slot lets ranges that cross a group boundary take the
-  // fast path; it is used only when it costs no resident workgroups.
+  // slot fast path; the matrix-core kernels stage whole ranges instead.
   const size_t slot = static_cast<size_t>(TC) * Kpad * C::T::XB;
-#ifndef MOE_TUNE_SLOTS
-  const int slots =
-      2 * slot <= 65536 && resident_blocks(fn, 2 * slot, kStreamBlock) >= resident_blocks(fn, slot, kStreamBlock) ? 2 : 1;
-#else
-  const int slots = MOE_TUNE_SLOTS;
-#endif
-  const size_t smem = slots * slot;
+  const size_t smem = lds_budget(fn);
+  if (slot > smem) return hipErrorInvalidConfiguration;
   FfnParams q = p;
-  q.lds_slots = slots;
+  q.lds_slots = 2 * slot <= smem ? 2 : 1;
+  q.lds_bytes = static_cast<long long>(smem);
   const int upg = units_per_group(rows, R);
   const int groups_max = p.mode == MODE_DEDUP ? p.ucap + p.S : p.n * (p.K + p.S);
   const long long units_max = static_cast<long long>(groups_max) * upg;
@@ -148,7 +168,12 @@ static hipError_t launch_typed(const FfnParams& p, hipStream_t s) {
     case 1: return launch_pair<WT, 1>(p, s);
     case 2: return launch_pair<WT, 2>(p, s);
     case 4: return launch_pair<WT, 4>(p, s);
-    default: return launch_pair<WT, 8>(p, s);
+    case 8: return launch_pair<WT, 8>(p, s);
+    default:
+      // f32 weights (dot products) stop at 8 tokens; larger groups take tiles
+      if constexpr (WT == WT_F32) return launch_pair<WT, 8>(p, s);
+      else return token_tile(p.mode, p.n) == 16 ? launch_pair<WT, 16>(p, s)
+                                                : launch_pair<WT, 32>(p, s);
   }
 }
 

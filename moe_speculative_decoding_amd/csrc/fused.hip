@@ -57,8 +57,8 @@ constexpr size_t kRouteLogitsOffset = kRouteTopkOffset + kMaxStreamWaves * sizeo
 // two-kernel FFN's shapes for the same tile, so both run the same arithmetic)
 template <int WT, int TC>
 __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt, int U, int NG,
-                                           uint8_t* xs, int* tok_h, float** tok_y, int* claim,
-                                           unsigned tag) {
+                                           uint8_t* xs, int* tok_h, float** tok_y, RangeTab& rt,
+                                           int* claim, unsigned tag) {
   using Tl = Tiles<WT, TC>;
   const FfnParams& p = lp.f;
   const int upg_u = units_per_group(p.f, Tl::RU);
@@ -70,8 +70,8 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
   {
     const long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
     if (lo < hi)
-      run_range<WT, Tl::TCU, Tl::RU, 2, Tl::SPCU, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, claim,
-                                                         sy);
+      run_range<WT, Tl::TCU, Tl::RU, 2, Tl::SPCU, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt,
+                                                         claim, sy);
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0)
@@ -80,7 +80,8 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
   {
     const long long lo = NUd * b / G, hi = NUd * (b + 1) / G;
     if (lo < hi)
-      run_range<WT, TC, Tl::RD, 1, Tl::SPCD, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, claim, sy);
+      run_range<WT, TC, Tl::RD, 1, Tl::SPCD, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, claim,
+                                                    sy);
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0)
@@ -104,6 +105,7 @@ void layer_kernel(LayerParams lp) {
   __shared__ float gates_l[kMaxSlots];
   __shared__ int U_l;
   __shared__ int claim;  // next unit of the running phase (stream.h)
+  __shared__ RangeTab rt;
   const FfnParams& p = lp.f;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = p.n, K = p.K, E = p.E, S = p.S, nk = n * K;
@@ -112,6 +114,10 @@ void layer_kernel(LayerParams lp) {
   // logits are copied to LDS first (one round trip to memory for all tokens)
   RouteLds& rl = *reinterpret_cast<RouteLds*>(xs);
   float* lg = reinterpret_cast<float*>(xs + kRouteLogitsOffset);
+  // the call's tag (workspace epoch + 1) travels with the logits: it is final
+  // before the launch (the previous call advanced it before it ended)
+  __shared__ unsigned tag_l;
+  if (tid == 0) tag_l = coh_load_u32(lp.epoch) + 1u;
   {
     // eight loads per lane in flight at once (clamped in bounds), then the stores
     constexpr int kPer = 8;
@@ -182,16 +188,13 @@ void layer_kernel(LayerParams lp) {
   __syncthreads();  // the routing scratch in xs is dead from here
 
   // ---- UP range b, then DOWN range b
-  __shared__ unsigned tag_l;
-  if (tid == 0) tag_l = coh_load_u32(lp.epoch) + 1u;
-  __syncthreads();
   const unsigned tag = tag_l;
   const int NG = mode == MODE_DEDUP ? U + S : n * (K + S);
   const int G = gridDim.x, b = blockIdx.x;
   if (AUTO && TC > 1 && mode == MODE_PERSLOT)
-    run_phases<WT, 1>(lp, mt, U, NG, xs, tok_h, tok_y, &claim, tag);
+    run_phases<WT, 1>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag);
   else
-    run_phases<WT, TC>(lp, mt, U, NG, xs, tok_h, tok_y, &claim, tag);
+    run_phases<WT, TC>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag);
 
   // ---- combine: one lane per (token, 4 columns), first workgroups only
   const int quads = p.d / 4;
@@ -278,18 +281,13 @@ static hipError_t launch_layer_t(const LayerParams& lp0, hipStream_t s) {
   const void* fn = reinterpret_cast<const void*>(&layer_kernel<WT, TC, NW, AUTO>);
   size_t slot = slot_bytes<WT, TC>(p);
   if (AUTO) slot = std::max(slot, slot_bytes<WT, 1>(p));
+  // one workgroup per CU: the launch takes all the LDS a workgroup may have
   const size_t floor_bytes = kRouteLogitsOffset + static_cast<size_t>(p.n) * p.E * 4;
-  auto need = [&](int slots) {
-    const size_t b = slots * slot;
-    return b > floor_bytes ? b : floor_bytes;
-  };
-  const int slots = 2 * slot <= 65536 && resident_blocks(fn, need(2), kStreamBlock) >=
-                                              resident_blocks(fn, need(1), kStreamBlock)
-                        ? 2
-                        : 1;
-  const size_t smem = need(slots);
+  const size_t smem = lds_budget(fn);
+  if (slot > smem || floor_bytes > smem) return hipErrorInvalidConfiguration;
   LayerParams lp = lp0;
-  lp.f.lds_slots = slots;
+  lp.f.lds_slots = 2 * slot <= smem ? 2 : 1;
+  lp.f.lds_bytes = static_cast<long long>(smem);
   int grid = resident_blocks(fn, smem, kStreamBlock);
   if (grid <= 0) return hipErrorInvalidConfiguration;
   if (grid > kMaxGrid) grid = kMaxGrid;
@@ -309,7 +307,12 @@ static hipError_t launch_layer_w(const LayerParams& lp, hipStream_t s) {
     case 1: return launch_layer_tc<WT, 1>(lp, s);
     case 2: return launch_layer_tc<WT, 2>(lp, s);
     case 4: return launch_layer_tc<WT, 4>(lp, s);
-    default: return launch_layer_tc<WT, 8>(lp, s);
+    case 8: return launch_layer_tc<WT, 8>(lp, s);
+    default:
+      // f32 weights (dot products) stop at 8 tokens; larger groups take tiles
+      if constexpr (WT == WT_F32) return launch_layer_tc<WT, 8>(lp, s);
+      else return token_tile(lp.f.mode, lp.f.n) == 16 ? launch_layer_tc<WT, 16>(lp, s)
+                                                      : launch_layer_tc<WT, 32>(lp, s);
   }
 }
 

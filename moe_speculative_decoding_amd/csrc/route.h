@@ -169,8 +169,57 @@ struct UnionLds {
   int bad;
 };
 
+// Union of nk <= 64 slots in one wavefront (lane s holds slot s).  Ballots
+// over the eight id bits give every lane the slots with a smaller id (lt)
+// and those with the same id (eq); the sorted union, the exclusive scan of
+// the per-expert counts, the stable permutation and the slot ranks are then
+// population counts of those masks: no LDS round trip and no barrier.
+__device__ __forceinline__ void build_union_wave(const int32_t* ids, int nk, int E, int lane,
+                                                 int32_t* __restrict__ U_out,
+                                                 int32_t* __restrict__ union_ids,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ perm,
+                                                 int32_t* __restrict__ slot_rank) {
+  const int cap = nk < E ? nk : E;
+  const bool act = lane < nk;
+  const int id = act ? ids[lane] : 0;
+  if (__ballot(act && (id < 0 || id >= E))) {
+    if (lane == 0) *U_out = -1;
+    return;
+  }
+  unsigned long long eq = __ballot(act), lt = 0ull;
+#pragma unroll
+  for (int b = 7; b >= 0; --b) {  // ids < 256
+    const bool bit = ((id >> b) & 1) != 0;
+    const unsigned long long ones = __ballot(act && bit);
+    if (bit) {
+      lt |= eq & ~ones;
+      eq &= ones;
+    } else {
+      eq &= ~ones;
+    }
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const bool first = act && (eq & below) == 0ull;
+  const unsigned long long fm = __ballot(first);
+  const int U = __popcll(fm);
+  const int start = __popcll(lt);  // slots with a smaller id
+  if (act) {
+    perm[start + __popcll(eq & below)] = lane;
+    slot_rank[lane] = __popcll(lt & fm);
+  }
+  if (first) {
+    union_ids[__popcll(lt & fm)] = id;
+    offsets[__popcll(lt & fm)] = start;
+  }
+  for (int i = U + lane; i < cap; i += kWave) union_ids[i] = -1;
+  for (int i = U + lane; i <= cap; i += kWave) offsets[i] = nk;
+  if (lane == 0) *U_out = U;
+}
+
 // Every thread of the workgroup calls this (it holds __syncthreads); threads
-// 0..255 do the work.
+// 0..255 do the work.  Up to 64 slots, wavefront 0 alone builds the union
+// (build_union_wave) and the caller's next barrier publishes it.
 __device__ __forceinline__ void build_union_256(const int32_t* ids, int n, int K, int E,
                                                 int32_t* __restrict__ U_out,
                                                 int32_t* __restrict__ union_ids,
@@ -181,6 +230,10 @@ __device__ __forceinline__ void build_union_256(const int32_t* ids, int n, int K
   const bool mine = tid < 256;
   const int nk = n * K;
   const int cap = nk < E ? nk : E;
+  if (nk <= kWave) {
+    if (wave == 0) build_union_wave(ids, nk, E, lane, U_out, union_ids, offsets, perm, slot_rank);
+    return;
+  }
   for (int i = tid; i < 4 * 256; i += blockDim.x) (&sh.wcnt[0][0])[i] = 0;
   if (tid == 0) sh.bad = 0;
   __syncthreads();

@@ -407,12 +407,13 @@ constexpr bool use_mfma(int WT, int TC, int R) {
 
 // Tile shapes shared by the two-kernel FFN and the one-launch pass (both must
 // run the same arithmetic): rows per wavefront R and load steps per chunk SPC
-// of the UP and DOWN phases, and the UP token tile (fp8, d = 7168: at most 4
-// tokens, 56 KB of LDS).  The matrix-core path takes four rows and keeps the
+// of the UP and DOWN phases, and the UP token tile: at most 16 tokens (the
+// gate and up accumulators of 32 would not fit 168 VGPRs), 8 for fp8 (d =
+// 7168: 112 KB of LDS).  The matrix-core path takes four rows and keeps the
 // bytes per chunk of the dot-product path.
 template <int WT, int TC>
 struct Tiles {
-  static constexpr int TCU = (WT == WT_FP8 && TC > 4) ? 4 : TC;
+  static constexpr int TCU = (WT == WT_FP8 && TC > 8) ? 8 : (TC > 16 ? 16 : TC);
   static constexpr int RU0 = WT == WT_FP8 ? 4 : kTuneRU;
   static constexpr int SPCU0 = WT == WT_FP8 ? 1 : kTuneSPCU;
   static constexpr int RD0 = kTuneRD;
@@ -678,57 +679,52 @@ __device__ __forceinline__ f32x4 mfma4(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Token rows of the B operand: lane 4b + q of token group g reads the staged
+// row at byte offset boff[g] (token 4g + q of the unit's group); only the
+// first tga groups hold tokens (tga is the same in every lane).
 template <int WT, int TC, int R, int NMAT, int SPC>
-__device__ __forceinline__ void mul_chunk_mf(int kc, int Kpad, int lane, const uint8_t* xs,
+__device__ __forceinline__ void mul_chunk_mf(int kc, int lane, const uint8_t* xs,
+                                             const int (&boff)[TC / 4], int tga,
                                              const u32x4 (&buf)[NMAT][SPC][1],
                                              const float (&sc)[NMAT][SPC], float* acc) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   using T = typename C::T;
   constexpr int TG = TC / 4;
-  const int q = lane & 3, b = lane >> 2;
+  const int b = lane >> 2;
 #pragma unroll
   for (int s = 0; s < SPC; ++s) {
     const int k = kc * C::CH + s * C::STEP + b * T::VEC;
-    // token 4g + q, elements [k, k + VEC): 16 bytes per 8 elements
-    u32x4 xf[TG][T::VEC / 8];
 #pragma unroll
-    for (int g = 0; g < TG; ++g)
+    for (int g = 0; g < TG; ++g) {
+      if (g > 0 && g >= tga) break;  // uniform: the unit's tokens end here
+      // token 4g + q, elements [k, k + VEC): 16 bytes per 8 elements
+      u32x4 xf[T::VEC / 8];
 #pragma unroll
-      for (int h = 0; h < T::VEC / 8; ++h)
-        xf[g][h] = ld16(xs + (static_cast<size_t>(4 * g + q) * Kpad + k + 8 * h) * 2);
+      for (int h = 0; h < T::VEC / 8; ++h) xf[h] = ld16(xs + boff[g] + (k + 8 * h) * 2);
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      const u32x4 w = buf[m][s][0];
-      if constexpr (WT == WT_BF16) {
-        const s16x4 a0 = as_s16x4(w.x, w.y), a1 = as_s16x4(w.z, w.w);
+      for (int m = 0; m < NMAT; ++m) {
+        const u32x4 w = buf[m][s][0];
+        float* d4 = acc + (m * TG + g) * 4;
+        if constexpr (WT == WT_BF16) {
+          f32x4 d = {d4[0], d4[1], d4[2], d4[3]};
+          d = mfma4(as_s16x4(w.x, w.y), as_s16x4(xf[0].x, xf[0].y), d);
+          d = mfma4(as_s16x4(w.z, w.w), as_s16x4(xf[0].z, xf[0].w), d);
 #pragma unroll
-        for (int g = 0; g < TG; ++g) {
-          f32x4 d = {acc[(m * TG + g) * 4 + 0], acc[(m * TG + g) * 4 + 1],
-                     acc[(m * TG + g) * 4 + 2], acc[(m * TG + g) * 4 + 3]};
-          d = mfma4(a0, as_s16x4(xf[g][0].x, xf[g][0].y), d);
-          d = mfma4(a1, as_s16x4(xf[g][0].z, xf[g][0].w), d);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[(m * TG + g) * 4 + r] = d[r];
-        }
-      } else {
-        // 16 E4M3FN codes -> bf16 exactly; the block scale of the lane's K
-        // range multiplies the block products of this step
-        const unsigned wd[4] = {w.x, w.y, w.z, w.w};
-        s16x4 a[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          a[h] = as_s16x4(__builtin_bit_cast(unsigned, fp8x2_to_bf16x2<false>(wd[h])),
-                          __builtin_bit_cast(unsigned, fp8x2_to_bf16x2<true>(wd[h])));
-#pragma unroll
-        for (int g = 0; g < TG; ++g) {
+          for (int r = 0; r < 4; ++r) d4[r] = d[r];
+        } else {
+          // 16 E4M3FN codes -> bf16 exactly; the block scale of the lane's K
+          // range multiplies the block products of this step
+          const unsigned wd[4] = {w.x, w.y, w.z, w.w};
           f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
-          t = mfma4(a[0], as_s16x4(xf[g][0].x, xf[g][0].y), t);
-          t = mfma4(a[1], as_s16x4(xf[g][0].z, xf[g][0].w), t);
-          t = mfma4(a[2], as_s16x4(xf[g][1].x, xf[g][1].y), t);
-          t = mfma4(a[3], as_s16x4(xf[g][1].z, xf[g][1].w), t);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[(m * TG + g) * 4 + r] = fmaf(sc[m][s], t[r], acc[(m * TG + g) * 4 + r]);
+          for (int h = 0; h < 4; ++h) {
+            const s16x4 a = as_s16x4(__builtin_bit_cast(unsigned, fp8x2_to_bf16x2<false>(wd[h])),
+                                     __builtin_bit_cast(unsigned, fp8x2_to_bf16x2<true>(wd[h])));
+            const u32x4 xv = xf[h >> 1];
+            t = mfma4(a, (h & 1) ? as_s16x4(xv.z, xv.w) : as_s16x4(xv.x, xv.y), t);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d4[r] = fmaf(sc[m][s], t[r], d4[r]);
         }
       }
     }
@@ -738,18 +734,20 @@ __device__ __forceinline__ void mul_chunk_mf(int kc, int Kpad, int lane, const u
 // End of a matrix-core unit: add the 16 block products of every (matrix,
 // token group) across lanes (bits 5 and 4 by halving, then bits 3 and 2), so
 // lane l with bits 2 and 3 clear holds row 2*bit5 + bit4, token l & 3; the
-// gate and up sums of one (row, token) land in the same lane.
+// gate and up sums of one (row, token) land in the same lane.  Token t of the
+// unit's group (t < nt) writes H row hrows[t] (UP) or output row yrows[t].
 template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
-__device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int r0, int rv, int rows,
-                                               int lane, const int* tok_h, float* const* tok_y,
-                                               float* acc) {
+__device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int tga, int r0, int rv,
+                                               int rows, int lane, const int* hrows,
+                                               float* const* yrows, float* acc) {
   constexpr int TG = TC / 4;
   const bool h5 = (lane & 32) != 0, h4 = (lane & 16) != 0;
   float res[NMAT][TG];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+  for (int g = 0; g < TG; ++g) {
+    if (g > 0 && g >= tga) break;
 #pragma unroll
-    for (int g = 0; g < TG; ++g) {
+    for (int m = 0; m < NMAT; ++m) {
       float* d = acc + (m * TG + g) * 4;
       float k0 = h5 ? d[2] : d[0], k1 = h5 ? d[3] : d[1];
       const float s0 = h5 ? d[0] : d[2], s1 = h5 ? d[1] : d[3];
@@ -763,17 +761,19 @@ __device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int r
 #pragma unroll
       for (int r = 0; r < 4; ++r) d[r] = 0.0f;
     }
+  }
   if ((lane & 12) != 0) return;
   const int r = (h5 ? 2 : 0) + (h4 ? 1 : 0), q = lane & 3;
   if (r >= rv) return;
 #pragma unroll
   for (int g = 0; g < TG; ++g) {
+    if (g > 0 && g >= tga) break;
     const int tt = 4 * g + q;
     if (tt >= nt) continue;
     if (NMAT == 2) {
       const float a = res[0][g];
       const float h = a / (1.0f + expf(-a)) * res[NMAT - 1][g];
-      const size_t off = static_cast<size_t>(tok_h[tt]) * rows + r0 + r;
+      const size_t off = static_cast<size_t>(hrows[tt]) * rows + r0 + r;
       if (COH) {
         coh_store(reinterpret_cast<float*>(p.H) + off, h);
       } else {
@@ -781,9 +781,9 @@ __device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int r
       }
     } else {
       if (COH) {
-        coh_store(tok_y[tt] + r0 + r, res[0][g]);
+        coh_store(yrows[tt] + r0 + r, res[0][g]);
       } else {
-        tok_y[tt][r0 + r] = res[0][g];
+        yrows[tt][r0 + r] = res[0][g];
       }
     }
   }
@@ -799,12 +799,227 @@ __device__ __forceinline__ void mul_finish(int nt, bool last, int kc, int Kpad, 
                                            const FfnParams& p, int r0, int rv, int rows,
                                            const int* tok_h, float* const* tok_y) {
   if constexpr (StreamCfg<WT, TC, R, NMAT, SPC>::MF) {
-    mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, Kpad, lane, xs, buf, sc, acc);
-    if (last) finish_unit_mf<WT, TC, R, NMAT, SPC, COH>(p, nt, r0, rv, rows, lane, tok_h, tok_y, acc);
+    // tokens staged as one tile [TC][Kpad]: token 4g + q in row 4g + q
+    int boff[TC / 4];
+#pragma unroll
+    for (int g = 0; g < TC / 4; ++g) boff[g] = (4 * g + (lane & 3)) * Kpad * 2;
+    mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, lane, xs, boff, TC / 4, buf, sc, acc);
+    if (last)
+      finish_unit_mf<WT, TC, R, NMAT, SPC, COH>(p, nt, TC / 4, r0, rv, rows, lane, tok_h, tok_y,
+                                                acc);
   } else {
     mul_chunk_nt<WT, TC, R, NMAT, SPC, TC>(kc, Kpad, lane, xs, buf, sc, acc);
     if (last) finish_unit<WT, TC, R, NMAT, SPC, COH, TC>(p, nt, r0, rv, rows, lane, tok_h, tok_y, acc);
   }
+}
+
+// ------------------------------------------------ matrix-core range table
+// The matrix-core kernels stage the tokens of a whole range once, packed
+// group after group: the token vectors of each group (UP, rows of x) or its
+// H rows (DOWN).  A unit of group j then multiplies only that group's rows
+// of the table (ceil(cnt/4) token groups), so a group of up to TC tokens
+// streams its expert once and the range needs no restaging between groups.
+constexpr int kRangeGroups = 8;  // groups one range may touch on this path
+struct RangeTab {
+  int ustart[kRangeGroups + 1];  // first unit of group j, relative to the range
+  int cnt[kRangeGroups];         // tokens of group j
+  int row0[kRangeGroups];        // first row of group j in the staged table
+  int xrow[kRangeGroups][32];    // row of x of token t of group j
+  int hrow[kRangeGroups][32];    // H row of token t of group j
+  float* yrow[kRangeGroups][32]; // output row of token t of group j
+};
+
+// Streams units [lo, hi) on the matrix cores from a range table; false (and
+// nothing done) when the range does not fit it: more than kRangeGroups
+// groups, a group of more than TC tokens, or a table larger than the LDS.
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
+__device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt, int U, long long lo,
+                                             long long hi, uint8_t* xs, RangeTab& rt, int* claim,
+                                             const Sync& sy) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  static_assert(C::MF, "matrix-core tiles only");
+  constexpr bool UP = NMAT == 2;
+  constexpr int TG = TC / 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = UP ? p.f : p.d;
+  const int Kdim = UP ? p.d : p.f;
+  const int nchunks = (Kdim + C::CH - 1) / C::CH;
+  const int Kpad = nchunks * C::CH;
+  const int upg = units_per_group(rows, R);
+  const int g0 = uni(static_cast<int>(lo / upg));
+  const int ng = uni(static_cast<int>((hi - 1) / upg)) - g0 + 1;
+  if (ng > kRangeGroups) return false;
+  int tot = 0, big = 0;
+  for (int j = 0; j < ng; ++j) {
+    Group G;
+    group_at(p, mt, U, g0 + j, G);
+    const int c = uni(G.cnt);
+    tot += c;
+    big |= c > TC;
+  }
+  const int trows = tot;
+  if (big || static_cast<long long>(trows) * Kpad * 2 > p.lds_bytes) return false;
+
+  // the range table (the LDS the previous phase used is free: its last
+  // barrier has passed)
+  if (static_cast<int>(threadIdx.x) < ng) {
+    const int j = threadIdx.x;
+    Group G;
+    group_at(p, mt, U, g0 + j, G);
+    const long long gs = static_cast<long long>(g0 + j) * upg;
+    rt.ustart[j] = static_cast<int>((gs > lo ? gs : lo) - lo);
+    rt.cnt[j] = G.cnt;
+    int r = 0;  // rows of the groups before j
+    for (int i = 0; i < j; ++i) {
+      Group Gi;
+      group_at(p, mt, U, g0 + i, Gi);
+      r += Gi.cnt;
+    }
+    rt.row0[j] = r;
+    if (j == ng - 1) rt.ustart[ng] = static_cast<int>(hi - lo);
+  }
+  for (int i = threadIdx.x; i < ng * 32; i += blockDim.x) {
+    const int j = i >> 5, t = i & 31;
+    Group G;
+    group_at(p, mt, U, g0 + j, G);
+    int xrow = 0, hrow = 0;
+    float* yrow = nullptr;
+    if (t < G.cnt) token_of(p, mt, G, t, xrow, hrow, yrow);
+    rt.xrow[j][t] = xrow;
+    rt.hrow[j][t] = hrow;
+    rt.yrow[j][t] = yrow;
+  }
+
+  // first unit of this wavefront, prefetched before the waits and the staging
+  const int nur = static_cast<int>(hi - lo);
+  u32x4 b0[NMAT][SPC][1], b1[NMAT][SPC][1];
+  float s0[NMAT][SPC], s1[NMAT][SPC];
+  float acc[C::NACC];
+#pragma unroll
+  for (int i = 0; i < C::NACC; ++i) acc[i] = 0.0f;
+  auto unit_group = [&](int u, Group& G, int& r0, int& rv) {
+    const long long gu = lo + (u < nur ? u : 0);
+    const int g = static_cast<int>(gu / upg);
+    group_at(p, mt, U, g, G);
+    G.e = uni(G.e);
+    G.shared = uni(G.shared);
+    r0 = static_cast<int>(gu - static_cast<long long>(g) * upg) * R;
+    const int valid = G.shared || (G.e >= 0 && G.e < p.E);
+    rv = (u < nur && valid) ? min(R, rows - r0) : 0;
+  };
+  {
+    Group G;
+    int r0, rv;
+    unit_group(wave, G, r0, rv);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, G, r0, rv, 0, rows, Kdim, lane, b0, s0);
+  }
+  if (UP && threadIdx.x == 0) {
+    for (int j = 0; j < ng; ++j) {
+      Group G;
+      group_at(p, mt, U, g0 + j, G);
+      if (!G.shared && (G.e < 0 || G.e >= p.E)) atomicOr(p.err, ERRBIT_BAD_IDS);
+    }
+  }
+  if (COH && !UP)
+    for (int j = 0; j < ng; ++j) wait_group_ready(sy, g0 + j);
+  __syncthreads();
+
+  // stage the table: the groups' rows of x (UP, bf16) or of H (DOWN: f32
+  // coherent loads rounded to bf16 in one launch, bf16 otherwise); zero
+  // beyond Kdim
+  {
+    const int vpt = Kpad / 8;
+    for (int v = threadIdx.x; v < trows * vpt; v += blockDim.x) {
+      const int row = v / vpt;
+      const int k = (v - row * vpt) * 8;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (k < Kdim) {
+        int j = 0;
+        while (j + 1 < ng && rt.row0[j + 1] <= row) ++j;
+        if (UP) {
+          const int xrow = rt.xrow[j][row - rt.row0[j]];
+          val = ld16(p.x + (static_cast<size_t>(xrow) * Kdim + k) * 2);
+        } else {
+          const int hrow = rt.hrow[j][row - rt.row0[j]];
+          if (COH) {
+            val = coh_h_to_staged<2>(p.H, (static_cast<size_t>(hrow) * Kdim + k) * 4);
+          } else {
+            val = ld16(p.H + (static_cast<size_t>(hrow) * Kdim + k) * 2);
+          }
+        }
+      }
+      st16(xs + static_cast<size_t>(v) * 16, val);
+    }
+  }
+  if (threadIdx.x == 0) *claim = static_cast<int>(blockDim.x) >> 6;
+  __syncthreads();
+
+  // unit u: group j of the range, its rows, and the B rows of its tokens
+  auto unit_tab = [&](int u, int& j, int& r0, int& rv, int& nt, int& tga, int (&boff)[TG]) {
+    j = 0;
+#pragma unroll
+    for (int i = 1; i < kRangeGroups; ++i)
+      if (i < ng && rt.ustart[i] <= u) j = i;
+    j = uni(j);
+    const long long gu = lo + (u < nur ? u : 0);
+    r0 = static_cast<int>(gu - static_cast<long long>(g0 + j) * upg) * R;
+    rv = u < nur ? min(R, rows - r0) : 0;
+    nt = uni(rt.cnt[j]);
+    tga = (nt + 3) >> 2;
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      const int t = min(4 * g + (lane & 3), nt - 1);
+      const int row = rt.row0[j] + (t < 0 ? 0 : t);
+      boff[g] = row * Kpad * 2;
+    }
+  };
+  int u = wave, kc = 0;
+  int j, r0, rv, nt, tga, boff[TG];
+  unit_tab(u, j, r0, rv, nt, tga, boff);
+  auto half = [&](int un, int kn, u32x4 (&bl)[NMAT][SPC][1], float (&sl)[NMAT][SPC],
+                  const u32x4 (&bm)[NMAT][SPC][1], const float (&sm)[NMAT][SPC]) {
+    {
+      Group G;
+      int q0, qv;
+      unit_group(un, G, q0, qv);
+      load_chunk<WT, TC, R, NMAT, SPC>(p, G, q0, qv, kn, rows, Kdim, lane, bl, sl);
+    }
+    mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, lane, xs, boff, tga, bm, sm, acc);
+    if (kc == nchunks - 1)
+      finish_unit_mf<WT, TC, R, NMAT, SPC, COH>(p, nt, tga, r0, rv, rows, lane, rt.hrow[j],
+                                                rt.yrow[j], acc);
+  };
+  auto take = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(claim, 1);
+    return uni(v);
+  };
+  int un = u, kn = kc + 1;
+  if (kn == nchunks) {
+    kn = 0;
+    un = take();
+  }
+  while (true) {
+    half(un, kn, b1, s1, b0, s0);
+    if (un >= nur) break;
+    if (kn == 0) unit_tab(un, j, r0, rv, nt, tga, boff);
+    u = un;
+    kc = kn;
+    if (++kn == nchunks) {
+      kn = 0;
+      un = take();
+    }
+    half(un, kn, b0, s0, b1, s1);
+    if (un >= nur) break;
+    if (kn == 0) unit_tab(un, j, r0, rv, nt, tga, boff);
+    u = un;
+    kc = kn;
+    if (++kn == nchunks) {
+      kn = 0;
+      un = take();
+    }
+  }
+  return true;
 }
 
 // ------------------------------------------------------------ one range
@@ -817,8 +1032,11 @@ __device__ __forceinline__ void mul_finish(int nt, bool last, int kc, int Kpad, 
 template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
 __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, int U, long long lo,
                                           long long hi, uint8_t* xs, int* tok_h, float** tok_y,
-                                          int* claim, const Sync& sy) {
+                                          RangeTab& rt, int* claim, const Sync& sy) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  if constexpr (C::MF) {
+    if (run_range_mf<WT, TC, R, NMAT, SPC, COH>(p, mt, U, lo, hi, xs, rt, claim, sy)) return;
+  }
   constexpr bool UP = NMAT == 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = UP ? p.f : p.d;
