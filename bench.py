@@ -421,9 +421,6 @@ def main():
     for mode, bkey, tkey in (("dedup", "union_bytes", "t_dedup"), ("slot", "requested_bytes", "t_slot")):
         beta, t0_ = cm.fit_bandwidth([per_n[n][bkey] for n in ns], [per_n[n][tkey] for n in ns])
         fit[mode] = {"GBs": round(beta / 1e9, 1), "t0_us": round(t0_ * 1e6, 2)}
-    rr = cm.fit_reread([per_n[n]["U"] for n in ns], [n * cfg.K for n in ns],
-                       layers[0].expert_bytes(), [per_n[n]["t_slot"] for n in ns])
-    fit["slot_reread_cost"] = round(rr["reread_cost"], 3)
     fit["crossover_n"] = cm.crossover(ns, [per_n[n]["t_slot"] - per_n[n]["t_dedup"] for n in ns])
     fit["ms_per_step_chained"] = round(ms_chain, 4)
 
@@ -455,6 +452,13 @@ def main():
                     "union_bytes": sum(b[0] for b in byt) / len(byt),
                     "requested_bytes": sum(b[1] for b in byt) / len(byt)}
         del sel
+    # per-slot re-read fit over n = 1..8 (four points would leave three
+    # parameters barely determined)
+    b_e = layers[0].expert_bytes()
+    rr = cm.fit_reread([model[n]["union_bytes"] / b_e for n in sorted(model)],
+                       [n * cfg.K for n in sorted(model)], b_e,
+                       [model[n]["t_slot"] for n in sorted(model)])
+    fit["slot_reread_cost"] = round(rr["reread_cost"], 3)
     for n in model:
         a = cm.aggregate([model[n]])
         model[n].update(u=a["u"], r=a["r"])
