@@ -119,21 +119,23 @@ def shape_sweep(dev, reps=10):
     128x128 block scales; independent and Markov routing, a 32-node tree).  Each point
     replays a graph of one pass per layer (layers alternate, so no pass finds its
     experts in the Infinity Cache); GB/s on union bytes (dedup) and on requested
-    bytes (per-slot)."""
+    bytes (per-slot).  The OLMoE-shaped layer is also run with the other reuse
+    probabilities of its recipe (p = 0, 0.8) and with independent routing."""
     import torch
 
     from moe_speculative_decoding_amd import _lib as L
     from moe_speculative_decoding_amd.layer import DeviceLayer, VerifyBuffers, to_device, verify_layer
     from synth import make_case
-    from synth.configs import DSV2LITE, DSV3, QWEN3
+    from synth.configs import DSV2LITE, DSV3, OLMOE, QWEN3
     from synth.gen import device_layer_weights
 
     stream = torch.cuda.current_stream()
-    plan = ((QWEN3, 4, (("logits_ar1", 1, False), ("logits_ar1", 8, False))),
-            (DSV2LITE, 4, (("markov:0.5", 1, False), ("markov:0.5", 8, False),
-                           ("markov:0.5", 16, True))),
-            (DSV3, 2, (("iid", 1, False), ("iid", 8, False), ("markov:0.5", 8, False),
-                       ("markov:0.5", 32, True))))
+    plan = ((OLMOE, 4, (("markov:0.0", 8, False), ("markov:0.8", 8, False), ("iid", 8, False))),
+            (QWEN3, 4, tuple(("logits_ar1", n, False) for n in (1, 2, 4, 8))),
+            (DSV2LITE, 4, tuple(("markov:0.5", n, False) for n in (1, 2, 4, 8)) +
+             (("markov:0.5", 16, True),)),
+            (DSV3, 2, tuple(("iid", n, False) for n in (1, 2, 4, 8)) +
+             (("markov:0.5", 8, False), ("markov:0.5", 32, True))))
     out = {}
     for cfg, nl, points in plan:
         layers = []

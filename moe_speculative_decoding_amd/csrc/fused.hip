@@ -208,19 +208,22 @@ void layer_kernel(LayerParams lp) {
   for (int task = b * kStreamBlock + tid; task < tasks; task += G * kStreamBlock) {
     const int t = task / quads;
     const int c = (task - t * quads) * 4;
+    // every load is issued unconditionally, so all are in flight at once:
+    // slots k >= K read the next token's rows or, past the end of the
+    // buffer, zeros (the buffer range check), and are not summed
     u32x4 yv[8], sv[4];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (k < K)
-        yv[k] = coh_ld16(p.y_slots,
-                         static_cast<unsigned>(((static_cast<size_t>(t) * K + k) * p.d + c) * 4),
-                         ys_size);
+      yv[k] = coh_ld16(p.y_slots,
+                       static_cast<unsigned>(((static_cast<size_t>(t) * K + k) * p.d + c) * 4),
+                       ys_size);
+    if (S > 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q < S)
+      for (int q = 0; q < 4; ++q)
         sv[q] = coh_ld16(p.y_shared,
                          static_cast<unsigned>(((static_cast<size_t>(t) * S + q) * p.d + c) * 4),
                          sh_size);
+    }
     // the order of moe_combine: k ascending, then the shared experts
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
