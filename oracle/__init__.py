@@ -13,3 +13,4 @@ from .evict_ref import evict_select, is_ancestor_closed, path_scores, rank_nodes
 from .ecospec_ref import (  # noqa: F401,E402
     cumulative_probability, ecospec_select, path_footprints,
 )
+from .budget_ref import apply_budget, expert_scores, kept_experts, verify_op_budget  # noqa: F401,E402
