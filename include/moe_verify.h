@@ -126,6 +126,34 @@ moe_status moe_route_union(const float* logits, int32_t n, int32_t E, int32_t K,
                            int32_t* offsets, int32_t* perm, int32_t* slot_rank,
                            moe_stream_t stream);
 
+/* Per-layer expert budget on a union ("MoE-Spec: Expert Budgeting for
+ * Efficient Speculative Decoding", abstract: a layer of the verify pass loads
+ * at most C experts, those contributing most to the verified tokens).  The
+ * page gives no formula; here an expert's contribution is the float32 sum of
+ * the gates of its slots (ascending slot order), the C largest are kept
+ * (equal contributions: the lower id; NaN below every number), and a dropped
+ * slot adds nothing to the layer output.
+ *   gates      (device) f32 [n][K]: the pass's gates
+ *   U, union_ids, offsets, perm, slot_rank (device, in/out): the union of
+ *              moe_build_union / moe_route_union for the same slots, rewritten
+ *              in place when C < U: U = C; union_ids the kept experts
+ *              ascending (-1 beyond); offsets over the kept groups, entries
+ *              from U on = the number of kept slots; perm the kept slots
+ *              grouped by expert as before, then the dropped slots in
+ *              ascending order; slot_rank -1 for a dropped slot.  Unchanged
+ *              when C >= U or U < 0.
+ *   gates_out  (device) f32 [n][K] (may be gates): 0 for a dropped slot; with
+ *              renorm = 1 the kept gates of a token that lost a slot are
+ *              divided by their float32 sum (k ascending; 0 if that sum is 0).
+ * moe_expert_ffn_dedup on the rewritten union streams the kept experts only
+ * and writes zero output rows for the dropped slots; moe_combine with
+ * gates_out then gives the budgeted layer output.
+ * 1 <= C; renorm 0 or 1.  Bit-exact and deterministic.  Errors: MOE_ERR_ARG. */
+moe_status moe_expert_budget(const float* gates, int32_t n, int32_t K, int32_t E, int32_t C,
+                             int32_t renorm, int32_t* U, int32_t* union_ids, int32_t* offsets,
+                             int32_t* perm, int32_t* slot_rank, float* gates_out,
+                             moe_stream_t stream);
+
 /* Deduplicating expert FFN: each expert of the union (and each shared expert)
  * is streamed from HBM once and applied to every slot routed to it (the
  * expert-bytes page, abstract).  The union arrays are those of
@@ -138,6 +166,8 @@ moe_status moe_route_union(const float* logits, int32_t n, int32_t E, int32_t K,
  *             b = bytes of one expert (3*d*f*elem, plus fp8 scales)
  *   ws        (device) workspace of at least moe_workspace_size(shape, n, DEDUP)
  *             bytes, zero-filled before its first use (moe_workspace_init).
+ * Slots that belong to no group (perm entries from offsets[U] on: those an
+ * expert budget dropped) get zero output rows.
  * Errors: MOE_ERR_ARG / _UNSUPPORTED / _WORKSPACE on the host; a device-side
  * U < 0 records MOE_ERR_BAD_IDS in the workspace. */
 moe_status moe_expert_ffn_dedup(const moe_shape* shape, const moe_weights* w,
@@ -174,9 +204,9 @@ moe_status moe_combine(const float* y_slots, const float* gates, const float* y_
  * the union of moe_build_union (deduplicating mode), the expert FFN of
  * moe_expert_ffn_dedup or moe_expert_ffn_perslot (mode) and the combine of
  * moe_combine, with the same results bit for bit (the pages of each step are
- * cited at those calls).  Every workgroup routes the pass itself; UP and DOWN
- * work is handed out with a ticket counter and exchanged between workgroups
- * through device-coherent stores, with bounded waits.
+ * cited at those calls).  Every workgroup routes the pass itself and streams
+ * a fixed share of the UP and DOWN work; intermediate results are exchanged
+ * between workgroups through device-coherent stores, with bounded waits.
  *   logits    (device) f32 [n][E];  x (device) [n][d] in shape->x_dtype
  *   out       (device) [n][d] of out_dtype (MOE_F32 or MOE_BF16)
  *   ids, gates (device, optional) [n][K] routing outputs
@@ -196,6 +226,22 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
                             int32_t* offsets, int32_t* perm, int32_t* slot_rank, float* y_slots,
                             float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
                             moe_stream_t stream);
+
+/* moe_verify_layer in deduplicating mode with a per-layer expert budget:
+ * the route and union, then moe_expert_budget(C, renorm) on them, the
+ * deduplicating FFN over the kept experts and the combine with the budgeted
+ * gates, with the same results bit for bit as that chain of calls.  gates
+ * (when given) receives the budgeted gates, the union outputs the budgeted
+ * union, y_slots zero rows for the dropped slots, bytes[0] (min(U, C) + S) b.
+ * Other arguments as moe_verify_layer.  Errors: MOE_ERR_ARG for C < 1 or
+ * renorm not 0 or 1, otherwise as moe_verify_layer. */
+moe_status moe_verify_layer_budget(const moe_shape* shape, const moe_weights* w,
+                                   const float* logits, const void* x, int32_t n, int32_t C,
+                                   int32_t renorm, void* out, int32_t out_dtype, int32_t* ids,
+                                   float* gates, int32_t* U, int32_t* union_ids, int32_t* offsets,
+                                   int32_t* perm, int32_t* slot_rank, float* y_slots,
+                                   float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
+                                   moe_stream_t stream);
 
 /* moe_verify_layer with the mode chosen on the device for each pass: the
  * pass deduplicates iff its byte share (U + S) / (n (K + S)) is below r, the

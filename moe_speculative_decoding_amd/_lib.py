@@ -60,6 +60,7 @@ _SIG = {
     "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_build_union": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_route_union": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_budget": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_dedup": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _I, _P, _P,
                                   _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_expert_ffn_perslot": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _I, _P, _P,
@@ -67,6 +68,9 @@ _SIG = {
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]),
     "moe_verify_layer": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I, _I, _P,
                               _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_verify_layer_budget": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I,
+                                     _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     C.c_size_t, _P]),
     "moe_verify_layer_auto": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I,
                                    C.c_float, _P, _I, _P, _P, _P, C.c_size_t, _P]),
     "moe_evict_select": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P]),
@@ -146,6 +150,13 @@ def moe_route_union(logits, n, E, K, ids, gates, U, union_ids, offsets, perm, sl
            "moe_route_union")
 
 
+def moe_expert_budget(gates, n, K, E, C_, renorm, U, union_ids, offsets, perm, slot_rank,
+                      gates_out, stream=None) -> None:
+    _check(lib.moe_expert_budget(ptr(gates), n, K, E, C_, int(renorm), ptr(U), ptr(union_ids),
+                                 ptr(offsets), ptr(perm), ptr(slot_rank), ptr(gates_out),
+                                 _stream(stream)), "moe_expert_budget")
+
+
 def moe_expert_ffn_dedup(shape: moe_shape, w: moe_weights, x, n, U, union_ids, offsets, perm,
                          y_slots, y_shared, bytes_, ws, ws_bytes, stream=None) -> None:
     _check(lib.moe_expert_ffn_dedup(C.byref(shape), C.byref(w), ptr(x), n, ptr(U), ptr(union_ids),
@@ -175,6 +186,18 @@ def moe_verify_layer(shape: moe_shape, w: moe_weights, logits, x, n, mode, out, 
                                 ptr(offsets), ptr(perm), ptr(slot_rank), ptr(y_slots),
                                 ptr(y_shared), ptr(bytes_), ptr(ws), ws_bytes, _stream(stream)),
            "moe_verify_layer")
+
+
+def moe_verify_layer_budget(shape: moe_shape, w: moe_weights, logits, x, n, C_, renorm, out,
+                            out_dtype, ids=None, gates=None, U=None, union_ids=None, offsets=None,
+                            perm=None, slot_rank=None, y_slots=None, y_shared=None, bytes_=None,
+                            ws=None, ws_bytes=0, stream=None) -> None:
+    _check(lib.moe_verify_layer_budget(C.byref(shape), C.byref(w), ptr(logits), ptr(x), n, C_,
+                                       int(renorm), ptr(out), out_dtype, ptr(ids), ptr(gates),
+                                       ptr(U), ptr(union_ids), ptr(offsets), ptr(perm),
+                                       ptr(slot_rank), ptr(y_slots), ptr(y_shared), ptr(bytes_),
+                                       ptr(ws), ws_bytes, _stream(stream)),
+           "moe_verify_layer_budget")
 
 
 def moe_verify_layer_auto(shape: moe_shape, w: moe_weights, logits, x, n, r, out, out_dtype,

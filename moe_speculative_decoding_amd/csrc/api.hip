@@ -203,6 +203,44 @@ moe::LayerParams layer_params(const moe_shape* shape, const moe_weights* w, cons
   lp.down_flags = lp.up_flags + moe::kMaxGrid;
   return lp;
 }
+
+// the one-launch pass of moe_verify_layer / moe_verify_layer_budget (budget
+// 0: none)
+moe_status verify_layer_impl(const moe_shape* shape, const moe_weights* w, const float* logits,
+                             const void* x, int n, int mode, int budget, int renorm, void* out,
+                             int out_dtype, int32_t* ids, float* gates, int32_t* U,
+                             int32_t* union_ids, int32_t* offsets, int32_t* perm,
+                             int32_t* slot_rank, float* y_slots, float* y_shared, uint64_t* bytes,
+                             void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (mode != MOE_MODE_DEDUP && mode != MOE_MODE_PERSLOT) return MOE_ERR_ARG;
+  moe_status st = moe_verify_layer_check(shape, w, logits, x, n, mode, out, out_dtype, y_slots,
+                                         y_shared, bytes, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if ((ids != nullptr && !aligned(ids, 4)) || (gates != nullptr && !aligned(gates, 4)))
+    return MOE_ERR_ARG;
+  const void* uni[5] = {U, union_ids, offsets, perm, slot_rank};
+  int given = 0;
+  for (const void* p : uni) {
+    if (p != nullptr && !aligned(p, 4)) return MOE_ERR_ARG;
+    given += p != nullptr;
+  }
+  if (given != 0 && given != 5) return MOE_ERR_ARG;
+  moe::LayerParams lp = layer_params(
+      shape, w, logits, x, n, mode == MOE_MODE_DEDUP ? moe::MODE_DEDUP : moe::MODE_PERSLOT, out,
+      out_dtype, y_slots, y_shared, bytes, ws);
+  lp.ids = ids;
+  lp.gates = gates;
+  lp.budget = budget;
+  lp.renorm = renorm;
+  if (mode == MOE_MODE_DEDUP && given == 5) {
+    lp.U = U;
+    lp.union_ids = union_ids;
+    lp.offsets = offsets;
+    lp.perm = perm;
+    lp.slot_rank = slot_rank;
+  }
+  return hip_status(moe::launch_layer(lp, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
+}
 }  // namespace
 
 extern "C" {
@@ -317,32 +355,36 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
                             int32_t* offsets, int32_t* perm, int32_t* slot_rank, float* y_slots,
                             float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
                             moe_stream_t stream) {
-  if (mode != MOE_MODE_DEDUP && mode != MOE_MODE_PERSLOT) return MOE_ERR_ARG;
-  moe_status st = moe_verify_layer_check(shape, w, logits, x, n, mode, out, out_dtype, y_slots,
-                                         y_shared, bytes, ws, ws_bytes);
-  if (st != MOE_OK) return st;
-  if ((ids != nullptr && !aligned(ids, 4)) || (gates != nullptr && !aligned(gates, 4)))
-    return MOE_ERR_ARG;
-  const void* uni[5] = {U, union_ids, offsets, perm, slot_rank};
-  int given = 0;
-  for (const void* p : uni) {
-    if (p != nullptr && !aligned(p, 4)) return MOE_ERR_ARG;
-    given += p != nullptr;
-  }
-  if (given != 0 && given != 5) return MOE_ERR_ARG;
-  moe::LayerParams lp = layer_params(
-      shape, w, logits, x, n, mode == MOE_MODE_DEDUP ? moe::MODE_DEDUP : moe::MODE_PERSLOT, out,
-      out_dtype, y_slots, y_shared, bytes, ws);
-  lp.ids = ids;
-  lp.gates = gates;
-  if (mode == MOE_MODE_DEDUP && given == 5) {
-    lp.U = U;
-    lp.union_ids = union_ids;
-    lp.offsets = offsets;
-    lp.perm = perm;
-    lp.slot_rank = slot_rank;
-  }
-  return hip_status(moe::launch_layer(lp, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
+  return verify_layer_impl(shape, w, logits, x, n, mode, 0, 0, out, out_dtype, ids, gates, U,
+                           union_ids, offsets, perm, slot_rank, y_slots, y_shared, bytes, ws,
+                           ws_bytes, stream);
+}
+
+moe_status moe_verify_layer_budget(const moe_shape* shape, const moe_weights* w,
+                                   const float* logits, const void* x, int32_t n, int32_t C,
+                                   int32_t renorm, void* out, int32_t out_dtype, int32_t* ids,
+                                   float* gates, int32_t* U, int32_t* union_ids, int32_t* offsets,
+                                   int32_t* perm, int32_t* slot_rank, float* y_slots,
+                                   float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
+                                   moe_stream_t stream) {
+  if (C < 1 || (renorm != 0 && renorm != 1)) return MOE_ERR_ARG;
+  return verify_layer_impl(shape, w, logits, x, n, MOE_MODE_DEDUP, C, renorm, out, out_dtype,
+                           ids, gates, U, union_ids, offsets, perm, slot_rank, y_slots, y_shared,
+                           bytes, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_budget(const float* gates, int32_t n, int32_t K, int32_t E, int32_t C,
+                             int32_t renorm, int32_t* U, int32_t* union_ids, int32_t* offsets,
+                             int32_t* perm, int32_t* slot_rank, float* gates_out,
+                             moe_stream_t stream) {
+  if (n < 1 || n > kMaxN || K < 1 || K > kMaxK || E < K || E > kMaxE) return MOE_ERR_ARG;
+  if (C < 1 || (renorm != 0 && renorm != 1)) return MOE_ERR_ARG;
+  const void* ptrs[7] = {gates, U, union_ids, offsets, perm, slot_rank, gates_out};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned(p, 4)) return MOE_ERR_ARG;
+  return hip_status(moe::launch_expert_budget(gates, n, K, E, C, renorm, U, union_ids, offsets,
+                                              perm, slot_rank, gates_out,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_verify_layer_auto(const moe_shape* shape, const moe_weights* w,

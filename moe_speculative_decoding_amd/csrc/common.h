@@ -117,6 +117,8 @@ struct LayerParams {
   unsigned* epoch;        // call counter of the workspace
   unsigned* up_flags;     // [kMaxGrid] UP range done (tag of the call)
   unsigned* down_flags;   // [kMaxGrid] DOWN range done
+  int budget;             // dedup: keep at most this many routed experts (0: no budget)
+  int renorm;             // budget: renormalise the kept gates of a token that lost a slot
 };
 
 // Tile shapes of the FFN phases (rows per wave R, load steps per chunk SPC
@@ -158,6 +160,9 @@ hipError_t launch_build_union(const int32_t* ids, int n, int K, int E, int32_t* 
 hipError_t launch_route_union(const float* logits, int n, int E, int K, int32_t* ids,
                               float* gates, int32_t* U, int32_t* union_ids, int32_t* offsets,
                               int32_t* perm, int32_t* slot_rank, hipStream_t s);
+hipError_t launch_expert_budget(const float* gates, int n, int K, int E, int C, int renorm,
+                                int32_t* U, int32_t* union_ids, int32_t* offsets, int32_t* perm,
+                                int32_t* slot_rank, float* gates_out, hipStream_t s);
 hipError_t launch_expert_ffn(const FfnParams& p, int w_dtype, hipStream_t s);
 hipError_t launch_layer(const LayerParams& lp, int w_dtype, hipStream_t s);
 hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,

@@ -58,10 +58,11 @@ void ffn_stream_kernel(FfnParams p) {
   const long long NU = static_cast<long long>(NG) * upg;
   const long long lo = NU * blockIdx.x / gridDim.x;
   const long long hi = NU * (blockIdx.x + 1) / gridDim.x;
-  if (lo >= hi) return;
 
   load_meta(p, mt);
   __syncthreads();
+  if (!UP && p.mode == MODE_DEDUP) zero_unrouted_rows(p, mt, U);
+  if (lo >= hi) return;
   run_range<WT, TC, R, NMAT, SPC, false>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, &claim, Sync{});
 }
 

@@ -52,6 +52,8 @@ struct RouteLds {
 };
 constexpr size_t kRouteTopkOffset = (sizeof(RouteLds) + 15) / 16 * 16;
 constexpr size_t kRouteLogitsOffset = kRouteTopkOffset + kMaxStreamWaves * sizeof(TopkLds);
+static_assert(sizeof(BudgetLds) <= kMaxStreamWaves * sizeof(TopkLds),
+              "the budget tables reuse the top-K scratch");
 
 // UP range b, then DOWN range b, with the tile shapes of token tile TC (the
 // two-kernel FFN's shapes for the same tile, so both run the same arithmetic)
@@ -104,6 +106,7 @@ void layer_kernel(LayerParams lp) {
   __shared__ int ids_l[kMaxSlots];
   __shared__ float gates_l[kMaxSlots];
   __shared__ int U_l;
+  __shared__ uint8_t drop_l[kMaxSlots / 8];  // expert budget: bit k of token t = slot dropped
   __shared__ int claim;  // next unit of the running phase (stream.h)
   __shared__ RangeTab rt;
   const FfnParams& p = lp.f;
@@ -149,6 +152,18 @@ void layer_kernel(LayerParams lp) {
     build_union_256(ids_l, n, K, E, &U_l, mt.b, mt.a, mt.c, rl.slot_rank, rl.ul);
     __syncthreads();
     U = uni(U_l);
+  }
+  // expert budget (deduplicating mode): the union keeps the lp.budget experts
+  // of largest gate mass; the top-K scratch is dead and holds its tables
+  const bool budgeted = mode == MODE_DEDUP && lp.budget > 0 && U > lp.budget;  // uniform
+  if (budgeted)
+    U = uni(apply_budget(U, lp.budget, lp.renorm, n, K, p.ucap, mt.b, mt.a, mt.c, rl.slot_rank,
+                         gates_l, *reinterpret_cast<BudgetLds*>(xs + kRouteTopkOffset)));
+  if (tid < n) {
+    unsigned m = 0;
+    if (budgeted)
+      for (int k = 0; k < K; ++k) m |= (rl.slot_rank[tid * K + k] < 0 ? 1u : 0u) << k;
+    drop_l[tid] = static_cast<uint8_t>(m);
   }
   if (mode == MODE_AUTO) {
     // the expert-bytes page's Eq. (7): deduplicate iff its byte share
@@ -224,11 +239,17 @@ void layer_kernel(LayerParams lp) {
                          static_cast<unsigned>(((static_cast<size_t>(t) * S + q) * p.d + c) * 4),
                          sh_size);
     }
-    // the order of moe_combine: k ascending, then the shared experts
+    // the order of moe_combine: k ascending, then the shared experts; a slot
+    // an expert budget dropped adds nothing and gets a zero output row
+    const unsigned dm = drop_l[t];
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (k < K) {
+      if (k < K && ((dm >> k) & 1u) != 0u)
+        st16(reinterpret_cast<uint8_t*>(p.y_slots) +
+                 ((static_cast<size_t>(t) * K + k) * p.d + c) * 4,
+             u32x4{0u, 0u, 0u, 0u});
+      if (k < K && ((dm >> k) & 1u) == 0u) {
         const float g = gates_l[t * K + k];
         acc[0] = fmaf(g, __uint_as_float(yv[k].x), acc[0]);
         acc[1] = fmaf(g, __uint_as_float(yv[k].y), acc[1]);

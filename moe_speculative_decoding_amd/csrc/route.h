@@ -311,4 +311,128 @@ __device__ __forceinline__ void build_union_256(const int32_t* ids, int n, int K
   }
 }
 
+
+// ----------------------------------------------------------- expert budget
+// LDS scratch of apply_budget.
+struct BudgetLds {
+  unsigned long long key[256];  // order key of union expert u (larger = kept first)
+  int old_perm[256];            // the perm before the rewrite
+  int newpos[256];              // u kept: its position in the budgeted union; dropped: -1
+  int wkept[4], wslots[4], wdrop[4];
+};
+
+// Per-layer expert budget ("MoE-Spec: Expert Budgeting for Efficient
+// Speculative Decoding", abstract: a layer loads at most C experts, those
+// contributing most to the verified tokens).  An expert's contribution is the
+// f32 sum of the gates of its slots in ascending slot order; the C largest
+// are kept (equal contributions: the lower id; NaN below every number), in
+// the order key of the router's top-K.  Rewrites, in place, the union arrays
+// of build_union_256 for the same slots: the kept experts ascending, their
+// slots grouped as before, offsets from the new U on = the kept slot count,
+// the dropped slots after the kept ones in ascending order, slot_rank -1 for
+// a dropped slot; a dropped slot's gate becomes 0 and, with renorm, the kept
+// gates of a token that lost a slot are divided by their f32 sum (k
+// ascending).  Every thread of the workgroup calls it (it holds
+// __syncthreads; at least 256 threads); returns the new U.  Call only with
+// 0 <= C < U.
+__device__ __forceinline__ int apply_budget(int U, int C, int renorm, int n, int K, int cap,
+                                            int32_t* union_ids, int32_t* offsets, int32_t* perm,
+                                            int32_t* slot_rank, float* gates, BudgetLds& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool mine = tid < 256;
+  const int nk = n * K;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  // contributions and order keys of the old union
+  int my_id = 0, my_off = 0, my_cnt = 0;
+  if (mine && tid < U) {
+    my_id = union_ids[tid];
+    my_off = offsets[tid];
+    my_cnt = offsets[tid + 1] - my_off;
+    float c = 0.0f;
+    for (int i = 0; i < my_cnt; ++i) c += gates[perm[my_off + i]];
+    sh.key[tid] = (static_cast<unsigned long long>(topk_key(c)) << 8) |
+                  static_cast<unsigned>(255 - my_id);
+  }
+  if (mine && tid < nk) sh.old_perm[tid] = perm[tid];
+  __syncthreads();
+
+  // rank = number of keys above mine; kept iff rank < C
+  bool kept = false;
+  if (mine && tid < U) {
+    const unsigned long long k = sh.key[tid];
+    int r = 0;
+    for (int v = 0; v < U; ++v) r += sh.key[v] > k ? 1 : 0;
+    kept = r < C;
+  }
+  // new position: kept experts below mine; new offset: their slot counts
+  const unsigned long long km = __ballot(kept);
+  const int kc = kept ? my_cnt : 0;
+  const int inc = wave_inclusive_sum(kc, lane);
+  if (mine && lane == kWave - 1) {
+    sh.wkept[wave] = __popcll(km);
+    sh.wslots[wave] = inc;
+  }
+  __syncthreads();
+  int bk = 0, bs = 0, Uk = 0, nkept = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) {
+      bk += sh.wkept[w];
+      bs += sh.wslots[w];
+    }
+    Uk += sh.wkept[w];
+    nkept += sh.wslots[w];
+  }
+  const int npos = kept ? bk + __popcll(km & below) : -1;
+  if (mine) sh.newpos[tid] = npos;
+  if (kept) {
+    const int noff = bs + inc - kc;
+    union_ids[npos] = my_id;
+    offsets[npos] = noff;
+    for (int i = 0; i < my_cnt; ++i) perm[noff + i] = sh.old_perm[my_off + i];
+  }
+  if (mine) {
+    for (int i = Uk + tid; i < cap; i += 256) union_ids[i] = -1;
+    for (int i = Uk + tid; i <= cap; i += 256) offsets[i] = nkept;
+  }
+  __syncthreads();
+
+  // slot ranks, and the dropped slots after the kept ones
+  const bool act = mine && tid < nk;
+  const int nr = act ? sh.newpos[slot_rank[tid]] : 0;
+  const bool drop = act && nr < 0;
+  const unsigned long long dm = __ballot(drop);
+  if (mine && lane == kWave - 1) sh.wdrop[wave] = __popcll(dm);
+  __syncthreads();
+  int bd = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (w < wave) bd += sh.wdrop[w];
+  if (act) {
+    slot_rank[tid] = nr;
+    if (drop) perm[nkept + bd + __popcll(dm & below)] = tid;
+  }
+  __syncthreads();
+
+  // gates of the dropped slots, and the kept ones renormalised
+  if (tid < n) {
+    float tot = 0.0f;
+    bool lost = false;
+    for (int k = 0; k < K; ++k) {
+      if (slot_rank[tid * K + k] < 0) lost = true;
+      else tot += gates[tid * K + k];
+    }
+    const bool div = renorm != 0 && lost;
+    for (int k = 0; k < K; ++k) {
+      const int s = tid * K + k;
+      float g = gates[s];
+      if (slot_rank[s] < 0) g = 0.0f;
+      else if (div) g = tot > 0.0f ? g / tot : 0.0f;
+      gates[s] = g;
+    }
+  }
+  __syncthreads();
+  return Uk;
+}
+
 }  // namespace moe

@@ -248,6 +248,19 @@ __device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
   }
 }
 
+// Deduplicating mode: the slots after offsets[U] in perm (dropped by an
+// expert budget) belong to no group; their output rows are zero.  Spread over
+// the whole grid; nothing to do for a plain union (offsets[U] = n*K).
+__device__ __forceinline__ void zero_unrouted_rows(const FfnParams& p, const Meta& mt, int U) {
+  const int nk = p.n * p.K, first = mt.a[U];
+  const long long total = static_cast<long long>(nk - first) * p.d;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const long long r = i / p.d;
+    p.y_slots[static_cast<size_t>(mt.c[first + r]) * p.d + (i - r * p.d)] = 0.0f;
+  }
+}
+
 // token j of a group: its row in x, its row in H and its output row
 __device__ __forceinline__ void token_of(const FfnParams& p, const Meta& mt, const Group& G, int j,
                                          int& xrow, int& hrow, float*& yrow) {

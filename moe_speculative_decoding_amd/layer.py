@@ -116,3 +116,34 @@ def verify_layer_auto(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor,
     own union and the measured bandwidth ratio r (moe_verify_layer_auto)."""
     L.moe_verify_layer_auto(layer.shape, layer.weights, logits, x, n, r, buf.out, buf.out_dtype,
                             mode_out, buf.bytes, buf.ws, buf.ws_bytes, stream)
+
+
+def verify_pass_budget(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor,
+                       logits: torch.Tensor, n: int, C: int, renorm: bool = False,
+                       stream=None) -> None:
+    """route + union -> expert budget (gates rewritten in place) -> deduplicating
+    FFN over the kept experts -> combine, all enqueued on one stream."""
+    K, E, S, d = layer.K, layer.E, layer.S, layer.d
+    ysh = buf.y_shared if S > 0 else None
+    L.moe_route_union(logits, n, E, K, buf.ids, buf.gates, buf.U, buf.union_ids, buf.offsets,
+                      buf.perm, buf.slot_rank, stream)
+    L.moe_expert_budget(buf.gates, n, K, E, C, renorm, buf.U, buf.union_ids, buf.offsets,
+                        buf.perm, buf.slot_rank, buf.gates, stream)
+    L.moe_expert_ffn_dedup(layer.shape, layer.weights, x, n, buf.U, buf.union_ids, buf.offsets,
+                           buf.perm, buf.y_slots, ysh, buf.bytes, buf.ws, buf.ws_bytes, stream)
+    L.moe_combine(buf.y_slots, buf.gates, ysh, n, K, S, d, buf.out, buf.out_dtype, stream)
+
+
+def verify_layer_budget(layer: DeviceLayer, buf: VerifyBuffers, x: torch.Tensor,
+                        logits: torch.Tensor, n: int, C: int, renorm: bool = False,
+                        stream=None, keep: bool = True) -> None:
+    """The budgeted pass in one launch (moe_verify_layer_budget)."""
+    ysh = buf.y_shared if layer.S > 0 else None
+    if keep:
+        L.moe_verify_layer_budget(layer.shape, layer.weights, logits, x, n, C, renorm, buf.out,
+                                  buf.out_dtype, buf.ids, buf.gates, buf.U, buf.union_ids,
+                                  buf.offsets, buf.perm, buf.slot_rank, buf.y_slots, ysh,
+                                  buf.bytes, buf.ws, buf.ws_bytes, stream)
+    else:
+        L.moe_verify_layer_budget(layer.shape, layer.weights, logits, x, n, C, renorm, buf.out,
+                                  buf.out_dtype, ws=buf.ws, ws_bytes=buf.ws_bytes, stream=stream)

@@ -18,9 +18,9 @@ of rarely used experts.  The page gives no formula; the readings taken here
   order, from float32 gates: the precision of the kernels, so both sides take
   the same keep/drop decision;
 * a dropped slot contributes nothing to the layer output (its gate becomes 0
-  and its expert output row is zero); with ``renorm`` the kept gates of each
-  token are divided by their sum (a token with no kept expert keeps gate 0
-  everywhere);
+  and its expert output row is zero); with ``renorm`` the kept gates of a
+  token that lost a slot are divided by their sum (a token with no kept
+  expert keeps gate 0 everywhere; a token that lost nothing is unchanged);
 * C >= U leaves the pass unchanged; the union bytes become (min(U, C) + S) b.
 """
 from __future__ import annotations
@@ -73,7 +73,8 @@ def apply_budget(ids: np.ndarray, gates: np.ndarray, union: Dict[str, object], C
     kept slots; perm lists the kept slots grouped by expert, then the dropped
     slots in ascending order; slot_rank is -1 for a dropped slot), plus
     ``gates`` float64 [n][K] (dropped slots 0, kept ones renormalised per token
-    when ``renorm``) and ``kept`` (the kept expert ids).
+    when ``renorm`` and the token lost a slot) and ``kept`` (the kept expert
+    ids).
     """
     ids = np.asarray(ids)
     n, K = ids.shape
@@ -101,11 +102,14 @@ def apply_budget(ids: np.ndarray, gates: np.ndarray, union: Dict[str, object], C
     g = np.zeros((n, K))
     for t in range(n):
         total = 0.0
+        lost = False
         for k in range(K):
             if flat[t * K + k] in keep:
                 g[t, k] = g64[t, k]
                 total += g64[t, k]
-        if renorm and total > 0.0:
+            else:
+                lost = True
+        if renorm and lost and total > 0.0:
             g[t] /= total
     return {"U": Uk, "union_ids": union_ids, "offsets": offsets, "perm": perm,
             "slot_rank": slot_rank, "gates": g, "kept": kept, "scores": scores,

@@ -175,6 +175,40 @@ def test_layer_auto_validation_before_launch():
     assert call(a7=L.MOE_FP8_E4M3) == L.MOE_ERR_UNSUPPORTED
 
 
+def test_budget_validation_before_launch():
+    eb = L.lib.moe_expert_budget
+    base = [FAKE, 4, 2, 8, 3, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    def call(**chg):
+        a = list(base)
+        for k, v in chg.items():
+            a[int(k[1:])] = v
+        return eb(*a)
+    assert call(a4=0) == L.MOE_ERR_ARG                   # C < 1
+    assert call(a5=2) == L.MOE_ERR_ARG                   # renorm not 0/1
+    assert call(a1=33) == L.MOE_ERR_ARG                  # n
+    assert call(a3=1) == L.MOE_ERR_ARG                   # E < K
+    assert call(a0=None) == L.MOE_ERR_ARG
+    assert call(a8=FAKE + 2) == L.MOE_ERR_ARG            # misaligned offsets
+    assert call(a11=None) == L.MOE_ERR_ARG
+    s = shape()
+    w = _weights()
+    need = L.moe_workspace_size(s, 8, L.MOE_MODE_DEDUP)
+    vb = L.lib.moe_verify_layer_budget
+    lb = [C.byref(s), C.byref(w), FAKE, FAKE, 8, 4, 1, FAKE, L.MOE_F32, None, None, None, None,
+          None, None, None, None, None, None, FAKE, need, None]
+    def lcall(**chg):
+        a = list(lb)
+        for k, v in chg.items():
+            a[int(k[1:])] = v
+        return vb(*a)
+    assert lcall(a5=0) == L.MOE_ERR_ARG                  # C < 1
+    assert lcall(a6=-1) == L.MOE_ERR_ARG                 # renorm
+    assert lcall(a4=0) == L.MOE_ERR_ARG                  # n
+    assert lcall(a11=FAKE) == L.MOE_ERR_ARG              # union outputs: all or none
+    assert lcall(a20=need - 1) == L.MOE_ERR_WORKSPACE
+    assert lcall(a8=L.MOE_FP8_E4M3) == L.MOE_ERR_UNSUPPORTED
+
+
 def test_evict_validation_before_launch():
     ev = L.lib.moe_evict_select
     base = [FAKE, FAKE, FAKE, 16, FAKE, None, None, FAKE, FAKE, 256, None]

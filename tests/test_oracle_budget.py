@@ -121,12 +121,13 @@ def test_structure_of_budgeted_union(seed):
         assert np.all(b["gates"][~np.isin(ids, list(keep))] == 0.0)
 
 
-def test_budget_not_binding_is_identity():
+@pytest.mark.parametrize("renorm", [False, True])
+def test_budget_not_binding_is_identity(renorm):
     case = make_case(TINY, 4, seed=0)
     plain = oracle.verify_op(case, "dedup")
     U = plain["union"]["U"]
     for C in (U, U + 3):
-        b = verify_op_budget(case, C)
+        b = verify_op_budget(case, C, renorm=renorm)
         assert np.array_equal(b["out"], plain["out"])
         for key in ("union_ids", "offsets", "perm", "slot_rank"):
             assert np.array_equal(b["union"][key], plain["union"][key])
@@ -160,7 +161,8 @@ def test_dropped_slots_contribute_nothing(renorm):
     g = np.where(keep, gates, 0.0)
     if renorm:
         tot = g.sum(axis=1, keepdims=True)
-        g = np.divide(g, tot, out=np.zeros_like(g), where=tot > 0)
+        lost = (~keep).any(axis=1, keepdims=True)
+        g = np.where(lost, np.divide(g, tot, out=np.zeros_like(g), where=tot > 0), g)
     ref = np.einsum("tk,tkd->td", g, y) + ysh.sum(axis=1)
     assert np.allclose(b["out"], ref, rtol=1e-12, atol=1e-12)
     assert np.all(b["y_slots"][~keep] == 0.0)
