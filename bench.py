@@ -197,6 +197,97 @@ def shape_sweep(dev, reps=10):
     return out
 
 
+def budget_sweep(dev, reps=10):
+    """The one-launch pass with a per-layer expert budget (moe_verify_layer_budget,
+    kept gates renormalised) against the same pass without one: time, budgeted union
+    bytes, GB/s on them, and what the budget costs in the layer output (relative L2 of
+    the budgeted output against the unbudgeted one, and the share of gate mass
+    dropped).  OLMoE shape at n = 8 (Markov p = 0.5, 8 layers) and the DeepSeek-V3
+    shape with a 32-node draft tree (2 layers)."""
+    import torch
+
+    from moe_speculative_decoding_amd import _lib as L
+    from moe_speculative_decoding_amd.layer import (DeviceLayer, VerifyBuffers, to_device,
+                                                    verify_layer, verify_layer_budget)
+    from synth import make_case
+    from synth.configs import DSV3, OLMOE
+    from synth.gen import device_layer_weights
+
+    stream = torch.cuda.current_stream()
+    plan = ((OLMOE, 8, "markov:0.5", 8, False, (8, 16, 24)),
+            (DSV3, 2, "markov:0.5", 32, True, (32, 64)))
+    out = {}
+    for cfg, nl, routing, n, tree, budgets in plan:
+        layers = [DeviceLayer(cfg.E, cfg.K, cfg.d, cfg.f, cfg.S, cfg.w_dtype, cfg.x_dtype,
+                              device_layer_weights(cfg, seed=0, layer=l, device=dev))
+                  for l in range(nl)]
+        ops = []
+        for l in range(nl):
+            case = make_case(cfg, n, routing, seed=0, window=l, layer=l, tree=tree)
+            ops.append((l, to_device(case.x, dev), to_device(case.logits, dev),
+                        VerifyBuffers(layers[l], n, dev)))
+
+        def timed(call):
+            for op in ops:
+                call(*op)
+            torch.cuda.synchronize()
+            for (_, _, _, b) in ops:
+                if L.moe_get_error(b.ws) != L.MOE_OK:
+                    raise RuntimeError("device error word set (%s n=%d)" % (cfg.name, n))
+            outs = [b.out[:n].double().cpu() for (_, _, _, b) in ops]
+            gates = [b.gates[:n].double().cpu() for (_, _, _, b) in ops]
+            byt = sum(b.bytes.cpu().tolist()[0] for (_, _, _, b) in ops) / nl
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(stream)
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    for op in ops:
+                        call(*op)
+            stream.wait_stream(st)
+            torch.cuda.synchronize()
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / (reps * nl)
+            del g
+            return t, byt, outs, gates
+
+        t0, b0, ref_out, ref_g = timed(
+            lambda l, x, lg, b: verify_layer(layers[l], b, x, lg, n, L.MOE_MODE_DEDUP))
+        base = "%s %s n=%d%s" % (cfg.name, routing, n, " tree" if tree else "")
+        out[base + " no budget"] = {"union_MB": round(b0 / 1e6, 1), "us": round(1e6 * t0, 2),
+                                    "GBs_union": round(b0 / t0 / 1e9, 1)}
+        log("budget %s: %s" % (base, json.dumps(out[base + " no budget"])))
+        for C in budgets:
+            kept_mass = []
+
+            def call(l, x, lg, b, C=C):
+                verify_layer_budget(layers[l], b, x, lg, n, C, True)
+
+            t, byt, outs, _ = timed(call)
+            # the dropped share of gate mass, from the unbudgeted gates and the kept slots
+            for (l, _, _, b) in ops:
+                keep = (b.slot_rank[:n * cfg.K].cpu() >= 0).reshape(n, cfg.K).double()
+                kept_mass.append(float((ref_g[l] * keep).sum() / ref_g[l].sum()))
+            dev_rel = [float(torch.linalg.norm(o - r) / torch.linalg.norm(r))
+                       for o, r in zip(outs, ref_out)]
+            key = "%s C=%d" % (base, C)
+            out[key] = {"union_MB": round(byt / 1e6, 1), "us": round(1e6 * t, 2),
+                        "GBs_union": round(byt / t / 1e9, 1),
+                        "speedup_vs_no_budget": round(t0 / t, 3),
+                        "gate_mass_dropped": round(1.0 - sum(kept_mass) / len(kept_mass), 4),
+                        "out_rel_l2_vs_no_budget": round(sum(dev_rel) / len(dev_rel), 4)}
+            log("budget %s: %s" % (key, json.dumps(out[key])))
+        del ops, layers
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -565,6 +656,7 @@ def main():
         log("cold (event-timed, includes ~6 us of dispatch): %s" % json.dumps(cold))
 
     shapes = None if args.no_shapes else shape_sweep(dev)
+    budget = None if args.no_shapes else budget_sweep(dev)
 
     cpu = None if args.no_cpu else cpu_baseline(cfg, args.p, args.cpu_seconds)
 
@@ -581,6 +673,7 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "fit": fit,
         "dispatch": dispatch, "draft_length": draft, "selection": selection,
         "shapes": shapes,
+        "budget": budget,
     }
     if cold is not None:
         line["cold"] = cold
