@@ -14,3 +14,4 @@ from .ecospec_ref import (  # noqa: F401,E402
     cumulative_probability, ecospec_select, path_footprints,
 )
 from .budget_ref import apply_budget, expert_scores, kept_experts, verify_op_budget  # noqa: F401,E402
+from .bellman_ref import accept_probs, bellman_policy, expected_cost  # noqa: F401,E402

@@ -358,3 +358,31 @@ def predicted_sets(nodes: int, layers: int, experts: int, k: int, seed: int, par
             s.update((l, int(e)) for e in keep + fill)
         out.append(s)
     return out
+
+
+def reference_sequence_inputs(N: int, L: int, seed: int, E: int = 128, K: int = 8):
+    """Inputs of the draft-length oracle over a reference sequence of N tokens:
+    q [N] float64, the draft model's probability of each reference token given
+    its prefix (runs of easy and hard text: Beta draws whose parameters switch
+    every 8-40 tokens), and cost [N][L][L+1] float64 in ms, Cost(i, k, a) of a
+    step at position i with k drafts of which a are accepted: a draft part
+    linear in k plus a target part linear in the unique experts the k+1
+    positions activate (independent routing of E experts, K per token, more
+    for the rejected tail) and in the prefix length.  Coefficients are
+    arbitrary, of the order of a 30B-parameter MoE on one GPU."""
+    g = np.random.default_rng([seed, 7004, N, L])
+    q = np.empty(N)
+    i = 0
+    while i < N:
+        run = int(g.integers(8, 41))
+        a, b = (8.0, 1.5) if g.random() < 0.5 else (1.5, 2.5)
+        q[i:i + run] = g.beta(a, b, size=min(run, N - i))
+        i += run
+    k = np.arange(1, L + 1, dtype=np.float64)[None, :, None]
+    a = np.arange(L + 1, dtype=np.float64)[None, None, :]
+    pos = np.arange(N, dtype=np.float64)[:, None, None]
+    u_mean = E * (1.0 - (1.0 - K / E) ** (k + 1))
+    junk = np.maximum(k - a, 0.0)
+    U = u_mean * (1.0 + 0.05 * g.standard_normal((N, L, L + 1))) + 0.5 * junk
+    cost = (0.459 * k + 0.073) + 11.0 + 0.06 * U + 2e-4 * (512 + pos)
+    return q, cost
