@@ -308,6 +308,29 @@ moe_status moe_ecospec_select(const int32_t* parent, const float* q, const uint6
                               double eps, int32_t* selected, uint64_t* buffer_out, void* ws,
                               size_t ws_bytes, moe_stream_t stream);
 
+/* Offline Bellman policy of draft lengths over a reference sequence ("The
+ * Limits of Speculation: Bounding Speculative Decoding in MoE", Sec. 4.1-4.3,
+ * Eqs. (7)-(8)): from position i a step drafts k tokens (1 <= k <= L),
+ * accepts a of them with P(a | k) = (prod_{j<a} p_j)(1 - p_a) (a < k) or
+ * prod_{j<k} p_j (a = k), costs Cost(i, k, a) and moves to min(i + a + 1, N);
+ *   dp[i] = min_k sum_{a=0..k} P(a | k) (Cost(i, k, a) + dp[min(i + a + 1, N)]),
+ * dp[N] = 0, by backward induction.
+ *   q      (device) f64 [N]: q[m] = the draft model's probability of reference
+ *          token m + 1 given the prefix up to m, in [0, 1]; p_j at position i
+ *          is q[i + j], and 0 past the end of the sequence
+ *   cost   (device) f64 [N][L][L+1]: cost[i][k-1][a] = Cost(i, k, a), finite
+ *   dp     (device) f64 [N+1]: minimum expected remaining cost from each position
+ *   k_best (device) int32 [N]: the minimising draft length (equal expected
+ *          costs: the shorter draft)
+ *   ws     workspace (>= 256 bytes, 256-aligned) for the error word.
+ * Each product and sum is one float64 operation, in the equations' order (j
+ * and a ascending), so results are deterministic.  1 <= N <= 2^22,
+ * 1 <= L <= 32.  Errors: MOE_ERR_ARG on the host; q outside [0, 1] or a
+ * non-finite cost records MOE_ERR_BAD_TREE (moe_get_error). */
+moe_status moe_bellman_policy(const double* q, const double* cost, int32_t N, int32_t L,
+                              double* dp, int32_t* k_best, void* ws, size_t ws_bytes,
+                              moe_stream_t stream);
+
 /* Bytes of workspace any FFN or layer call needs for passes of up to n_max
  * tokens (0 for an invalid shape). */
 size_t moe_workspace_size(const moe_shape* shape, int32_t n_max, int32_t mode);

@@ -76,6 +76,7 @@ _SIG = {
     "moe_evict_select": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_ecospec_select": (_I, [_P, _P, _P, _P, _I, _I, _I, C.c_double, _P, _P, _P, C.c_size_t,
                                 _P]),
+    "moe_bellman_policy": (_I, [_P, _P, _I, _I, _P, _P, _P, C.c_size_t, _P]),
     "moe_workspace_size": (C.c_size_t, [C.POINTER(moe_shape), _I, _I]),
     "moe_workspace_init": (_I, [_P, C.c_size_t, _P]),
     "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
@@ -219,6 +220,11 @@ def moe_ecospec_select(parent, q, pred, buffer0, N, W, gamma, eps, selected, buf
     _check(lib.moe_ecospec_select(ptr(parent), ptr(q), ptr(pred), ptr(buffer0), N, W, gamma,
                                   float(eps), ptr(selected), ptr(buffer_out), ptr(ws), ws_bytes,
                                   _stream(stream)), "moe_ecospec_select")
+
+
+def moe_bellman_policy(q, cost, N, L_, dp, k_best, ws, ws_bytes, stream=None) -> None:
+    _check(lib.moe_bellman_policy(ptr(q), ptr(cost), N, L_, ptr(dp), ptr(k_best), ptr(ws),
+                                  ws_bytes, _stream(stream)), "moe_bellman_policy")
 
 
 def moe_workspace_size(shape: moe_shape, n_max: int, mode: int) -> int:

@@ -15,6 +15,8 @@ constexpr int kMaxN = 32, kMaxK = 8, kMaxE = 256, kMaxS = 4, kMaxDim = 65536;
 constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxSetWords = 256;          // 64-bit words of one (layer, expert) set
 constexpr int kMaxTreeSetWords = 8192;     // N * W: the footprints fit 64 KB of LDS
+constexpr int kMaxSequence = 1 << 22;      // positions of a Bellman reference sequence
+constexpr int kMaxDraftLength = 32;        // draft lengths of the Bellman policy (one lane each)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -438,6 +440,19 @@ moe_status moe_ecospec_select(const int32_t* parent, const float* q, const uint6
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_ecospec(parent, q, pred, buffer0, N, W, gamma, eps, selected,
                                         buffer_out, static_cast<uint32_t*>(ws),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_bellman_policy(const double* q, const double* cost, int32_t N, int32_t L,
+                              double* dp, int32_t* k_best, void* ws, size_t ws_bytes,
+                              moe_stream_t stream) {
+  if (N < 1 || N > kMaxSequence || L < 1 || L > kMaxDraftLength) return MOE_ERR_ARG;
+  const void* need8[3] = {q, cost, dp};
+  for (const void* p : need8)
+    if (p == nullptr || !aligned(p, 8)) return MOE_ERR_ARG;
+  if (k_best == nullptr || !aligned(k_best, 4)) return MOE_ERR_ARG;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_bellman(q, cost, N, L, dp, k_best, static_cast<uint32_t*>(ws),
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -174,6 +174,8 @@ hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t*
 hipError_t launch_evict(const int32_t* parent, const float* q, const float* cost, int N,
                         int32_t* order, double* scores, double* expected, int32_t* k_best,
                         uint32_t* err, hipStream_t s);
+hipError_t launch_bellman(const double* q, const double* cost, int N, int L, double* dp,
+                          int32_t* k_best, uint32_t* err, hipStream_t s);
 hipError_t launch_decode_fp8(const uint8_t* codes, float* out, long long count, hipStream_t s);
 
 }  // namespace moe

@@ -283,4 +283,128 @@ hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t*
   return hipGetLastError();
 }
 
+
+// ----------------------------------------------------- Bellman draft lengths
+// "The Limits of Speculation: Bounding Speculative Decoding in MoE", Sec. 4:
+// over a reference sequence of N tokens, dp[i] = min_k sum_{a=0..k}
+// P(a | k) (Cost(i, k, a) + dp[min(i + a + 1, N)]) with dp[N] = 0 (Eq. (8)),
+// P(a | k) = (prod_{j<a} p_j)(1 - p_a) for a < k, P(k | k) = prod_{j<k} p_j
+// (Eq. (7)), p_j = q[i + j] (0 past the end).  Backward induction is a chain
+// of N dependent steps, so one wavefront runs it: lane k - 1 evaluates draft
+// length k, the window's q values and the dp values ahead ride in two
+// register rings (lane j holds q[i + j] and dp[i + 1 + j]; a step shifts
+// them up one lane), and a butterfly picks the smallest expected cost (equal
+// costs: the shorter draft).  Every product and sum is a separately rounded
+// float64 operation in the order of the equations (a ascending), so dp and
+// the policy are reproducible bit for bit.  The other three wavefronts stage
+// the next block of cost rows and q values into LDS while wavefront 0 works
+// through the current one.
+constexpr int kBellmanBlock = 256;
+constexpr int kBellmanCostLds = 2048;  // doubles of cost rows per staging buffer
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long b = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(b), lane);
+  const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(b >> 32), lane);
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+__global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __restrict__ q,
+                                                                const double* __restrict__ cost,
+                                                                int N, int L,
+                                                                double* __restrict__ dp_out,
+                                                                int32_t* __restrict__ k_out,
+                                                                uint32_t* __restrict__ err) {
+#pragma clang fp contract(off)  // every product and sum rounded on its own, as the equations read
+  __shared__ double cst[2][kBellmanCostLds];
+  __shared__ double qs[2][kBellmanCostLds / 2];
+  __shared__ int bad;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rowd = L * (L + 1);
+  const int T = kBellmanCostLds / rowd > 1 ? kBellmanCostLds / rowd : 1;
+  const int nb = (N + T - 1) / T;
+  if (tid == 0) {
+    bad = 0;
+    dp_out[N] = 0.0;
+  }
+  __syncthreads();
+  // block b holds positions [lo, hi), hi = N - b T; threads [t0, t0 + nt) stage it
+  auto stage = [&](int b, int t0, int nt) {
+    const int hi = N - b * T, lo = hi - T > 0 ? hi - T : 0;
+    const int buf = b & 1;
+    const int cnt = (hi - lo) * rowd;
+    int flag = 0;
+    for (int x = tid - t0; x < cnt; x += nt) {
+      const double v = cost[static_cast<size_t>(lo) * rowd + x];
+      flag |= !__builtin_isfinite(v);
+      cst[buf][x] = v;
+    }
+    for (int x = tid - t0; x < hi - lo; x += nt) {
+      const double v = q[lo + x];
+      flag |= !(v >= 0.0 && v <= 1.0);
+      qs[buf][x] = v;
+    }
+    if (flag) bad = 1;
+  };
+  stage(0, 0, kBellmanBlock);
+  __syncthreads();
+
+  double qr = 0.0;   // lane j: q[i + j]      (0 at and past N)
+  double dpr = 0.0;  // lane j: dp[i + 1 + j] (dp[N] = 0, and 0 stands for the capped states)
+  const int k = lane + 1;
+  for (int b = 0; b < nb; ++b) {
+    if (wave != 0) {
+      if (b + 1 < nb) stage(b + 1, kWave, kBellmanBlock - kWave);
+    } else {
+      const int hi = N - b * T, lo = hi - T > 0 ? hi - T : 0;
+      const int buf = b & 1;
+      for (int i = hi - 1; i >= lo; --i) {
+        const double qin = qs[buf][i - lo];
+        qr = __shfl_up(qr, 1);
+        if (lane == 0) qr = qin;
+        const double* crow = &cst[buf][(i - lo) * rowd + (k - 1) * (L + 1)];
+        double acc = 0.0, pre = 1.0;
+        for (int a = 0; a <= L; ++a) {
+          const double pa = readlane_f64(qr, a);
+          const double da = readlane_f64(dpr, a);
+          if (k <= L && a <= k) {
+            double P = pre;
+            if (a < k) {
+              P = pre * (1.0 - pa);
+              pre = pre * pa;
+            }
+            acc = acc + P * (crow[a] + da);  // not fused: contraction is off here
+          }
+        }
+        // smallest expected cost over the lanes; equal costs: the shorter draft
+        double v = k <= L ? acc : __longlong_as_double(0x7ff0000000000000ll);
+        int kk = k <= L ? k : 1 << 20;
+        for (int o = 32; o >= 1; o >>= 1) {
+          const double v2 = __shfl_xor(v, o);
+          const int k2 = __shfl_xor(kk, o);
+          if (v2 < v || (v2 == v && k2 < kk)) {
+            v = v2;
+            kk = k2;
+          }
+        }
+        dpr = __shfl_up(dpr, 1);
+        if (lane == 0) {
+          dpr = v;
+          dp_out[i] = v;
+          k_out[i] = kk;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0 && bad) atomicOr(err, ERRBIT_BAD_TREE);
+}
+
+hipError_t launch_bellman(const double* q, const double* cost, int N, int L, double* dp,
+                          int32_t* k_best, uint32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(bellman_kernel, dim3(1), dim3(kBellmanBlock), 0, s, q, cost, N, L, dp,
+                     k_best, err);
+  return hipGetLastError();
+}
+
 }  // namespace moe

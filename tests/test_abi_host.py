@@ -209,6 +209,23 @@ def test_budget_validation_before_launch():
     assert lcall(a8=L.MOE_FP8_E4M3) == L.MOE_ERR_UNSUPPORTED
 
 
+def test_bellman_validation_before_launch():
+    bp = L.lib.moe_bellman_policy
+    base = [FAKE, FAKE, 100, 8, FAKE, FAKE, FAKE, 256, None]
+    def call(**chg):
+        a = list(base)
+        for k, v in chg.items():
+            a[int(k[1:])] = v
+        return bp(*a)
+    assert call(a2=0) == L.MOE_ERR_ARG                   # N
+    assert call(a3=0) == L.MOE_ERR_ARG                   # L
+    assert call(a3=33) == L.MOE_ERR_ARG
+    assert call(a0=FAKE + 4) == L.MOE_ERR_ARG            # q must be 8-aligned
+    assert call(a4=None) == L.MOE_ERR_ARG
+    assert call(a5=FAKE + 2) == L.MOE_ERR_ARG
+    assert call(a7=255) == L.MOE_ERR_WORKSPACE
+
+
 def test_evict_validation_before_launch():
     ev = L.lib.moe_evict_select
     base = [FAKE, FAKE, FAKE, 16, FAKE, None, None, FAKE, FAKE, 256, None]

@@ -1,0 +1,79 @@
+"""GPU parity of the Bellman draft-length policy ("The Limits of Speculation:
+Bounding Speculative Decoding in MoE", Sec. 4, Eqs. (7)-(8)) against the
+oracle, through the C ABI.
+
+Both sides evaluate every product and sum as one float64 operation in the
+equations' order, so dp and the policy are compared bit for bit.  Cases:
+synthetic reference sequences (runs of easy and hard text) for several draft
+limits, sequences shorter and longer than one staging block of the kernel,
+the closed forms of always- and never-accepted drafts, and invalid inputs
+(recorded in the error word).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth.gen import reference_sequence_inputs
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from moe_speculative_decoding_amd import _lib as L  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def run(q, cost, L_):
+    N = len(q)
+    dq = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64)).to(DEV)
+    dc = torch.from_numpy(np.ascontiguousarray(cost, dtype=np.float64)).to(DEV)
+    dp = torch.full((N + 1,), -1.0, dtype=torch.float64, device=DEV)
+    kb = torch.full((N,), -1, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    L.moe_bellman_policy(dq, dc, N, L_, dp, kb, ws, 256)
+    torch.cuda.synchronize()
+    return dp.cpu().numpy(), kb.cpu().numpy(), L.moe_get_error(ws)
+
+
+@pytest.mark.parametrize("N,L_,seed", [
+    (1, 1, 0), (7, 3, 1), (200, 8, 2), (300, 12, 3), (97, 32, 4), (1000, 4, 5), (513, 1, 6),
+])
+def test_bellman_matches_oracle(N, L_, seed):
+    print("bellman N=%d L=%d seed=%d" % (N, L_, seed), flush=True)
+    q, cost = reference_sequence_inputs(N, L_, seed)
+    ref_dp, ref_pol = oracle.bellman_policy(q, cost, L_)
+    dp, pol, err = run(q, cost, L_)
+    assert err == L.MOE_OK
+    assert np.array_equal(dp, ref_dp)
+    assert np.array_equal(pol, ref_pol)
+
+
+def test_bellman_closed_forms():
+    N, L_ = 40, 5
+    q = np.ones(N)
+    cost = np.full((N, L_, L_ + 1), 2.5)
+    dp, pol, err = run(q, cost, L_)
+    assert err == L.MOE_OK
+    assert np.array_equal(dp, np.array([2.5 * -(-(N - i) // (L_ + 1)) for i in range(N + 1)]))
+    q0 = np.zeros(N)
+    cost0 = np.array([[[0.5 * k + 3.0] * (L_ + 1) for k in range(1, L_ + 1)] for _ in range(N)])
+    dp0, pol0, err0 = run(q0, cost0, L_)
+    assert err0 == L.MOE_OK and np.all(pol0 == 1)
+    assert np.allclose(dp0, [(N - i) * 3.5 for i in range(N + 1)], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bad", ["q_above_one", "q_nan", "cost_inf"])
+def test_bellman_rejects_invalid_inputs_on_device(bad):
+    N, L_ = 30, 4
+    q, cost = reference_sequence_inputs(N, L_, 9)
+    if bad == "q_above_one":
+        q[17] = 1.5
+    elif bad == "q_nan":
+        q[3] = np.nan
+    else:
+        cost[29, 2, 1] = np.inf
+    _, _, err = run(q, cost, L_)
+    assert err == L.MOE_ERR_BAD_TREE
