@@ -621,6 +621,19 @@ def main():
                              for _ in range(8)])
         selection["ecospec_N%d_L%d_E%d_g%d_us" % (N, nl, ne, gamma)] = round(1e6 * time_graph(g, 8), 2)
         del g
+    # offline Bellman draft-length policy over a reference sequence
+    from synth.gen import reference_sequence_inputs
+    for N, Lmax in ((2048, 8), (2048, 12)):
+        qv, cv = reference_sequence_inputs(N, Lmax, 0)
+        d_q = torch.from_numpy(qv).to(dev)
+        d_c = torch.from_numpy(cv).to(dev)
+        dpv = torch.empty(N + 1, dtype=torch.float64, device=dev)
+        kbv = torch.empty(N, dtype=torch.int32, device=dev)
+        g = capture(lambda: [L.moe_bellman_policy(d_q, d_c, N, Lmax, dpv, kbv, sel_ws, 256)])
+        t = time_graph(g, 1)
+        del g
+        selection["bellman_N%d_L%d_us" % (N, Lmax)] = round(1e6 * t, 1)
+        selection["bellman_N%d_L%d_mean_k" % (N, Lmax)] = round(float(kbv.double().mean()), 3)
     if L.moe_get_error(sel_ws) != L.MOE_OK:
         raise RuntimeError("selection kernels set the error word")
     log("selection: %s" % json.dumps(selection))

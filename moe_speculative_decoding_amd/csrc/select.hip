@@ -291,14 +291,16 @@ hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t*
 // P(a | k) = (prod_{j<a} p_j)(1 - p_a) for a < k, P(k | k) = prod_{j<k} p_j
 // (Eq. (7)), p_j = q[i + j] (0 past the end).  Backward induction is a chain
 // of N dependent steps, so one wavefront runs it: lane k - 1 evaluates draft
-// length k, the window's q values and the dp values ahead ride in two
-// register rings (lane j holds q[i + j] and dp[i + 1 + j]; a step shifts
-// them up one lane), and a butterfly picks the smallest expected cost (equal
-// costs: the shorter draft).  Every product and sum is a separately rounded
-// float64 operation in the order of the equations (a ascending), so dp and
-// the policy are reproducible bit for bit.  The other three wavefronts stage
-// the next block of cost rows and q values into LDS while wavefront 0 works
-// through the current one.
+// length k from its cost row (read from LDS into registers at the start of
+// the step), the q values and dp values ahead live in two 64-lane register
+// rings (position m at lane m mod 64; a step writes one lane of each and
+// broadcasts the others with readlane; lanes of positions at or past N hold
+// 0), and the smallest expected cost comes from a DPP minimum and a ballot
+// (equal costs: the lowest lane, the shorter draft).  Every product and sum is
+// a separately rounded float64 operation in the order of the equations (a
+// ascending), so dp and the policy are reproducible bit for bit.  The other
+// three wavefronts stage the next block of cost rows and q values into LDS
+// while wavefront 0 works through the current one.
 constexpr int kBellmanBlock = 256;
 constexpr int kBellmanCostLds = 2048;  // doubles of cost rows per staging buffer
 
@@ -308,7 +310,30 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(b >> 32), lane);
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
+// v in lane `lane` (uniform), old elsewhere
+__device__ __forceinline__ double writelane_f64(double v, int lane, double old) {
+  return static_cast<int>(threadIdx.x & (kWave - 1)) == lane ? v : old;
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = __double_as_longlong(v);
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<unsigned>(b)), CTRL, 0xF, 0xF, false));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<unsigned>(b >> 32)), CTRL, 0xF, 0xF, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+// minimum over the wavefront (no NaN): DPP inside rows of 16, then the rows
+__device__ __forceinline__ double wave_min_f64(double v) {
+  v = fmin(v, dpp_f64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmin(v, dpp_f64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmin(v, dpp_f64<0x141>(v));  // row_half_mirror
+  v = fmin(v, dpp_f64<0x140>(v));  // row_mirror
+  return fmin(fmin(readlane_f64(v, 0), readlane_f64(v, 16)),
+              fmin(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
 
+template <int LM>  // L <= LM: the cost row of a lane fits LM + 1 registers
 __global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __restrict__ q,
                                                                 const double* __restrict__ cost,
                                                                 int N, int L,
@@ -349,9 +374,11 @@ __global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __
   stage(0, 0, kBellmanBlock);
   __syncthreads();
 
-  double qr = 0.0;   // lane j: q[i + j]      (0 at and past N)
-  double dpr = 0.0;  // lane j: dp[i + 1 + j] (dp[N] = 0, and 0 stands for the capped states)
+  const double inf = __longlong_as_double(0x7ff0000000000000ll);
+  double qr = 0.0;   // lane m % 64: q[m]   (0 at and past N)
+  double dpr = 0.0;  // lane m % 64: dp[m]  (dp[N] = 0; 0 past N stands for the capped states)
   const int k = lane + 1;
+  const bool act = k <= L;
   for (int b = 0; b < nb; ++b) {
     if (wave != 0) {
       if (b + 1 < nb) stage(b + 1, kWave, kBellmanBlock - kWave);
@@ -359,38 +386,33 @@ __global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __
       const int hi = N - b * T, lo = hi - T > 0 ? hi - T : 0;
       const int buf = b & 1;
       for (int i = hi - 1; i >= lo; --i) {
-        const double qin = qs[buf][i - lo];
-        qr = __shfl_up(qr, 1);
-        if (lane == 0) qr = qin;
         const double* crow = &cst[buf][(i - lo) * rowd + (k - 1) * (L + 1)];
+        double c[LM + 1];
+#pragma unroll
+        for (int a = 0; a <= LM; ++a) c[a] = (act && a <= k) ? crow[a] : 0.0;
+        qr = writelane_f64(qs[buf][i - lo], i & 63, qr);
         double acc = 0.0, pre = 1.0;
-        for (int a = 0; a <= L; ++a) {
-          const double pa = readlane_f64(qr, a);
-          const double da = readlane_f64(dpr, a);
-          if (k <= L && a <= k) {
-            double P = pre;
-            if (a < k) {
-              P = pre * (1.0 - pa);
-              pre = pre * pa;
+#pragma unroll
+        for (int a = 0; a <= LM; ++a) {
+          if (a <= L) {
+            const double pa = readlane_f64(qr, (i + a) & 63);
+            const double da = readlane_f64(dpr, (i + 1 + a) & 63);
+            if (act && a <= k) {
+              double P = pre;
+              if (a < k) {
+                P = pre * (1.0 - pa);
+                pre = pre * pa;
+              }
+              acc = acc + P * (c[a] + da);  // not fused: contraction is off here
             }
-            acc = acc + P * (crow[a] + da);  // not fused: contraction is off here
           }
         }
-        // smallest expected cost over the lanes; equal costs: the shorter draft
-        double v = k <= L ? acc : __longlong_as_double(0x7ff0000000000000ll);
-        int kk = k <= L ? k : 1 << 20;
-        for (int o = 32; o >= 1; o >>= 1) {
-          const double v2 = __shfl_xor(v, o);
-          const int k2 = __shfl_xor(kk, o);
-          if (v2 < v || (v2 == v && k2 < kk)) {
-            v = v2;
-            kk = k2;
-          }
-        }
-        dpr = __shfl_up(dpr, 1);
+        const double v = act ? acc : inf;
+        const double vmin = wave_min_f64(v);
+        const int kk = __ffsll(static_cast<unsigned long long>(__ballot(act && v == vmin)));
+        dpr = writelane_f64(vmin, i & 63, dpr);
         if (lane == 0) {
-          dpr = v;
-          dp_out[i] = v;
+          dp_out[i] = vmin;
           k_out[i] = kk;
         }
       }
@@ -402,8 +424,15 @@ __global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __
 
 hipError_t launch_bellman(const double* q, const double* cost, int N, int L, double* dp,
                           int32_t* k_best, uint32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(bellman_kernel, dim3(1), dim3(kBellmanBlock), 0, s, q, cost, N, L, dp,
-                     k_best, err);
+  if (L <= 8)
+    hipLaunchKernelGGL(bellman_kernel<8>, dim3(1), dim3(kBellmanBlock), 0, s, q, cost, N, L, dp,
+                       k_best, err);
+  else if (L <= 16)
+    hipLaunchKernelGGL(bellman_kernel<16>, dim3(1), dim3(kBellmanBlock), 0, s, q, cost, N, L, dp,
+                       k_best, err);
+  else
+    hipLaunchKernelGGL(bellman_kernel<32>, dim3(1), dim3(kBellmanBlock), 0, s, q, cost, N, L, dp,
+                       k_best, err);
   return hipGetLastError();
 }
 
