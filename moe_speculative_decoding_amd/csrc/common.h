@@ -124,10 +124,10 @@ struct LayerParams {
 // Tile shapes of the FFN phases (rows per wave R, load steps per chunk SPC
 // for UP and DOWN); the defaults are the measured best on MI355X.
 #ifndef MOE_TUNE_RU
-#define MOE_TUNE_RU 2
+#define MOE_TUNE_RU 1
 #endif
 #ifndef MOE_TUNE_SPCU
-#define MOE_TUNE_SPCU 2
+#define MOE_TUNE_SPCU 4
 #endif
 #ifndef MOE_TUNE_RD
 #define MOE_TUNE_RD 4

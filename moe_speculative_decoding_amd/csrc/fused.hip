@@ -118,9 +118,10 @@ void layer_kernel(LayerParams lp) {
   RouteLds& rl = *reinterpret_cast<RouteLds*>(xs);
   float* lg = reinterpret_cast<float*>(xs + kRouteLogitsOffset);
   // the call's tag (workspace epoch + 1) travels with the logits: it is final
-  // before the launch (the previous call advanced it before it ended)
+  // before the launch (the previous call advanced it before it ended); every
+  // wavefront loads it, so no wavefront's logits wait behind it
   __shared__ unsigned tag_l;
-  if (tid == 0) tag_l = coh_load_u32(lp.epoch) + 1u;
+  const unsigned tag_v = coh_load_u32(lp.epoch);  // one request per wavefront
   {
     // eight loads per lane in flight at once (clamped in bounds), then the stores
     constexpr int kPer = 8;
@@ -134,6 +135,7 @@ void layer_kernel(LayerParams lp) {
         if (base + i * kStreamBlock + tid < words) lg[base + i * kStreamBlock + tid] = v[i];
     }
   }
+  if (tid == 0) tag_l = tag_v + 1u;
   __syncthreads();
   TopkLds* tk = reinterpret_cast<TopkLds*>(xs + kRouteTopkOffset);
   for (int t = wave; t < n; t += kStreamWaves) {
