@@ -292,11 +292,11 @@ hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t*
 // (Eq. (7)), p_j = q[i + j] (0 past the end).  Backward induction is a chain
 // of N dependent steps, so one wavefront runs it: lane k - 1 evaluates draft
 // length k from its cost row (read from LDS into registers at the start of
-// the step), the q values and dp values ahead live in two 64-lane register
-// rings (position m at lane m mod 64; a step writes one lane of each and
-// broadcasts the others with readlane; lanes of positions at or past N hold
-// 0), and the smallest expected cost comes from a DPP minimum and a ballot
-// (equal costs: the lowest lane, the shorter draft).  Every product and sum is
+// the step); the q values and dp values ahead sit in register windows that
+// every lane holds alike (a step shifts them by one), so the products of
+// Eq. (7) need no cross-lane traffic, and the smallest expected cost comes
+// from a DPP minimum and a ballot (equal costs: the lowest lane, the shorter
+// draft).  Every product and sum is
 // a separately rounded float64 operation in the order of the equations (a
 // ascending), so dp and the policy are reproducible bit for bit.  The other
 // three wavefronts stage the next block of cost rows and q values into LDS
@@ -309,10 +309,6 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(b), lane);
   const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(b >> 32), lane);
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
-}
-// v in lane `lane` (uniform), old elsewhere
-__device__ __forceinline__ double writelane_f64(double v, int lane, double old) {
-  return static_cast<int>(threadIdx.x & (kWave - 1)) == lane ? v : old;
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
@@ -375,8 +371,14 @@ __global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __
   __syncthreads();
 
   const double inf = __longlong_as_double(0x7ff0000000000000ll);
-  double qr = 0.0;   // lane m % 64: q[m]   (0 at and past N)
-  double dpr = 0.0;  // lane m % 64: dp[m]  (dp[N] = 0; 0 past N stands for the capped states)
+  // windows ahead of position i, the same in every lane: qw[a] = q[i + a]
+  // (p_a), dw[a] = dp[i + 1 + a]; positions at or past N hold 0 (dp[N] = 0,
+  // and min(i + a + 1, N) = N there).  A step shifts both by one.
+  double qw[LM], dw[LM + 1];
+#pragma unroll
+  for (int a = 0; a < LM; ++a) qw[a] = 0.0;
+#pragma unroll
+  for (int a = 0; a <= LM; ++a) dw[a] = 0.0;
   const int k = lane + 1;
   const bool act = k <= L;
   for (int b = 0; b < nb; ++b) {
@@ -390,27 +392,32 @@ __global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __
         double c[LM + 1];
 #pragma unroll
         for (int a = 0; a <= LM; ++a) c[a] = (act && a <= k) ? crow[a] : 0.0;
-        qr = writelane_f64(qs[buf][i - lo], i & 63, qr);
-        double acc = 0.0, pre = 1.0;
+#pragma unroll
+        for (int a = LM - 1; a > 0; --a) qw[a] = qw[a - 1];
+        qw[0] = qs[buf][i - lo];
+        // Eq. (7) along the window (the same in every lane): pre_a = prod_{j<a}
+        // p_j, and P(a | k) = pre_a (1 - p_a) for a < k, pre_k for a = k
+        double pre[LM + 1], stop[LM];
+        pre[0] = 1.0;
+#pragma unroll
+        for (int a = 0; a < LM; ++a) {
+          stop[a] = pre[a] * (1.0 - qw[a]);
+          pre[a + 1] = pre[a] * qw[a];
+        }
+        // Eq. (8) for draft length k = lane + 1, a ascending
+        double acc = 0.0;
 #pragma unroll
         for (int a = 0; a <= LM; ++a) {
-          if (a <= L) {
-            const double pa = readlane_f64(qr, (i + a) & 63);
-            const double da = readlane_f64(dpr, (i + 1 + a) & 63);
-            if (act && a <= k) {
-              double P = pre;
-              if (a < k) {
-                P = pre * (1.0 - pa);
-                pre = pre * pa;
-              }
-              acc = acc + P * (c[a] + da);  // not fused: contraction is off here
-            }
-          }
+          const double P = a < k ? (a < LM ? stop[a] : 0.0) : pre[a];
+          const double t = acc + P * (c[a] + dw[a]);  // not fused: contraction is off here
+          acc = (act && a <= k) ? t : acc;
         }
         const double v = act ? acc : inf;
         const double vmin = wave_min_f64(v);
         const int kk = __ffsll(static_cast<unsigned long long>(__ballot(act && v == vmin)));
-        dpr = writelane_f64(vmin, i & 63, dpr);
+#pragma unroll
+        for (int a = LM; a > 0; --a) dw[a] = dw[a - 1];
+        dw[0] = vmin;
         if (lane == 0) {
           dp_out[i] = vmin;
           k_out[i] = kk;
@@ -424,7 +431,10 @@ __global__ __launch_bounds__(kBellmanBlock) void bellman_kernel(const double* __
 
 hipError_t launch_bellman(const double* q, const double* cost, int N, int L, double* dp,
                           int32_t* k_best, uint32_t* err, hipStream_t s) {
-  if (L <= 8)
+  if (L <= 4)
+    hipLaunchKernelGGL(bellman_kernel<4>, dim3(1), dim3(kBellmanBlock), 0, s, q, cost, N, L, dp,
+                       k_best, err);
+  else if (L <= 8)
     hipLaunchKernelGGL(bellman_kernel<8>, dim3(1), dim3(kBellmanBlock), 0, s, q, cost, N, L, dp,
                        k_best, err);
   else if (L <= 16)
