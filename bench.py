@@ -105,8 +105,14 @@ def cpu_baseline(cfg, p, budget_s):
                 total_bytes += r["union_bytes"]
             rounds += 1
     log("cpu oracle: %d rounds of n=1,2,4,8 in %.1f s" % (rounds, total_s))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": model,
             "sample": "float64 numpy oracle, dedup mode, one OLMoE-shaped layer, Markov p=%s: "
                       "the operations at n=1,2,4,8 (route+union+FFN+combine incl. weight "
                       "decode), %d rounds, %.1f s on one thread" % (p, rounds, total_s)}
