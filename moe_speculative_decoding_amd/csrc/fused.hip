@@ -151,7 +151,10 @@ void layer_kernel(LayerParams lp) {
   int U = 0;
   int mode = p.mode;
   if (mode != MODE_PERSLOT) {
-    build_union_256(ids_l, n, K, E, &U_l, mt.b, mt.a, mt.c, rl.slot_rank, rl.ul);
+    if (n == 1)  // one token: its top-K ids are distinct
+      build_union_one_token(ids_l, K, E, &U_l, mt.b, mt.a, mt.c, rl.slot_rank);
+    else
+      build_union_256(ids_l, n, K, E, &U_l, mt.b, mt.a, mt.c, rl.slot_rank, rl.ul);
     __syncthreads();
     U = uni(U_l);
   }

@@ -217,6 +217,38 @@ __device__ __forceinline__ void build_union_wave(const int32_t* ids, int nk, int
   if (lane == 0) *U_out = U;
 }
 
+// The union of one token's K slots, whose ids are distinct (the token's
+// top-K): the ids in ascending order, one slot each.  Wavefront 0 builds it
+// (the caller's next barrier publishes it); the same outputs as
+// build_union_256 for such slots.
+__device__ __forceinline__ void build_union_one_token(const int32_t* ids, int K, int E,
+                                                      int32_t* __restrict__ U_out,
+                                                      int32_t* __restrict__ union_ids,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ slot_rank) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63;
+  const bool act = lane < K;
+  const int id = act ? ids[lane] : 0;
+  if (__ballot(act && (id < 0 || id >= E))) {
+    if (lane == 0) *U_out = -1;
+    return;
+  }
+  int r = 0;  // ids below mine
+  for (int j = 0; j < K; ++j) r += __shfl(id, j) < id ? 1 : 0;
+  if (act) {
+    union_ids[r] = id;
+    offsets[r] = r;
+    perm[r] = lane;
+    slot_rank[lane] = r;
+  }
+  if (lane == 0) {
+    offsets[K] = K;
+    *U_out = K;
+  }
+}
+
 // Every thread of the workgroup calls this (it holds __syncthreads); threads
 // 0..255 do the work.  Up to 64 slots, wavefront 0 alone builds the union
 // (build_union_wave) and the caller's next barrier publishes it.
