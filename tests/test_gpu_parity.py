@@ -68,7 +68,8 @@ def test_route_topk_matches_oracle(cfg, n, routing, tree):
     assert np.all(np.abs(gates - rg) <= 1e-6 + 1e-5 * np.abs(rg))
 
 
-@pytest.mark.parametrize("n,E,K", [(32, 256, 8), (5, 8, 8), (7, 13, 3), (1, 64, 1)])
+@pytest.mark.parametrize("n,E,K", [(32, 256, 8), (5, 8, 8), (7, 13, 3), (1, 64, 1), (9, 64, 8),
+                                   (3, 37, 5), (6, 100, 7)])
 def test_route_topk_ties_nan_signed_zero(n, E, K):
     g = np.random.default_rng(E * 7 + K)
     vals = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0, np.nan, -np.inf], dtype=np.float32)
