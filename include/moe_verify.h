@@ -22,7 +22,8 @@
  *   - Pointers marked (device) are device pointers; the caller allocates and
  *     owns all memory.  The library allocates nothing and keeps no state
  *     between calls; calls on different streams with disjoint buffers may run
- *     concurrently.
+ *     concurrently, except the one-launch passes (moe_verify_layer*), which
+ *     need the whole device (see there).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream).  Outputs are valid once the stream has reached the call.
  *   - Arguments are validated on the host before anything is enqueued; an
@@ -218,6 +219,12 @@ moe_status moe_combine(const float* y_slots, const float* gates, const float* y_
  *   ws        workspace of at least moe_workspace_size(shape, n, mode) bytes,
  *             zero-filled before its first use; the call leaves its counters
  *             zero.  Calls sharing a workspace must not overlap in time.
+ * The launch fills the device (one workgroup per CU) and its workgroups wait
+ * for one another, so all of them must be resident at once: do not run it
+ * beside other kernels that hold CUs (another stream's one-launch pass
+ * included).  If a workgroup cannot start, the others' bounded waits give up
+ * and record MOE_ERR_TIMEOUT instead of hanging; the outputs are then
+ * unspecified.
  * Errors: MOE_ERR_ARG / _UNSUPPORTED / _WORKSPACE on the host; a bounded
  * device wait that gives up records MOE_ERR_TIMEOUT (moe_get_error). */
 moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const float* logits,
