@@ -115,6 +115,7 @@ def _margin_ok(ref, C, n):
     (DSV2LITE, 5, "markov:0.5", False, 6, 1),
     (OLMOE, 8, "markov:0.5", False, 16, 0),
     (OLMOE, 8, "markov:0.0", False, 24, 1),
+    (OLMOE, 1, "markov:0.5", False, 3, 1),        # one token: its top-3 with renormalised gates
 ])
 def test_budgeted_pass_matches_oracle(cfg, n, routing, tree, C, renorm):
     case = make_case(cfg, n, routing, seed=3, tree=tree)
