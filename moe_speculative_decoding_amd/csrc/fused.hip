@@ -138,13 +138,30 @@ void layer_kernel(LayerParams lp) {
   if (tid == 0) tag_l = tag_v + 1u;
   __syncthreads();
   TopkLds* tk = reinterpret_cast<TopkLds*>(xs + kRouteTopkOffset);
-  for (int t = wave; t < n; t += kStreamWaves) {
-    int id;
-    float g;
-    route_token(lg + t * E, E, K, lane, tk[wave], id, g);
-    if (lane < K) {
-      ids_l[t * K + lane] = id;
-      gates_l[t * K + lane] = g;
+  const int team = n <= kStreamWaves / 2 ? kStreamWaves / n : 1;  // wavefronts per token
+  if (team > 1) {
+    // few tokens: the idle wavefronts share the rank counts
+    const int t = wave / team, q = wave - t * team;
+    if (t < n) route_team_count(lg + t * E, E, lane, q, team, tk[wave]);
+    __syncthreads();
+    if (t < n && q == 0) {
+      int id;
+      float g;
+      route_team_select(lg + t * E, E, K, lane, tk + wave, team, id, g);
+      if (lane < K) {
+        ids_l[t * K + lane] = id;
+        gates_l[t * K + lane] = g;
+      }
+    }
+  } else {
+    for (int t = wave; t < n; t += kStreamWaves) {
+      int id;
+      float g;
+      route_token(lg + t * E, E, K, lane, tk[wave], id, g);
+      if (lane < K) {
+        ids_l[t * K + lane] = id;
+        gates_l[t * K + lane] = g;
+      }
     }
   }
   __syncthreads();

@@ -82,6 +82,7 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
 // Per-wavefront LDS scratch of the top-K.
 struct TopkLds {
   unsigned long long key[256];  // 64-bit keys of the token's experts (0 beyond E)
+  int part[256];                // a team member's partial ranks (route_team_*)
   int sel_id[8];
   float sel_l[8];
 };
@@ -96,10 +97,9 @@ struct TopkLds {
 // selected id and its gate: the softmax over the K selected logits, whose
 // first selection holds the maximum.
 template <int J>
-__device__ __forceinline__ void route_token_j(const float* __restrict__ row, int E, int K, int lane,
-                                              TopkLds& sc, int& my_id, float& my_gate) {
-  float val[J];
-  unsigned long long key[J];
+__device__ __forceinline__ void topk_keys(const float* __restrict__ row, int E, int lane,
+                                          TopkLds& sc, float (&val)[J],
+                                          unsigned long long (&key)[J]) {
 #pragma unroll
   for (int j = 0; j < J; ++j) val[j] = row[min(lane + kWave * j, E - 1)];  // all loads first
 #pragma unroll
@@ -111,11 +111,14 @@ __device__ __forceinline__ void route_token_j(const float* __restrict__ row, int
     sc.key[e] = key[j];
   }
   __builtin_amdgcn_wave_barrier();  // LDS ops of one wavefront run in order
-  int rank[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) rank[j] = 0;
+}
+
+// rank[j] += the keys of sc.key[i0 .. i1) above key[j] (i0, i1 multiples of 16)
+template <int J>
+__device__ __forceinline__ void topk_count(const TopkLds& sc, int i0, int i1,
+                                           const unsigned long long (&key)[J], int (&rank)[J]) {
 #pragma unroll 1
-  for (int i = 0; i < J * kWave; i += 16) {
+  for (int i = i0; i < i1; i += 16) {
     // eight broadcast reads (the same address in every lane) in flight at once
     u32x4 kk[8];
 #pragma unroll
@@ -128,6 +131,13 @@ __device__ __forceinline__ void route_token_j(const float* __restrict__ row, int
       for (int j = 0; j < J; ++j) rank[j] += (k0 > key[j]) + (k1 > key[j]);
     }
   }
+}
+
+// the experts of rank < K in rank order, and lane k's gate
+template <int J>
+__device__ __forceinline__ void topk_select(const float (&val)[J], const int (&rank)[J], int E,
+                                            int K, int lane, TopkLds& sc, int& my_id,
+                                            float& my_gate) {
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + kWave * j;
@@ -146,6 +156,19 @@ __device__ __forceinline__ void route_token_j(const float* __restrict__ row, int
   __builtin_amdgcn_wave_barrier();  // the scratch may be reused by the next token
 }
 
+template <int J>
+__device__ __forceinline__ void route_token_j(const float* __restrict__ row, int E, int K, int lane,
+                                              TopkLds& sc, int& my_id, float& my_gate) {
+  float val[J];
+  unsigned long long key[J];
+  topk_keys<J>(row, E, lane, sc, val, key);
+  int rank[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) rank[j] = 0;
+  topk_count<J>(sc, 0, J * kWave, key, rank);
+  topk_select<J>(val, rank, E, K, lane, sc, my_id, my_gate);
+}
+
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int K, int lane,
                                             TopkLds& sc, int& my_id, float& my_gate) {
   if (E <= kWave) {
@@ -154,6 +177,68 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     route_token_j<2>(row, E, K, lane, sc, my_id, my_gate);
   } else {
     route_token_j<4>(row, E, K, lane, sc, my_id, my_gate);
+  }
+}
+
+// A team of S wavefronts routes one token (few tokens, idle wavefronts): the
+// ranks are sums of counts over disjoint key slices, so they and the
+// selection are the same integers as route_token's.  Member q counts the
+// keys of slice q into its scratch (route_team_count); after a workgroup
+// barrier the team's first member sums the S partial ranks and selects
+// (route_team_select, `team` = the members' scratch, in member order).
+template <int J>
+__device__ __forceinline__ void route_team_count_j(const float* __restrict__ row, int E, int lane,
+                                                   int q, int S, TopkLds& sc) {
+  float val[J];
+  unsigned long long key[J];
+  topk_keys<J>(row, E, lane, sc, val, key);  // every member keeps its own copy
+  const int sl = ((J * kWave + S - 1) / S + 15) / 16 * 16;
+  const int i0 = min(J * kWave, q * sl), i1 = min(J * kWave, i0 + sl);
+  int rank[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) rank[j] = 0;
+  topk_count<J>(sc, i0, i1, key, rank);
+#pragma unroll
+  for (int j = 0; j < J; ++j) sc.part[lane + kWave * j] = rank[j];
+}
+
+template <int J>
+__device__ __forceinline__ void route_team_select_j(const float* __restrict__ row, int E, int K,
+                                                    int lane, TopkLds* team, int S, int& my_id,
+                                                    float& my_gate) {
+  float val[J];
+  int rank[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    val[j] = row[min(lane + kWave * j, E - 1)];
+    rank[j] = 0;
+  }
+  for (int q = 0; q < S; ++q)
+#pragma unroll
+    for (int j = 0; j < J; ++j) rank[j] += team[q].part[lane + kWave * j];
+  topk_select<J>(val, rank, E, K, lane, team[0], my_id, my_gate);
+}
+
+__device__ __forceinline__ void route_team_count(const float* __restrict__ row, int E, int lane,
+                                                 int q, int S, TopkLds& sc) {
+  if (E <= kWave) {
+    route_team_count_j<1>(row, E, lane, q, S, sc);
+  } else if (E <= 2 * kWave) {
+    route_team_count_j<2>(row, E, lane, q, S, sc);
+  } else {
+    route_team_count_j<4>(row, E, lane, q, S, sc);
+  }
+}
+
+__device__ __forceinline__ void route_team_select(const float* __restrict__ row, int E, int K,
+                                                  int lane, TopkLds* team, int S, int& my_id,
+                                                  float& my_gate) {
+  if (E <= kWave) {
+    route_team_select_j<1>(row, E, K, lane, team, S, my_id, my_gate);
+  } else if (E <= 2 * kWave) {
+    route_team_select_j<2>(row, E, K, lane, team, S, my_id, my_gate);
+  } else {
+    route_team_select_j<4>(row, E, K, lane, team, S, my_id, my_gate);
   }
 }
 
@@ -235,8 +320,10 @@ __device__ __forceinline__ void build_union_one_token(const int32_t* ids, int K,
     if (lane == 0) *U_out = -1;
     return;
   }
-  int r = 0;  // ids below mine
-  for (int j = 0; j < K; ++j) r += __shfl(id, j) < id ? 1 : 0;
+  int r = 0;  // ids below mine: broadcast reads of the K ids, all in flight at once
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < K) r += ids[j] < id ? 1 : 0;
   if (act) {
     union_ids[r] = id;
     offsets[r] = r;
