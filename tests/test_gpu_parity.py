@@ -293,6 +293,48 @@ def test_layer_one_workspace_across_pass_sizes():
             assert np.array_equal(_bits(shared.out[:n]), _bits(chain.out[:n])), (step, n, mode)
 
 
+# ------------------------------- one-launch pass: top-K of few tokens in teams
+@pytest.mark.parametrize("n,E,K", [(1, 37, 5), (1, 256, 8), (2, 100, 8), (3, 256, 8),
+                                   (4, 64, 8), (5, 100, 7), (6, 256, 3), (7, 64, 8)])
+def test_layer_routing_teams_with_ties(n, E, K):
+    """The one-launch pass splits the rank counts of each of few tokens (n <= 6)
+    over a team of wavefronts: ids, union and byte counters bit for bit against
+    the oracle, gates and layer output bit for bit against the chain of entry
+    points (whose top-K takes one wavefront per token), with tied, NaN, -inf
+    and signed-zero logits, for one, two and four experts per lane."""
+    from moe_speculative_decoding_amd.layer import VerifyBuffers, to_device, verify_layer, verify_pass
+    from gpu_harness import _bits, upload_layer
+    cfg = LayerConfig(name="teams", cfg_id=83, E=E, K=K, d=264, f=136, S=0, w_dtype="bf16",
+                      x_dtype="bf16", n_values=(n,), routing=("logits_iid",), tolerance=1e-2)
+    case = make_case(cfg, n, None, seed=E + n)
+    g = np.random.default_rng(1000 + 31 * E + n)
+    vals = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0, np.nan, -np.inf], dtype=np.float32)
+    logits = vals[g.integers(0, len(vals), (n, E))]
+    print("teams n=%d E=%d K=%d" % (n, E, K), flush=True)
+    layer = upload_layer(case)
+    x, lg = to_device(case.x, DEV), to_device(logits, DEV)
+    buf = VerifyBuffers(layer, n, DEV)
+    verify_layer(layer, buf, x, lg, n, L.MOE_MODE_DEDUP)
+    chain = VerifyBuffers(layer, n, DEV)
+    verify_pass(layer, chain, x, lg, n, L.MOE_MODE_DEDUP)
+    torch.cuda.synchronize()
+    assert L.moe_get_error(buf.ws) == L.MOE_OK
+    rid, _ = oracle.route_topk(logits, K)
+    assert np.array_equal(buf.ids[:n].cpu().numpy(), rid)
+    un = oracle.build_union(rid, E)
+    assert int(buf.U.item()) == un["U"]
+    for k in ("union_ids", "offsets"):
+        got = getattr(buf, k).cpu().numpy()[:len(un[k])]
+        assert np.array_equal(got, un[k]), k
+    assert np.array_equal(buf.perm[:n * K].cpu().numpy(), un["perm"])
+    assert np.array_equal(buf.slot_rank[:n * K].cpu().numpy(), un["slot_rank"])
+    ub, rb = oracle.byte_counts(cfg.d, cfg.f, cfg.w_dtype, K, 0, n, un["U"])
+    b = buf.bytes.cpu().numpy()
+    assert int(b[0]) == ub and int(b[1]) == rb
+    assert np.array_equal(_bits(buf.gates[:n]), _bits(chain.gates[:n]))
+    assert np.array_equal(_bits(buf.out[:n]), _bits(chain.out[:n]))
+
+
 # ------------------------------------ one-launch pass, mode chosen on device
 @pytest.mark.parametrize("cfg,n", [(RAGGED_BF16, 5), (TINY, 4), (RAGGED_F32, 11)])
 def test_layer_auto_mode_follows_eq7(cfg, n):
