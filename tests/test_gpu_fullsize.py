@@ -6,8 +6,8 @@ The layers are the benchmark's own: every expert of the layer drawn on the
 device (synth.gen.device_layer_weights), so the DeepSeek-V3-shaped layer holds
 all 256 fp8 experts (11 GB).  The oracle checks routing, the union arrays and
 the byte counters in full (bit for bit), and the slot outputs and layer output
-of a few sampled tokens (every token of the OLMoE-shaped n = 8 pass): for
-each sampled token its K experts (and the shared experts) are copied back
+of a few sampled tokens (every token of the OLMoE-shaped passes, which the
+benchmark times at n = 1, 2, 4 and 8): for each sampled token its K experts (and the shared experts) are copied back
 from the device and evaluated by the oracle in float64.  Tolerances as in
 ``gpu_harness`` (contractual bound and the derived bf16-rounding bound).
 """
@@ -44,6 +44,8 @@ def _expert_to_host(w, e, cfg):
 
 @pytest.mark.parametrize("cfg,n,routing,tree,tokens", [
     (OLMOE, 8, "markov:0.5", False, range(8)),
+    (OLMOE, 4, "markov:0.5", False, range(4)),
+    (OLMOE, 2, "markov:0.5", False, range(2)),
     (OLMOE, 1, "markov:0.5", False, (0,)),
     (QWEN3, 8, "logits_ar1", False, (0, 5)),
     (DSV2LITE, 16, "markov:0.5", True, (0, 9, 15)),
