@@ -103,3 +103,82 @@ def test_one_launch_pass_full_size_sampled(cfg, n, routing, tree, tokens):
         check_vectors(out_dev[t][None, :], out_ref[None, :], tight, "%s token %d out" % (cfg.name, t))
     del w, sh, layer, buf
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg,n,routing,tree,C,tokens", [
+    (OLMOE, 8, "markov:0.5", False, 16, range(8)),
+    (OLMOE, 8, "markov:0.5", False, 24, (0, 4, 7)),
+    (OLMOE, 8, "markov:0.5", False, 8, (1, 6)),
+    (DSV3, 32, "markov:0.5", True, 32, (0, 17, 31)),
+    (DSV3, 32, "markov:0.5", True, 64, (3, 30)),
+])
+def test_one_launch_budget_full_size_sampled(cfg, n, routing, tree, C, tokens):
+    """The budgeted one-launch pass (moe_verify_layer_budget, kept gates
+    renormalised) on the benchmark's budget sweep layers: routing, the kept
+    union, gates and byte counters against the oracle's budget
+    (oracle.apply_budget) in full, slot and layer outputs of sampled tokens
+    against the oracle on the experts copied back, dropped slots zero."""
+    from moe_speculative_decoding_amd.layer import verify_layer_budget
+    print("full size budget %s n=%d C=%d" % (cfg.name, n, C), flush=True)
+    case = make_case(cfg, n, routing, seed=0, window=0, layer=0, tree=tree)
+    ids, gates = oracle.route_topk(case.logits, cfg.K)
+    un = oracle.build_union(ids, cfg.E)
+    bud = oracle.apply_budget(ids, gates, un, C, True)
+    sc = np.sort(bud["scores"].astype(np.float64))[::-1]
+    # no contribution within float32 reach of the cut: the device sums its own
+    # float32 gates, the oracle the float32 roundings of its float64 ones
+    assert C >= len(sc) or sc[C - 1] - sc[C] > 1e-5 * n, "near-tie at the cut: another seed"
+    w = device_layer_weights(cfg, seed=0, layer=0, device=DEV)
+    sh = device_layer_weights(cfg, seed=0, layer=0, device=DEV, shared=True) if cfg.S else None
+    layer = DeviceLayer(cfg.E, cfg.K, cfg.d, cfg.f, cfg.S, cfg.w_dtype, cfg.x_dtype, w, sh)
+    buf = VerifyBuffers(layer, n, DEV)
+    buf.y_slots.fill_(5.0)  # dropped rows must come back zero
+    verify_layer_budget(layer, buf, to_device(case.x, DEV), to_device(case.logits, DEV), n, C,
+                        True)
+    torch.cuda.synchronize()
+    assert L.moe_get_error(buf.ws) == L.MOE_OK
+
+    assert np.array_equal(buf.ids[:n].cpu().numpy(), ids)
+    U = bud["U"]
+    assert U == min(C, un["U"])
+    assert int(buf.U.item()) == U
+    for key in ("union_ids", "offsets"):
+        got = getattr(buf, key).cpu().numpy()[:len(bud[key])]
+        assert np.array_equal(got, bud[key]), key
+    assert np.array_equal(buf.perm[:n * cfg.K].cpu().numpy(), bud["perm"])
+    assert np.array_equal(buf.slot_rank[:n * cfg.K].cpu().numpy(), bud["slot_rank"])
+    g_dev = buf.gates[:n].cpu().numpy().astype(np.float64)
+    g_ref = bud["gates"]
+    assert np.all(np.abs(g_dev - g_ref) <= 1e-6 + 1e-5 * np.abs(g_ref)), "gates"
+    assert np.array_equal(g_dev == 0.0, g_ref == 0.0)
+    ub, rb = oracle.byte_counts(cfg.d, cfg.f, cfg.w_dtype, cfg.K, cfg.S, n, U)
+    b = buf.bytes.cpu().numpy()
+    assert int(b[0]) == ub and int(b[1]) == rb
+
+    tight = min(cfg.tolerance, derived_bound(cfg))
+    keep = bud["slot_rank"].reshape(n, cfg.K) >= 0
+    xs = oracle.decode_x(case.x, cfg.x_dtype)
+    y_dev = buf.y_slots[:n].cpu().numpy()
+    assert np.all(y_dev[~keep] == 0.0), "dropped slots must have zero rows"
+    out_dev = buf.out[:n].float().cpu().numpy()
+    decoded = {}
+    shared = [_expert_to_host(sh, s_, cfg) for s_ in range(cfg.S)] if cfg.S else []
+    for t in tokens:
+        y_ref = np.zeros((cfg.K, cfg.d))
+        for k in range(cfg.K):
+            if not keep[t, k]:
+                continue
+            e = int(ids[t, k])
+            if e not in decoded:
+                decoded[e] = _expert_to_host(w, e, cfg)
+            y_ref[k] = oracle.swiglu(xs[t], decoded[e])
+        if keep[t].any():
+            check_vectors(y_dev[t][keep[t]], y_ref[keep[t]], tight,
+                          "%s token %d kept y_slots" % (cfg.name, t))
+        out_ref = (g_ref[t][:, None] * y_ref).sum(axis=0)
+        for s_, ex in enumerate(shared):
+            out_ref = out_ref + oracle.swiglu(xs[t], ex)
+        check_vectors(out_dev[t][None, :], out_ref[None, :], tight,
+                      "%s token %d budget out" % (cfg.name, t))
+    del w, sh, layer, buf
+    torch.cuda.empty_cache()
