@@ -1,6 +1,6 @@
-"""GPU parity at the benchmark's full layer sizes, in the launch the benchmark
-times (the deduplicating one-launch pass, moe_verify_layer), on sampled
-outputs.
+"""GPU parity at the benchmark's full layer sizes, in the launches the
+benchmark times (the one-launch pass, moe_verify_layer, deduplicating and
+per-slot, and its budgeted form), on sampled outputs.
 
 The layers are the benchmark's own: every expert of the layer drawn on the
 device (synth.gen.device_layer_weights), so the DeepSeek-V3-shaped layer holds
@@ -42,25 +42,35 @@ def _expert_to_host(w, e, cfg):
     return oracle.DecodedExpert(stored, cfg.w_dtype)
 
 
-@pytest.mark.parametrize("cfg,n,routing,tree,tokens", [
-    (OLMOE, 8, "markov:0.5", False, range(8)),
-    (OLMOE, 4, "markov:0.5", False, range(4)),
-    (OLMOE, 2, "markov:0.5", False, range(2)),
-    (OLMOE, 1, "markov:0.5", False, (0,)),
-    (QWEN3, 8, "logits_ar1", False, (0, 5)),
-    (DSV2LITE, 16, "markov:0.5", True, (0, 9, 15)),
-    (DSV3, 8, "iid", False, (0, 7)),
-    (DSV3, 32, "markov:0.5", True, (0, 17, 31)),
+@pytest.mark.parametrize("cfg,n,routing,tree,tokens,mode", [
+    (OLMOE, 8, "markov:0.5", False, range(8), "dedup"),
+    (OLMOE, 4, "markov:0.5", False, range(4), "dedup"),
+    (OLMOE, 2, "markov:0.5", False, range(2), "dedup"),
+    (OLMOE, 1, "markov:0.5", False, (0,), "dedup"),
+    (OLMOE, 8, "markov:0.5", False, (0, 7), "perslot"),
+    (OLMOE, 1, "markov:0.5", False, (0,), "perslot"),
+    (QWEN3, 8, "logits_ar1", False, (0, 5), "dedup"),
+    (QWEN3, 1, "logits_ar1", False, (0,), "dedup"),
+    (DSV2LITE, 1, "markov:0.5", False, (0,), "dedup"),
+    (DSV2LITE, 8, "markov:0.5", False, (2, 6), "dedup"),
+    (DSV2LITE, 16, "markov:0.5", True, (0, 9, 15), "dedup"),
+    (DSV3, 1, "iid", False, (0,), "dedup"),
+    (DSV3, 4, "iid", False, (1, 3), "dedup"),
+    (DSV3, 8, "iid", False, (0, 7), "dedup"),
+    (DSV3, 8, "markov:0.5", False, (4,), "dedup"),
+    (DSV3, 32, "markov:0.5", True, (0, 17, 31), "dedup"),
 ])
-def test_one_launch_pass_full_size_sampled(cfg, n, routing, tree, tokens):
-    print("full size %s n=%d routing=%s tree=%s" % (cfg.name, n, routing, tree), flush=True)
+def test_one_launch_pass_full_size_sampled(cfg, n, routing, tree, tokens, mode):
+    print("full size %s n=%d routing=%s tree=%s %s" % (cfg.name, n, routing, tree, mode),
+          flush=True)
+    dedup = mode == "dedup"
     w = device_layer_weights(cfg, seed=0, layer=0, device=DEV)
     sh = device_layer_weights(cfg, seed=0, layer=0, device=DEV, shared=True) if cfg.S else None
     layer = DeviceLayer(cfg.E, cfg.K, cfg.d, cfg.f, cfg.S, cfg.w_dtype, cfg.x_dtype, w, sh)
     case = make_case(cfg, n, routing, seed=0, window=0, layer=0, tree=tree)
     buf = VerifyBuffers(layer, n, DEV)
     verify_layer(layer, buf, to_device(case.x, DEV), to_device(case.logits, DEV), n,
-                 L.MOE_MODE_DEDUP)
+                 L.MOE_MODE_DEDUP if dedup else L.MOE_MODE_PERSLOT)
     torch.cuda.synchronize()
     assert L.moe_get_error(buf.ws) == L.MOE_OK
 
@@ -70,14 +80,16 @@ def test_one_launch_pass_full_size_sampled(cfg, n, routing, tree, tokens):
     assert np.all(np.abs(g_dev - gates) <= 1e-6 + 1e-5 * np.abs(gates))
     un = oracle.build_union(ids, cfg.E)
     U = un["U"]
-    assert int(buf.U.item()) == U
-    assert np.array_equal(buf.union_ids.cpu().numpy()[:len(un["union_ids"])], un["union_ids"])
-    assert np.array_equal(buf.offsets.cpu().numpy()[:len(un["offsets"])], un["offsets"])
-    assert np.array_equal(buf.perm[:n * cfg.K].cpu().numpy(), un["perm"])
-    assert np.array_equal(buf.slot_rank[:n * cfg.K].cpu().numpy(), un["slot_rank"])
+    if dedup:  # the per-slot pass leaves the union arrays alone
+        assert int(buf.U.item()) == U
+        assert np.array_equal(buf.union_ids.cpu().numpy()[:len(un["union_ids"])],
+                              un["union_ids"])
+        assert np.array_equal(buf.offsets.cpu().numpy()[:len(un["offsets"])], un["offsets"])
+        assert np.array_equal(buf.perm[:n * cfg.K].cpu().numpy(), un["perm"])
+        assert np.array_equal(buf.slot_rank[:n * cfg.K].cpu().numpy(), un["slot_rank"])
     ub, rb = oracle.byte_counts(cfg.d, cfg.f, cfg.w_dtype, cfg.K, cfg.S, n, U)
     b = buf.bytes.cpu().numpy()
-    assert int(b[0]) == ub and int(b[1]) == rb
+    assert int(b[0]) == (ub if dedup else rb) and int(b[1]) == rb
 
     tight = min(cfg.tolerance, derived_bound(cfg))
     xs = oracle.decode_x(case.x, cfg.x_dtype)
