@@ -40,6 +40,7 @@ def run(q, cost, L_):
 
 @pytest.mark.parametrize("N,L_,seed", [
     (1, 1, 0), (7, 3, 1), (200, 8, 2), (300, 12, 3), (97, 32, 4), (1000, 4, 5), (513, 1, 6),
+    (2048, 8, 0), (2048, 12, 0),  # the sizes the benchmark times
 ])
 def test_bellman_matches_oracle(N, L_, seed):
     print("bellman N=%d L=%d seed=%d" % (N, L_, seed), flush=True)

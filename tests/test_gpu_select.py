@@ -153,6 +153,7 @@ def test_ecospec_figure3_on_device():
 @pytest.mark.parametrize("N,L_,E,k,gamma,seed", [
     (1, 1, 8, 2, 1, 0), (14, 16, 64, 8, 4, 1), (32, 48, 128, 8, 8, 2), (64, 16, 64, 8, 32, 3),
     (120, 4, 64, 6, 60, 4), (1024, 2, 64, 4, 16, 5), (35, 58, 256, 8, 12, 6),
+    (64, 48, 128, 8, 16, 1),  # a size the benchmark times
 ])
 def test_ecospec_matches_oracle(N, L_, E, k, gamma, seed):
     parent, q = draft_tree(N, seed, p_one=0.1)
