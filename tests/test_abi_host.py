@@ -299,3 +299,16 @@ def test_byte_counts_match_oracle(cfg):
             + r(32 * cfg.S * cfg.d * 4))
     assert L.moe_workspace_size(s, 32, L.MOE_MODE_DEDUP) == need
     assert L.moe_workspace_size(s, 32, L.MOE_MODE_PERSLOT) == need
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No fallback: importing the binding with no built library raises, and so
+    does every entry point of the layer helpers that imports it."""
+    import subprocess
+    import sys
+    env = dict(os.environ, MOE_VERIFY_LIB="/nonexistent/libmoe_verify.so")
+    for mod in ("moe_speculative_decoding_amd._lib", "moe_speculative_decoding_amd.layer"):
+        r = subprocess.run([sys.executable, "-c", "import %s" % mod], env=env, cwd=ROOT,
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode != 0, mod
+        assert "ImportError" in r.stderr and "not built" in r.stderr, r.stderr[-400:]
