@@ -59,6 +59,10 @@ def _expert_to_host(w, e, cfg):
     (DSV3, 8, "iid", False, (0, 7), "dedup"),
     (DSV3, 8, "markov:0.5", False, (4,), "dedup"),
     (DSV3, 32, "markov:0.5", True, (0, 17, 31), "dedup"),
+    (QWEN3, 8, "logits_ar1", False, (3,), "perslot"),
+    (DSV2LITE, 16, "markov:0.5", True, (4, 12), "perslot"),
+    (DSV3, 8, "iid", False, (2,), "perslot"),
+    (DSV3, 32, "markov:0.5", True, (5, 26), "perslot"),
 ])
 def test_one_launch_pass_full_size_sampled(cfg, n, routing, tree, tokens, mode):
     print("full size %s n=%d routing=%s tree=%s %s" % (cfg.name, n, routing, tree, mode),
