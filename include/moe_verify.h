@@ -72,7 +72,8 @@ typedef enum {
   MOE_ERR_HIP = 4,          /* the HIP runtime refused a launch or copy */
   MOE_ERR_BAD_IDS = 5,      /* (device) an expert id outside [0, E) was seen */
   MOE_ERR_TIMEOUT = 6,      /* (device) a bounded wait gave up */
-  MOE_ERR_BAD_TREE = 7      /* (device) a draft tree or its probabilities out of range */
+  MOE_ERR_BAD_TREE = 7,     /* (device) a draft tree or its probabilities out of range */
+  MOE_ERR_TOO_LARGE = 8     /* the pass needs more than moe_verify_layer_noalloc's scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -234,6 +235,34 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
                             float* y_shared, uint64_t* bytes, void* ws, size_t ws_bytes,
                             moe_stream_t stream);
 
+/* moe_verify_layer without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The control block, hand-over flags,
+ * intermediate activations and any slot outputs the caller does not keep
+ * live in a static device array of 16 MiB that every GPU the library runs on
+ * holds until the process ends; the call itself allocates nothing.
+ *   Arguments, outputs and results as moe_verify_layer (same kernels, the
+ *   same results bit for bit), less ws and ws_bytes.
+ *   Limit: passes whose moe_verify_layer workspace need (control block and
+ *   flags 33,024 B, H n(K+S)f*4 B, plus n*K*d*4 B when y_slots is NULL and
+ *   n*S*d*4 B when y_shared is NULL, each rounded up to 256 B) exceeds
+ *   16 MiB return MOE_ERR_TOO_LARGE before anything is enqueued.
+ *   Set-up: the first call on a device looks up that device's copy of the
+ *   array and clears its control block and flags with a kernel enqueued on
+ *   `stream` ahead of the pass.
+ *   Sharing: every call on one GPU uses the same array, which keeps the last
+ *   call's contents; calls that overlap in time on one GPU (different
+ *   streams, or graphs replayed concurrently) race and give unspecified
+ *   results.  Device faults are recorded in the array's error word, which
+ *   moe_get_error(NULL, stream) reads and clears.
+ * Errors: as moe_verify_layer, plus MOE_ERR_TOO_LARGE. */
+moe_status moe_verify_layer_noalloc(const moe_shape* shape, const moe_weights* w,
+                                    const float* logits, const void* x, int32_t n, int32_t mode,
+                                    void* out, int32_t out_dtype, int32_t* ids, float* gates,
+                                    int32_t* U, int32_t* union_ids, int32_t* offsets,
+                                    int32_t* perm, int32_t* slot_rank, float* y_slots,
+                                    float* y_shared, uint64_t* bytes, moe_stream_t stream);
+
 /* moe_verify_layer in deduplicating mode with a per-layer expert budget:
  * the route and union, then moe_expert_budget(C, renorm) on them, the
  * deduplicating FFN over the kept experts and the combine with the budgeted
@@ -353,7 +382,8 @@ moe_status moe_byte_counts(const moe_shape* shape, int32_t n, int32_t U,
 
 /* Synchronizes `stream`, then returns and clears the device error word kept
  * at the start of `ws`: MOE_OK, MOE_ERR_BAD_IDS, MOE_ERR_BAD_TREE or
- * MOE_ERR_TIMEOUT. */
+ * MOE_ERR_TIMEOUT.  ws = NULL reads the error word of the current device's
+ * moe_verify_layer_noalloc scratch (MOE_OK if no such call ran there). */
 moe_status moe_get_error(void* ws, moe_stream_t stream);
 
 /* Diagnostic: decode `count` E4M3FN codes (device) to f32 (device) with the

@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("MOE_VERIFY_LIB") or os.path.join(_HERE, "libmoe_verif
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, 1, 2, 3
 MOE_ERR_HIP, MOE_ERR_BAD_IDS, MOE_ERR_TIMEOUT, MOE_ERR_BAD_TREE = 4, 5, 6, 7
+MOE_ERR_TOO_LARGE = 8
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_MODE_DEDUP, MOE_MODE_PERSLOT = 0, 1
 
@@ -68,6 +69,8 @@ _SIG = {
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]),
     "moe_verify_layer": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I, _I, _P,
                               _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_verify_layer_noalloc": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I,
+                                      _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_verify_layer_budget": (_I, [C.POINTER(moe_shape), C.POINTER(moe_weights), _P, _P, _I,
                                      _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      C.c_size_t, _P]),
@@ -189,6 +192,17 @@ def moe_verify_layer(shape: moe_shape, w: moe_weights, logits, x, n, mode, out, 
            "moe_verify_layer")
 
 
+def moe_verify_layer_noalloc(shape: moe_shape, w: moe_weights, logits, x, n, mode, out,
+                             out_dtype, ids=None, gates=None, U=None, union_ids=None,
+                             offsets=None, perm=None, slot_rank=None, y_slots=None,
+                             y_shared=None, bytes_=None, stream=None) -> None:
+    _check(lib.moe_verify_layer_noalloc(C.byref(shape), C.byref(w), ptr(logits), ptr(x), n, mode,
+                                        ptr(out), out_dtype, ptr(ids), ptr(gates), ptr(U),
+                                        ptr(union_ids), ptr(offsets), ptr(perm), ptr(slot_rank),
+                                        ptr(y_slots), ptr(y_shared), ptr(bytes_), _stream(stream)),
+           "moe_verify_layer_noalloc")
+
+
 def moe_verify_layer_budget(shape: moe_shape, w: moe_weights, logits, x, n, C_, renorm, out,
                             out_dtype, ids=None, gates=None, U=None, union_ids=None, offsets=None,
                             perm=None, slot_rank=None, y_slots=None, y_shared=None, bytes_=None,
@@ -242,7 +256,8 @@ def moe_byte_counts(shape: moe_shape, n: int, U: int):
 
 
 def moe_get_error(ws, stream=None) -> int:
-    """Status of the device error word (also returned, not raised)."""
+    """Status of the device error word (also returned, not raised); ws=None reads
+    the error word of moe_verify_layer_noalloc's scratch on the current device."""
     return int(lib.moe_get_error(ptr(ws), _stream(stream)))
 
 

@@ -4,7 +4,17 @@
 // work is enqueued, so an invalid call enqueues nothing.
 #include "moe_verify.h"
 
+#include <mutex>
+
 #include "common.h"
+
+// moe_verify_layer_noalloc keeps its workspace (control block, hand-over
+// flags, H and the slot outputs the caller keeps none of) in this array.
+// In host code `scratch` names a host-side stand-in, never the device
+// memory: host code uses only the address hipGetSymbolAddress returns for
+// the current device, kept per device in g_scratch.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -156,12 +166,19 @@ int wt_of(int w_dtype) {
 }
 
 
+// workspace bytes the one-launch pass needs: control block and flags, H in
+// f32, and the slot outputs the caller does not keep
+size_t layer_ws_need(const moe_shape* shape, int n, const float* y_slots, const float* y_shared) {
+  return kHOffset + layer_h_bytes(shape, n) +
+         (y_slots == nullptr ? layer_ys_bytes(shape, n) : 0) +
+         (y_shared == nullptr ? layer_ysh_bytes(shape, n) : 0);
+}
+
 // argument checks of the one-launch pass shared by its fixed-mode and
-// automatic-mode entry points
-moe_status moe_verify_layer_check(const moe_shape* shape, const moe_weights* w,
-                                  const float* logits, const void* x, int n, int mode, void* out,
-                                  int out_dtype, const float* y_slots, const float* y_shared,
-                                  const uint64_t* bytes, const void* ws, size_t ws_bytes) {
+// automatic-mode entry points, everything but the workspace
+moe_status layer_args_check(const moe_shape* shape, const moe_weights* w, const float* logits,
+                            const void* x, int n, int mode, void* out, int out_dtype,
+                            const float* y_slots, const float* y_shared, const uint64_t* bytes) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (n < 1 || n > kMaxN) return MOE_ERR_ARG;
@@ -175,11 +192,35 @@ moe_status moe_verify_layer_check(const moe_shape* shape, const moe_weights* w,
       (y_shared != nullptr && !aligned(y_shared, 16)))
     return MOE_ERR_ARG;
   if (bytes != nullptr && !aligned(bytes, 8)) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+moe_status moe_verify_layer_check(const moe_shape* shape, const moe_weights* w,
+                                  const float* logits, const void* x, int n, int mode, void* out,
+                                  int out_dtype, const float* y_slots, const float* y_shared,
+                                  const uint64_t* bytes, const void* ws, size_t ws_bytes) {
+  moe_status st = layer_args_check(shape, w, logits, x, n, mode, out, out_dtype, y_slots,
+                                   y_shared, bytes);
+  if (st != MOE_OK) return st;
   if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
-  const size_t need = kHOffset + layer_h_bytes(shape, n) +
-                      (y_slots == nullptr ? layer_ys_bytes(shape, n) : 0) +
-                      (y_shared == nullptr ? layer_ysh_bytes(shape, n) : 0);
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < layer_ws_need(shape, n, y_slots, y_shared)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// the optional routing and union outputs of the fixed-mode pass: 4-byte
+// aligned, the five union arrays all or none
+moe_status layer_outputs_check(const int32_t* ids, const float* gates, const int32_t* U,
+                               const int32_t* union_ids, const int32_t* offsets,
+                               const int32_t* perm, const int32_t* slot_rank, int* given) {
+  if ((ids != nullptr && !aligned(ids, 4)) || (gates != nullptr && !aligned(gates, 4)))
+    return MOE_ERR_ARG;
+  const void* uni[5] = {U, union_ids, offsets, perm, slot_rank};
+  *given = 0;
+  for (const void* p : uni) {
+    if (p != nullptr && !aligned(p, 4)) return MOE_ERR_ARG;
+    *given += p != nullptr;
+  }
+  if (*given != 0 && *given != 5) return MOE_ERR_ARG;
   return MOE_OK;
 }
 
@@ -218,15 +259,9 @@ moe_status verify_layer_impl(const moe_shape* shape, const moe_weights* w, const
   moe_status st = moe_verify_layer_check(shape, w, logits, x, n, mode, out, out_dtype, y_slots,
                                          y_shared, bytes, ws, ws_bytes);
   if (st != MOE_OK) return st;
-  if ((ids != nullptr && !aligned(ids, 4)) || (gates != nullptr && !aligned(gates, 4)))
-    return MOE_ERR_ARG;
-  const void* uni[5] = {U, union_ids, offsets, perm, slot_rank};
   int given = 0;
-  for (const void* p : uni) {
-    if (p != nullptr && !aligned(p, 4)) return MOE_ERR_ARG;
-    given += p != nullptr;
-  }
-  if (given != 0 && given != 5) return MOE_ERR_ARG;
+  st = layer_outputs_check(ids, gates, U, union_ids, offsets, perm, slot_rank, &given);
+  if (st != MOE_OK) return st;
   moe::LayerParams lp = layer_params(
       shape, w, logits, x, n, mode == MOE_MODE_DEDUP ? moe::MODE_DEDUP : moe::MODE_PERSLOT, out,
       out_dtype, y_slots, y_shared, bytes, ws);
@@ -242,6 +277,45 @@ moe_status verify_layer_impl(const moe_shape* shape, const moe_weights* w, const
     lp.slot_rank = slot_rank;
   }
   return hip_status(moe::launch_layer(lp, wt_of(shape->w_dtype), static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------- allocation-free variant
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// This device's scratch address, set up on the first call on the device
+// (with the device current): the symbol's address is looked up once and
+// the control block and flags are cleared with a fill kernel on `stream`,
+// ahead of the call that follows on the same stream (device globals start
+// zero-filled; the clear states the requirement).  Under stream capture
+// the clear becomes the graph's first node.
+moe_status scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  moe_status st = hip_status(hipGetDevice(&dev));
+  if (st != MOE_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (st != MOE_OK) return st;
+    if (p == nullptr || !aligned(p, 256)) return MOE_ERR_WORKSPACE;
+    st = hip_status(moe::launch_fill_zero(p, kHOffset, stream));
+    if (st != MOE_OK) return st;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
+// the scratch address of the current device if a call has set it up there
+void* scratch_if_set_up() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  return g_scratch[dev];
 }
 }  // namespace
 
@@ -259,6 +333,7 @@ const char* moe_status_str(int32_t s) {
     case MOE_ERR_BAD_IDS: return "expert id outside [0, E)";
     case MOE_ERR_TIMEOUT: return "bounded device wait gave up";
     case MOE_ERR_BAD_TREE: return "draft tree or probabilities out of range";
+    case MOE_ERR_TOO_LARGE: return "pass needs more scratch than the static array holds";
     default: return "unknown status";
   }
 }
@@ -360,6 +435,29 @@ moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const 
   return verify_layer_impl(shape, w, logits, x, n, mode, 0, 0, out, out_dtype, ids, gates, U,
                            union_ids, offsets, perm, slot_rank, y_slots, y_shared, bytes, ws,
                            ws_bytes, stream);
+}
+
+moe_status moe_verify_layer_noalloc(const moe_shape* shape, const moe_weights* w,
+                                    const float* logits, const void* x, int32_t n, int32_t mode,
+                                    void* out, int32_t out_dtype, int32_t* ids, float* gates,
+                                    int32_t* U, int32_t* union_ids, int32_t* offsets,
+                                    int32_t* perm, int32_t* slot_rank, float* y_slots,
+                                    float* y_shared, uint64_t* bytes, moe_stream_t stream) {
+  // every argument is checked before the scratch is touched
+  moe_status st = layer_args_check(shape, w, logits, x, n, mode, out, out_dtype, y_slots,
+                                   y_shared, bytes);
+  if (st != MOE_OK) return st;
+  int given = 0;
+  st = layer_outputs_check(ids, gates, U, union_ids, offsets, perm, slot_rank, &given);
+  if (st != MOE_OK) return st;
+  if (layer_ws_need(shape, n, y_slots, y_shared) > kScratchBytes) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = scratch_of_current_device(s, &ws);
+  if (st != MOE_OK) return st;
+  return verify_layer_impl(shape, w, logits, x, n, mode, 0, 0, out, out_dtype, ids, gates, U,
+                           union_ids, offsets, perm, slot_rank, y_slots, y_shared, bytes, ws,
+                           kScratchBytes, stream);
 }
 
 moe_status moe_verify_layer_budget(const moe_shape* shape, const moe_weights* w,
@@ -479,8 +577,13 @@ int32_t moe_last_hip_error(void) { return static_cast<int32_t>(g_last_hip); }
 const char* moe_hip_error_string(void) { return hipGetErrorString(g_last_hip); }
 
 moe_status moe_get_error(void* ws, moe_stream_t stream) {
-  if (ws == nullptr || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ws == nullptr) {
+    // the static scratch of moe_verify_layer_noalloc on the current device
+    ws = scratch_if_set_up();
+    if (ws == nullptr) return hip_status(hipStreamSynchronize(s));  // no call ran there
+  }
+  if (!aligned(ws, 256)) return MOE_ERR_WORKSPACE;
   moe_status st = hip_status(hipStreamSynchronize(s));
   if (st != MOE_OK) return st;
   uint32_t word = 0;

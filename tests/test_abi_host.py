@@ -55,7 +55,7 @@ def test_binding_signatures_match_header():
 
 def test_abi_version_and_status_strings():
     assert L.moe_abi_version() == 1
-    for s in range(8):
+    for s in range(9):
         assert L.status_str(s) and L.status_str(s) != "unknown status"
     assert L.status_str(99) == "unknown status"
 
@@ -312,3 +312,33 @@ def test_binding_fails_loudly_without_the_library():
                            capture_output=True, text=True, timeout=120)
         assert r.returncode != 0, mod
         assert "ImportError" in r.stderr and "not built" in r.stderr, r.stderr[-400:]
+
+
+def test_noalloc_validation_before_launch():
+    # every check runs before the static scratch is looked up, so no call
+    # here reaches the device
+    s = shape()
+    w = _weights()
+    fn = L.lib.moe_verify_layer_noalloc
+    args = [C.byref(s), C.byref(w), FAKE, FAKE, 8, L.MOE_MODE_DEDUP, FAKE, L.MOE_F32] + \
+        [None] * 10 + [None]
+    bad = list(args); bad[4] = 0               # n = 0
+    assert fn(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[5] = 2               # mode
+    assert fn(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[7] = 5               # out dtype
+    assert fn(*bad) == L.MOE_ERR_UNSUPPORTED
+    bad = list(args); bad[10] = FAKE           # U given without the other union arrays
+    assert fn(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[15] = FAKE + 4       # misaligned y_slots
+    assert fn(*bad) == L.MOE_ERR_ARG
+    # beyond the 16 MiB scratch: n*K*d*4 B of slot outputs alone exceed it
+    big = shape(d=16384, f=1024)
+    bad = list(args); bad[0] = C.byref(big); bad[4] = 32
+    assert fn(*bad) == L.MOE_ERR_TOO_LARGE
+    # the same pass with the slot outputs kept by the caller needs H only
+    need = 33024 + 32 * 8 * 1024 * 4
+    assert need <= 16 << 20
+    need_ys = need + 32 * 8 * 16384 * 4
+    assert need_ys > 16 << 20
+    assert L.moe_workspace_size(big, 32, L.MOE_MODE_DEDUP) == need_ys
