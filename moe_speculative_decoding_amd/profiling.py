@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the verify-pass kernels (host-side text tools).
 
     python -m moe_speculative_decoding_amd.profiling traffic FETCH_DIR WRITE_DIR MANIFEST
-        HBM traffic per deduplicating call from two `rocprofv3 --pmc FETCH_SIZE`
+        HBM traffic per one-launch pass (both modes) from two `rocprofv3 --pmc FETCH_SIZE`
         and `--pmc WRITE_SIZE` runs of `bench.py --counters MANIFEST`.  Each counter is
         scaled by what it reads for a plain 1 GiB device copy in the same run (the
         calibration factor = copy bytes / counted bytes).
@@ -11,6 +11,14 @@
 
     python -m moe_speculative_decoding_amd.profiling stats TRACE_DIR
         kernel-duration table from a `rocprofv3 --kernel-trace --stats` run.
+
+    python -m moe_speculative_decoding_amd.profiling step TRACE_DIR MANIFEST
+        mean duration of every operation of the step, from a kernel trace of
+        `bench.py --profile-step --step-manifest MANIFEST`.
+
+    python -m moe_speculative_decoding_amd.profiling valu PMC_DIR MANIFEST
+        VALUBusy, VALU and MFMA instruction counts per pass from a `--pmc` run of
+        `bench.py --counters MANIFEST`.
 """
 from __future__ import annotations
 
@@ -61,49 +69,120 @@ def per_dispatch(d: str, counter: str):
     return [(k, names[k], acc[k]) for k in sorted(acc)]
 
 
+def _counted(d: str, counter: str, man: dict):
+    """(calibration factor, [bytes of launch i of the manifest]) for one counter run."""
+    rows = per_dispatch(d, counter)
+    kname = man.get("kernel", "layer_kernel")
+    need = len(man["launches"])
+    idx = [i for i, (_, n, _) in enumerate(rows) if kname in n]
+    if len(idx) < need:
+        raise ValueError("expected %d %s dispatches, found %d" % (need, kname, len(idx)))
+    first = idx[-need]
+    # the three calibration copies are the last dispatches before the counted
+    # launches that are not the library's (a copy reads and writes copy_bytes)
+    others = [v for (_, n, v) in rows[:first] if "moe::" not in n]
+    copies = others[-man["copies"]:]
+    factor = man["copy_bytes"] / (sum(copies) / len(copies)) if copies else float("nan")
+    return factor, [factor * rows[i][2] for i in idx[-need:]]
+
+
 def traffic(fetch_dir: str, write_dir: str, manifest_path: str) -> dict:
+    """HBM bytes per one-launch pass from a FETCH_SIZE and a WRITE_SIZE run of
+    `bench.py --counters`: per mode and (routing, n), against the union bytes
+    U*b (both modes) and the requested bytes n*(K+S)*b (per-slot)."""
     with open(manifest_path) as fh:
         man = json.load(fh)
+    ff, fetch = _counted(fetch_dir, "FETCH_SIZE", man)
+    wf, write = _counted(write_dir, "WRITE_SIZE", man)
+    out = {"workload": man.get("workload"), "fetch_factor": ff, "write_factor": wf,
+           "expert_bytes": man.get("expert_bytes")}
+    for mode in ("dedup", "perslot"):
+        sel = [i for i, l in enumerate(man["launches"]) if l["mode"] == mode]
+        if not sel:
+            continue
+        groups = defaultdict(list)
+        for i in sel:
+            l = man["launches"][i]
+            groups["%s n=%d" % (l["routing"], l["n"])].append(i)
+        pts = {}
+        for key, ii in groups.items():
+            f = sum(fetch[i] for i in ii) / len(ii)
+            w = sum(write[i] for i in ii) / len(ii)
+            ub = sum(man["launches"][i]["union_bytes"] for i in ii) / len(ii)
+            rb = sum(man["launches"][i]["requested_bytes"] for i in ii) / len(ii)
+            pts[key] = {"fetch_bytes_per_call": f, "write_bytes_per_call": w,
+                        "union_bytes_per_call": ub, "requested_bytes_per_call": rb,
+                        "fetch_over_union": f / ub, "fetch_over_requested": f / rb}
+        tf = sum(fetch[i] for i in sel)
+        tw = sum(write[i] for i in sel)
+        tu = sum(man["launches"][i]["union_bytes"] for i in sel)
+        tr = sum(man["launches"][i]["requested_bytes"] for i in sel)
+        out[mode] = {"points": pts, "traffic_bytes_per_call": (tf + tw) / len(sel),
+                     "fetch_bytes_per_call": tf / len(sel),
+                     "union_bytes_per_call": tu / len(sel), "fetch_over_union": tf / tu,
+                     "fetch_over_requested": tf / tr}
+    return out
+
+
+def valu(d: str, manifest_path: str) -> dict:
+    """VALU activity per one-launch pass from a `--pmc VALUBusy SQ_INSTS_VALU
+    SQ_INSTS_MFMA` run of `bench.py --counters` (VALUBusy: the share of the
+    kernel's GPU time in which vector ALU instructions are processed, the
+    vendor's derived counter)."""
+    with open(manifest_path) as fh:
+        man = json.load(fh)
+    kname = man.get("kernel", "layer_kernel")
+    vals = {}
+    for r in _counter_rows(d):
+        if kname not in r["Kernel_Name"]:
+            continue
+        k = int(r["Dispatch_Id"])
+        vals.setdefault(k, defaultdict(float))[r["Counter_Name"]] += float(r["Counter_Value"])
+    ids = sorted(vals)[-len(man["launches"]):]
+    groups = defaultdict(list)
+    for k, l in zip(ids, man["launches"]):
+        groups["%s %s n=%d" % (l["mode"], l["routing"], l["n"])].append(vals[k])
     out = {}
-    for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        rows = per_dispatch(d, counter)
-        # the counted block is the last per_op * ops dispatches of the counted
-        # kernel; the three calibration copies are the last non-library
-        # dispatches before it
-        kname, k = man.get("kernel", "ffn_stream_kernel"), man.get("per_op", 2)
-        ffn_idx = [i for i, (_, n, _) in enumerate(rows) if kname in n]
-        need = k * len(man["ops"])
-        if len(ffn_idx) < need:
-            raise ValueError("expected %d %s dispatches, found %d" % (need, kname, len(ffn_idx)))
-        first = ffn_idx[-need]
-        ffn = [(rows[i][1], rows[i][2]) for i in ffn_idx[-need:]]
-        others = [v for (_, n, v) in rows[:first] if "moe::" not in n]
-        copies = others[-man["copies"]:]
-        # a copy reads copy_bytes and writes copy_bytes
-        factor = man["copy_bytes"] / (sum(copies) / len(copies)) if copies else float("nan")
-        per_op = [factor * sum(v for _, v in ffn[k * i:k * (i + 1)]) for i in range(len(man["ops"]))]
-        out[label] = {"factor": factor, "per_op": per_op, "copies_counted": copies}
+    for key, vs in groups.items():
+        out[key] = {c: sum(v.get(c, 0.0) for v in vs) / len(vs)
+                    for c in ("VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_MFMA")}
+    return out
+
+
+def step_stats(trace_dir: str, manifest_path: str) -> dict:
+    """Mean duration of each operation of the step from a `--kernel-trace` run
+    of `bench.py --profile-step --step-manifest`: the layer_kernel dispatches
+    repeat the step's operation order, so dispatch i belongs to operation
+    i mod ops; per (routing, n), and the step's union bytes over its summed
+    mean durations."""
+    with open(manifest_path) as fh:
+        man = json.load(fh)
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if "layer_kernel" in r["Kernel_Name"]:
+                    rows.append((int(r["Start_Timestamp"]),
+                                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
     ops = man["ops"]
-    by_n = defaultdict(lambda: [0.0, 0.0, 0.0, 0])
+    if len(rows) % len(ops) != 0:
+        raise ValueError("%d layer_kernel dispatches for %d operations" % (len(rows), len(ops)))
+    reps = len(rows) // len(ops)
+    per_op = [0.0] * len(ops)
+    for i, (_, dur) in enumerate(rows):
+        per_op[i % len(ops)] += dur / reps
+    groups = defaultdict(list)
     for i, op in enumerate(ops):
-        t = by_n[op["n"]]
-        t[0] += out["fetch"]["per_op"][i]
-        t[1] += out["write"]["per_op"][i]
-        t[2] += op["union_bytes"]
-        t[3] += 1
-    summary = {
-        "fetch_factor": out["fetch"]["factor"], "write_factor": out["write"]["factor"],
-        "per_n": {str(n): {"fetch_bytes_per_call": v[0] / v[3], "write_bytes_per_call": v[1] / v[3],
-                           "union_bytes_per_call": v[2] / v[3], "fetch_over_union": v[0] / v[2]}
-                  for n, v in sorted(by_n.items())},
-    }
-    tot_f = sum(out["fetch"]["per_op"])
-    tot_w = sum(out["write"]["per_op"])
-    tot_u = sum(op["union_bytes"] for op in ops)
-    summary["traffic_bytes_per_call"] = (tot_f + tot_w) / len(ops)
-    summary["union_bytes_per_call"] = tot_u / len(ops)
-    summary["fetch_over_union"] = tot_f / tot_u
-    return summary
+        groups["%s n=%d" % (op["routing"], op["n"])].append(i)
+    pts = {key: {"us": sum(per_op[i] for i in ii) / len(ii) / 1e3,
+                 "union_bytes": sum(ops[i]["union_bytes"] for i in ii) / len(ii)}
+           for key, ii in groups.items()}
+    tb = sum(op["union_bytes"] for op in ops)
+    tt = sum(per_op) * 1e-9
+    return {"replays": reps, "points": pts, "step_kernel_us": sum(per_op) / 1e3,
+            "GBs_union": tb / tt / 1e9}
 
 
 def stats(trace_dir: str) -> str:
@@ -122,7 +201,11 @@ def stats(trace_dir: str) -> str:
 
 
 def main(argv):
-    if len(argv) >= 4 and argv[0] == "traffic":
+    if len(argv) >= 3 and argv[0] == "valu":
+        print(json.dumps(valu(argv[1], argv[2]), indent=1))
+    elif len(argv) >= 3 and argv[0] == "step":
+        print(json.dumps(step_stats(argv[1], argv[2]), indent=1))
+    elif len(argv) >= 4 and argv[0] == "traffic":
         rec = traffic(argv[1], argv[2], argv[3])
         if len(argv) >= 6 and argv[4] == "--out":
             rec["kernel_source_sha256"] = kernel_source_hash()
