@@ -14,9 +14,9 @@ of rarely used experts.  The page gives no formula; the readings taken here
 * the C experts of largest contribution are kept; equal contributions go to
   the lower expert id, a NaN contribution ranks below every number, and
   -0.0 equals +0.0 (the same order as the router's top-K);
-* the contribution is summed in float32, slot by slot in ascending slot
-  order, from float32 gates: the precision of the kernels, so both sides take
-  the same keep/drop decision;
+* the contribution is the plain sum of those gates in float64, slot by slot
+  in ascending slot order (the gates are the oracle's own float64 softmax
+  values, or the float64 values of gates the caller gives);
 * a dropped slot contributes nothing to the layer output (its gate becomes 0
   and its expert output row is zero); with ``renorm`` the kept gates of a
   token that lost a slot are divided by their sum (a token with no kept
@@ -31,7 +31,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 
-def _order_key(score: np.float32, e: int):
+def _order_key(score: float, e: int):
     # larger score first; NaN after every number; equal scores: lower id first
     v = float(score)
     if math.isnan(v):
@@ -39,18 +39,18 @@ def _order_key(score: np.float32, e: int):
     return (0, -v, e)
 
 
-def expert_scores(union: Dict[str, object], gates32: np.ndarray) -> np.ndarray:
-    """Contribution of each union expert: float32 sum of its slots' gates, ascending slot."""
+def expert_scores(union: Dict[str, object], gates: np.ndarray) -> np.ndarray:
+    """Contribution of each union expert: float64 sum of its slots' gates, ascending slot."""
     U = int(union["U"])
-    flat = np.asarray(gates32, dtype=np.float32).reshape(-1)
+    flat = np.asarray(gates, dtype=np.float64).reshape(-1)
     offsets = union["offsets"]
     perm = union["perm"]
-    scores = np.zeros(U, dtype=np.float32)
+    scores = np.zeros(U, dtype=np.float64)
     for u in range(U):
-        acc = np.float32(0.0)
+        acc = 0.0
         slots = sorted(int(perm[p]) for p in range(int(offsets[u]), int(offsets[u + 1])))
         for s in slots:
-            acc = np.float32(acc + flat[s])
+            acc += float(flat[s])
         scores[u] = acc
     return scores
 
@@ -81,7 +81,7 @@ def apply_budget(ids: np.ndarray, gates: np.ndarray, union: Dict[str, object], C
     nk = n * K
     U = int(union["U"])
     g64 = np.asarray(gates, dtype=np.float64)
-    scores = expert_scores(union, g64.astype(np.float32))
+    scores = expert_scores(union, g64)
     kept = kept_experts(union, scores, C)
     keep = set(kept)
     flat = [int(v) for v in ids.reshape(-1)]

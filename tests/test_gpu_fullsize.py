@@ -142,7 +142,7 @@ def test_one_launch_budget_full_size_sampled(cfg, n, routing, tree, C, tokens):
     bud = oracle.apply_budget(ids, gates, un, C, True)
     sc = np.sort(bud["scores"].astype(np.float64))[::-1]
     # no contribution within float32 reach of the cut: the device sums its own
-    # float32 gates, the oracle the float32 roundings of its float64 ones
+    # float32 gates in float32, the oracle its float64 gates in float64
     assert C >= len(sc) or sc[C - 1] - sc[C] > 1e-5 * n, "near-tie at the cut: another seed"
     w = device_layer_weights(cfg, seed=0, layer=0, device=DEV)
     sh = device_layer_weights(cfg, seed=0, layer=0, device=DEV, shared=True) if cfg.S else None

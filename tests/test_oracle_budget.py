@@ -2,7 +2,7 @@
 
 Against: brute force over every C-subset of the union (the kept set holds the
 largest total contribution), contributions recounted with numpy's weighted
-bincount (float64, independent of the oracle's float32 loop), hand-worked
+bincount (a library formulation the oracle's loop does not use), hand-worked
 examples of the grouping arrays and of the tie rule, the identity when the
 budget is not binding, and the closed form at one token: a budget of C with
 renormalised gates is routing with C experts per token (the softmax over the
@@ -68,10 +68,10 @@ def test_contributions_match_weighted_bincount(seed):
     n, K, E = 5, 3, 9
     ids, gates = _random_routing(g, n, K, E)
     un = oracle.build_union(ids, E)
-    sc = expert_scores(un, gates.astype(np.float32))
+    sc = expert_scores(un, gates)
     ref = np.bincount(ids.reshape(-1), weights=gates.reshape(-1), minlength=E)
     for u in range(un["U"]):
-        assert abs(float(sc[u]) - ref[un["union_ids"][u]]) <= 1e-6
+        assert abs(float(sc[u]) - ref[un["union_ids"][u]]) <= 1e-14
 
 
 @pytest.mark.parametrize("seed", range(8))
