@@ -336,33 +336,44 @@ def test_layer_routing_teams_with_ties(n, E, K):
 
 
 # ------------------------------------ one-launch pass, mode chosen on device
-@pytest.mark.parametrize("cfg,n", [(RAGGED_BF16, 5), (TINY, 4), (RAGGED_F32, 11)])
-def test_layer_auto_mode_follows_eq7(cfg, n):
-    """moe_verify_layer_auto picks deduplication iff (U+S)/(n(K+S)) < r, from
-    the union it counts itself, and then matches that mode's chain bit for bit."""
+@pytest.mark.parametrize("cfg,n,routing", [(RAGGED_BF16, 5, None), (TINY, 4, None),
+                                           (RAGGED_F32, 11, None), (OLMOE, 4, "markov:0.5")])
+def test_layer_auto_mode_follows_eq7(cfg, n, routing):
+    """moe_verify_layer_auto picks deduplication iff (U+S)/(n(K+S)) < r (the
+    expert-bytes page, Eq. (7)), with the mode expected from the oracle's own
+    union; its layer output matches the oracle's pass in that mode within the
+    harness tolerances, its byte counters the oracle's, and (same arithmetic)
+    the chain of entry points of that mode bit for bit."""
     from moe_speculative_decoding_amd.layer import (VerifyBuffers, to_device, verify_layer_auto,
                                                     verify_pass)
-    from gpu_harness import _bits, upload_layer
-    case = make_case(cfg, n, None, seed=31)
-    layer = upload_layer(case)
+    from gpu_harness import _bits, check_vectors, derived_bound, upload_layer
+    case = make_case(cfg, n, routing, seed=31)
+    ref = oracle.verify_op(case, "dedup")
+    U = int(ref["union"]["U"])
+    u = (U + cfg.S) / (n * (cfg.K + cfg.S))
+    refs = {L.MOE_MODE_DEDUP: ref, L.MOE_MODE_PERSLOT: oracle.verify_op(case, "perslot")}
+    layer = upload_layer(case, ref["union"]["union_ids"][:U])
     x, logits = to_device(case.x, DEV), to_device(case.logits, DEV)
     chains = {}
     for mode in (L.MOE_MODE_DEDUP, L.MOE_MODE_PERSLOT):
         chains[mode] = VerifyBuffers(layer, n, DEV)
         verify_pass(layer, chains[mode], x, logits, n, mode)
     torch.cuda.synchronize()
-    U = int(chains[L.MOE_MODE_DEDUP].U.item())
-    u = (U + cfg.S) / (n * (cfg.K + cfg.S))
+    tight = min(cfg.tolerance, derived_bound(cfg))
     buf = VerifyBuffers(layer, n, DEV)
     mode_out = torch.full((1,), -1, dtype=torch.int32, device=DEV)
     for r in (0.0, u * 0.999, u * 1.001, 2.0):
         expect = L.MOE_MODE_DEDUP if u < r else L.MOE_MODE_PERSLOT
-        print("n=%d U=%d u=%.4f r=%.4f expect=%d" % (n, U, u, r, expect), flush=True)
+        print("%s n=%d U=%d u=%.4f r=%.4f expect=%d" % (cfg.name, n, U, u, r, expect), flush=True)
         buf.out.zero_()
         verify_layer_auto(layer, buf, x, logits, n, r, mode_out)
         torch.cuda.synchronize()
         assert L.moe_get_error(buf.ws) == L.MOE_OK
         assert int(mode_out.item()) == expect
-        ref = chains[expect]
-        assert np.array_equal(_bits(buf.out[:n]), _bits(ref.out[:n])), r
-        assert np.array_equal(_bits(buf.bytes), _bits(ref.bytes)), r
+        want = refs[expect]
+        check_vectors(buf.out[:n].float().cpu().numpy(), want["out"], tight, "auto out r=%g" % r)
+        b = buf.bytes.cpu().numpy()
+        expect0 = want["union_bytes"] if expect == L.MOE_MODE_DEDUP else want["requested_bytes"]
+        assert int(b[0]) == expect0 and int(b[1]) == want["requested_bytes"], r
+        chain = chains[expect]
+        assert np.array_equal(_bits(buf.out[:n]), _bits(chain.out[:n])), r
