@@ -220,12 +220,17 @@ moe_status moe_combine(const float* y_slots, const float* gates, const float* y_
  *   ws        workspace of at least moe_workspace_size(shape, n, mode) bytes,
  *             zero-filled before its first use; the call leaves its counters
  *             zero.  Calls sharing a workspace must not overlap in time.
- * The launch fills the device (one workgroup per CU) and its workgroups wait
- * for one another, so all of them must be resident at once: do not run it
- * beside other kernels that hold CUs (another stream's one-launch pass
- * included).  If a workgroup cannot start, the others' bounded waits give up
- * and record MOE_ERR_TIMEOUT instead of hanging; the outputs are then
- * unspecified.
+ * The launch fills the CUs its stream may use (one workgroup per CU; a
+ * stream created with a CU mask gets one workgroup per CU of its mask) and
+ * its workgroups wait for one another, so all of them must be resident at
+ * once: do not run it beside other kernels that hold CUs (another stream's
+ * one-launch pass, or collective kernels on another stream); the chain of
+ * entry points above has no such waits and gives the same results.  If a
+ * workgroup cannot start, the others' bounded waits give up and record
+ * MOE_ERR_TIMEOUT instead of hanging; the outputs are then unspecified.  A
+ * wait gives up after 2^21 polls (about a second), or after the number of
+ * polls in the 32-bit workspace word at byte 192 when that word is nonzero
+ * and smaller (moe_workspace_init leaves it zero).
  * Errors: MOE_ERR_ARG / _UNSUPPORTED / _WORKSPACE on the host; a bounded
  * device wait that gives up records MOE_ERR_TIMEOUT (moe_get_error). */
 moe_status moe_verify_layer(const moe_shape* shape, const moe_weights* w, const float* logits,
@@ -366,6 +371,30 @@ moe_status moe_ecospec_select(const int32_t* parent, const float* q, const uint6
 moe_status moe_bellman_policy(const double* q, const double* cost, int32_t N, int32_t L,
                               double* dp, int32_t* k_best, void* ws, size_t ws_bytes,
                               moe_stream_t stream);
+
+/* One-time layout transform of expert weights into the layouts above
+ * (untimed set-up, not part of a verify pass).  The source layout is the
+ * d x f / f x d matrices of the SwiGLU expert stored row by row (input
+ * feature first), as a caller holding W_gate, W_up [E][d][f] and W_down
+ * [E][f][d] has them:
+ *   src_gate, src_up (device) [count][d][f];  src_down (device) [count][f][d]
+ *   src_s_gate, src_s_up (device, fp8 only) f32 [count][d/128][f/128];
+ *   src_s_down (device, fp8 only) f32 [count][f/128][d/128]
+ * and the outputs are the library's layouts (one row per output feature):
+ *   dst_gate, dst_up [count][f][d];  dst_down [count][d][f];  fp8 scales
+ *   dst_s_gate, dst_s_up [count][f/128][d/128], dst_s_down [count][d/128][f/128]
+ * Every element (and every block scale) is copied bit for bit.  count is E
+ * for the routed experts or S for the shared ones (1 <= count <= 256);
+ * elements are of shape->w_dtype; the caller allocates every buffer and
+ * sources and destinations must not overlap.  The scale arguments are read
+ * only for fp8 weights.
+ * Errors: MOE_ERR_ARG (pointers, count, a destination equal to its source),
+ * MOE_ERR_UNSUPPORTED (dtype, d or f), MOE_ERR_HIP. */
+moe_status moe_pack_weights(const moe_shape* shape, int32_t count, const void* src_gate,
+                            const void* src_up, const void* src_down, const float* src_s_gate,
+                            const float* src_s_up, const float* src_s_down, void* dst_gate,
+                            void* dst_up, void* dst_down, float* dst_s_gate, float* dst_s_up,
+                            float* dst_s_down, moe_stream_t stream);
 
 /* Bytes of workspace any FFN or layer call needs for passes of up to n_max
  * tokens (0 for an invalid shape). */

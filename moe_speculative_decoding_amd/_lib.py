@@ -80,6 +80,7 @@ _SIG = {
     "moe_ecospec_select": (_I, [_P, _P, _P, _P, _I, _I, _I, C.c_double, _P, _P, _P, C.c_size_t,
                                 _P]),
     "moe_bellman_policy": (_I, [_P, _P, _I, _I, _P, _P, _P, C.c_size_t, _P]),
+    "moe_pack_weights": (_I, [C.POINTER(moe_shape), _I] + [_P] * 12 + [_P]),
     "moe_workspace_size": (C.c_size_t, [C.POINTER(moe_shape), _I, _I]),
     "moe_workspace_init": (_I, [_P, C.c_size_t, _P]),
     "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
@@ -239,6 +240,15 @@ def moe_ecospec_select(parent, q, pred, buffer0, N, W, gamma, eps, selected, buf
 def moe_bellman_policy(q, cost, N, L_, dp, k_best, ws, ws_bytes, stream=None) -> None:
     _check(lib.moe_bellman_policy(ptr(q), ptr(cost), N, L_, ptr(dp), ptr(k_best), ptr(ws),
                                   ws_bytes, _stream(stream)), "moe_bellman_policy")
+
+
+def moe_pack_weights(shape: moe_shape, count, src_gate, src_up, src_down, src_s_gate,
+                     src_s_up, src_s_down, dst_gate, dst_up, dst_down, dst_s_gate, dst_s_up,
+                     dst_s_down, stream=None) -> None:
+    _check(lib.moe_pack_weights(C.byref(shape), count, ptr(src_gate), ptr(src_up), ptr(src_down),
+                                ptr(src_s_gate), ptr(src_s_up), ptr(src_s_down), ptr(dst_gate),
+                                ptr(dst_up), ptr(dst_down), ptr(dst_s_gate), ptr(dst_s_up),
+                                ptr(dst_s_down), _stream(stream)), "moe_pack_weights")
 
 
 def moe_workspace_size(shape: moe_shape, n_max: int, mode: int) -> int:

@@ -242,6 +242,7 @@ moe::LayerParams layer_params(const moe_shape* shape, const moe_weights* w, cons
   lp.out = out;
   lp.out_bf16 = out_dtype == MOE_BF16;
   lp.epoch = reinterpret_cast<unsigned*>(base + moe::kEpochOffset);
+  lp.spin = reinterpret_cast<const unsigned*>(base + moe::kSpinOffset);
   lp.up_flags = reinterpret_cast<unsigned*>(base + moe::kFlagsOffset);
   lp.down_flags = lp.up_flags + moe::kMaxGrid;
   return lp;
@@ -552,6 +553,45 @@ moe_status moe_bellman_policy(const double* q, const double* cost, int32_t N, in
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_bellman(q, cost, N, L, dp, k_best, static_cast<uint32_t*>(ws),
                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_pack_weights(const moe_shape* shape, int32_t count, const void* src_gate,
+                            const void* src_up, const void* src_down, const float* src_s_gate,
+                            const float* src_s_up, const float* src_s_down, void* dst_gate,
+                            void* dst_up, void* dst_down, float* dst_s_gate, float* dst_s_up,
+                            float* dst_s_down, moe_stream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (count < 1 || count > kMaxE) return MOE_ERR_ARG;
+  const int es = elem_bytes(shape->w_dtype);
+  const void* src[3] = {src_gate, src_up, src_down};
+  void* dst[3] = {dst_gate, dst_up, dst_down};
+  for (int m = 0; m < 3; ++m) {
+    if (src[m] == nullptr || dst[m] == nullptr || src[m] == dst[m]) return MOE_ERR_ARG;
+    if (!aligned(src[m], es) || !aligned(dst[m], es)) return MOE_ERR_ARG;
+  }
+  const bool fp8 = shape->w_dtype == MOE_FP8_E4M3;
+  const float* ssrc[3] = {src_s_gate, src_s_up, src_s_down};
+  float* sdst[3] = {dst_s_gate, dst_s_up, dst_s_down};
+  if (fp8)
+    for (int m = 0; m < 3; ++m)
+      if (ssrc[m] == nullptr || sdst[m] == nullptr || ssrc[m] == sdst[m] || !aligned(ssrc[m], 4) ||
+          !aligned(sdst[m], 4))
+        return MOE_ERR_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = shape->d, f = shape->f;
+  // gate, up: [count][d][f] -> [count][f][d]; down: [count][f][d] -> [count][d][f]
+  const int rows[3] = {d, d, f}, cols[3] = {f, f, d};
+  for (int m = 0; m < 3; ++m) {
+    st = hip_status(moe::launch_transpose(src[m], dst[m], count, rows[m], cols[m], es, s));
+    if (st != MOE_OK) return st;
+    if (fp8) {
+      st = hip_status(moe::launch_transpose(ssrc[m], sdst[m], count, rows[m] / 128, cols[m] / 128,
+                                            4, s));
+      if (st != MOE_OK) return st;
+    }
+  }
+  return MOE_OK;
 }
 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, moe_stream_t stream) {

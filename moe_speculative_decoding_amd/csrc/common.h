@@ -16,12 +16,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kBlock = 256;  // 4 waves
 // The streaming kernels (expert FFN, one-launch pass) run one workgroup per
-// CU whose wavefronts share the CU's work through an LDS counter: sixteen
-// when the kernel fits 128 VGPRs (four per SIMD), else twelve (168 VGPRs).
-constexpr int kMaxStreamWaves = 16;
-#ifndef MOE_TUNE_NW16
-#define MOE_TUNE_NW16 0
-#endif
+// CU of twelve wavefronts (three per SIMD, at most 168 VGPRs) that share the
+// CU's work through an LDS counter.
+constexpr int kStreamWaves = 12;
+constexpr int kMaxStreamWaves = 16;  // routing scratch is sized for up to this many
 
 enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
 enum { MODE_DEDUP = 0, MODE_PERSLOT = 1, MODE_AUTO = 2 };  // AUTO: the one-launch pass decides
@@ -37,6 +35,9 @@ enum : uint32_t { ERRBIT_BAD_IDS = 1u, ERRBIT_TIMEOUT = 2u, ERRBIT_BAD_TREE = 4u
 constexpr size_t kCtrlBytes = 256;
 constexpr size_t kEpochOffset = 64;
 constexpr size_t kZeroOffset = 128;
+// a nonzero word here replaces kSpinLimit for the one-launch pass (tests
+// lower it to make a bounded wait give up; zero after moe_workspace_init)
+constexpr size_t kSpinOffset = 192;
 constexpr int kMaxGrid = 4096;
 constexpr size_t kFlagsOffset = kCtrlBytes;
 constexpr size_t kHOffset = kFlagsOffset + 2 * kMaxGrid * 4;
@@ -115,28 +116,17 @@ struct LayerParams {
   float r_auto;           // MODE_AUTO: deduplicate iff (U+S) < r_auto * n*(K+S)
   int32_t* mode_out;      // optional: the mode a MODE_AUTO pass ran
   unsigned* epoch;        // call counter of the workspace
+  const unsigned* spin;   // polls of a bounded wait (0: kSpinLimit)
   unsigned* up_flags;     // [kMaxGrid] UP range done (tag of the call)
   unsigned* down_flags;   // [kMaxGrid] DOWN range done
   int budget;             // dedup: keep at most this many routed experts (0: no budget)
   int renorm;             // budget: renormalise the kept gates of a token that lost a slot
 };
 
-// Tile shapes of the FFN phases (rows per wave R, load steps per chunk SPC
-// for UP and DOWN); the defaults are the measured best on MI355X.
-#ifndef MOE_TUNE_RU
-#define MOE_TUNE_RU 1
-#endif
-#ifndef MOE_TUNE_SPCU
-#define MOE_TUNE_SPCU 4
-#endif
-#ifndef MOE_TUNE_RD
-#define MOE_TUNE_RD 4
-#endif
-#ifndef MOE_TUNE_SPCD
-#define MOE_TUNE_SPCD 2
-#endif
-constexpr int kTuneRU = MOE_TUNE_RU, kTuneSPCU = MOE_TUNE_SPCU;
-constexpr int kTuneRD = MOE_TUNE_RD, kTuneSPCD = MOE_TUNE_SPCD;
+// Tile shapes of the dot-product FFN phases (rows per wave R, load steps per
+// chunk SPC for UP and DOWN), the measured best on MI355X.
+constexpr int kRowsUp = 1, kStepsUp = 4;
+constexpr int kRowsDown = 4, kStepsDown = 2;
 
 // token tile: a group serves at most n tokens (a token names an expert once),
 // so the tile is the next power of two of n (up to 32); f32 weights take at
@@ -148,6 +138,8 @@ inline int token_tile(int mode, int n) {
 
 // resident workgroups of a kernel of `block` threads on the current device
 int resident_blocks(const void* fn, size_t smem, int block);
+// CUs a launch on stream s may occupy (its CU mask), 0 if unknown
+int stream_cus(hipStream_t s);
 // dynamic LDS a launch of fn may take on the current device (the device's
 // per-workgroup LDS less fn's static LDS); 0 if the query fails
 size_t lds_budget(const void* fn);
@@ -168,6 +160,9 @@ hipError_t launch_layer(const LayerParams& lp, int w_dtype, hipStream_t s);
 hipError_t launch_combine(const float* y_slots, const float* gates, const float* y_shared,
                           int n, int K, int S, int d, void* out, int out_bf16, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// [count][R][C] -> [count][C][R] of 1-, 2- or 4-byte elements
+hipError_t launch_transpose(const void* src, void* dst, int count, int R, int C, int elem,
+                            hipStream_t s);
 hipError_t launch_ecospec(const int32_t* parent, const float* q, const uint64_t* pred,
                           const uint64_t* buffer0, int N, int W, int gamma, double eps,
                           int32_t* selected, uint64_t* buffer_out, uint32_t* err, hipStream_t s);

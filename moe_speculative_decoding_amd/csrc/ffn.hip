@@ -121,11 +121,29 @@ int resident_blocks(const void* fn, size_t smem, int block) {
   return total;
 }
 
+// CUs a launch on stream s may occupy: the population of the stream's CU
+// mask (a stream created with one, or a process-wide mask), at most the
+// device's CU count; the device's CU count when the query is refused
+int stream_cus(hipStream_t s) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  uint32_t mask[32] = {};
+  if (hipExtStreamGetCUMask(s, 32, mask) != hipSuccess) {
+    (void)hipGetLastError();  // the refusal must not surface as the launch's error
+    return cus;
+  }
+  int n = 0;
+  for (int i = 0; i < cus && i < 32 * 32; ++i) n += static_cast<int>((mask[i / 32] >> (i % 32)) & 1u);
+  return n > 0 ? n : cus;
+}
+
 template <int WT, int TC, int R, int NMAT, int SPC>
 static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
   constexpr bool UP = NMAT == 2;
-  constexpr int NW = (MOE_TUNE_NW16 && TC <= 2 && WT != WT_FP8) ? 16 : 12;
+  constexpr int NW = kStreamWaves;
   constexpr int kStreamBlock = NW * kWave;
   const int rows = UP ? p.f : p.d;
   const int Kdim = UP ? p.d : p.f;
@@ -145,9 +163,6 @@ static hipError_t launch_phase(const FfnParams& p, hipStream_t s) {
   const long long units_max = static_cast<long long>(groups_max) * upg;
   long long grid = resident_blocks(fn, smem, kStreamBlock);
   if (grid <= 0) return hipErrorInvalidConfiguration;
-#ifdef MOE_TUNE_MAXBPC
-  if (grid > 256LL * MOE_TUNE_MAXBPC) grid = 256LL * MOE_TUNE_MAXBPC;
-#endif
   if (grid > units_max) grid = units_max;
   hipLaunchKernelGGL((ffn_stream_kernel<WT, TC, R, NMAT, SPC, NW>), dim3(static_cast<unsigned>(grid)),
                      dim3(kStreamBlock), smem, s, q);

@@ -31,9 +31,10 @@
 //     workgroup has read it), which retires all flags of the call at once.
 //     There are no read-modify-write atomics on shared words: contended
 //     device-scope atomics serialise at the memory side.
-// The grid is the device's resident capacity for the kernel, so every
-// workgroup runs at once; each wait is bounded besides and records a
-// time-out in the error word instead of hanging.
+// The grid is the kernel's resident capacity on the CUs the launch stream may
+// use (its CU mask), so every workgroup runs at once while no other kernel
+// holds CUs; each wait is bounded besides and records a time-out in the
+// error word instead of hanging.
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -60,7 +61,7 @@ static_assert(sizeof(BudgetLds) <= kMaxStreamWaves * sizeof(TopkLds),
 template <int WT, int TC>
 __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt, int U, int NG,
                                            uint8_t* xs, int* tok_h, float** tok_y, RangeTab& rt,
-                                           int* claim, unsigned tag) {
+                                           int* claim, unsigned tag, int limit) {
   using Tl = Tiles<WT, TC>;
   const FfnParams& p = lp.f;
   const int upg_u = units_per_group(p.f, Tl::RU);
@@ -68,7 +69,7 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
   const long long NUu = static_cast<long long>(NG) * upg_u;
   const long long NUd = static_cast<long long>(NG) * upg_d;
   const int G = gridDim.x, b = blockIdx.x;
-  const Sync sy{lp.up_flags, tag, NUu, G, upg_u, p.err};
+  const Sync sy{lp.up_flags, tag, NUu, G, upg_u, p.err, limit};
   {
     const long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
     if (lo < hi)
@@ -97,7 +98,7 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
 template <int WT, int TC, int NW, bool AUTO>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void layer_kernel(LayerParams lp) {
-  constexpr int kStreamWaves = NW, kStreamBlock = NW * kWave;
+  constexpr int kWaves = NW, kStreamBlock = NW * kWave;
   constexpr int TCM = TC;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   __shared__ int tok_h[2 * TCM];
@@ -121,7 +122,9 @@ void layer_kernel(LayerParams lp) {
   // before the launch (the previous call advanced it before it ended); every
   // wavefront loads it, so no wavefront's logits wait behind it
   __shared__ unsigned tag_l;
+  __shared__ int limit_l;
   const unsigned tag_v = coh_load_u32(lp.epoch);  // one request per wavefront
+  const unsigned spin_v = *lp.spin;
   {
     // eight loads per lane in flight at once (clamped in bounds), then the stores
     constexpr int kPer = 8;
@@ -135,10 +138,14 @@ void layer_kernel(LayerParams lp) {
         if (base + i * kStreamBlock + tid < words) lg[base + i * kStreamBlock + tid] = v[i];
     }
   }
-  if (tid == 0) tag_l = tag_v + 1u;
+  if (tid == 0) {
+    tag_l = tag_v + 1u;
+    limit_l = spin_v != 0u && spin_v <= static_cast<unsigned>(kSpinLimit) ? static_cast<int>(spin_v)
+                                                                           : kSpinLimit;
+  }
   __syncthreads();
   TopkLds* tk = reinterpret_cast<TopkLds*>(xs + kRouteTopkOffset);
-  const int team = n <= kStreamWaves / 2 ? kStreamWaves / n : 1;  // wavefronts per token
+  const int team = n <= kWaves / 2 ? kWaves / n : 1;  // wavefronts per token
   if (team > 1) {
     // few tokens: the idle wavefronts share the rank counts
     const int t = wave / team, q = wave - t * team;
@@ -154,7 +161,7 @@ void layer_kernel(LayerParams lp) {
       }
     }
   } else {
-    for (int t = wave; t < n; t += kStreamWaves) {
+    for (int t = wave; t < n; t += kWaves) {
       int id;
       float g;
       route_token(lg + t * E, E, K, lane, tk[wave], id, g);
@@ -226,18 +233,19 @@ void layer_kernel(LayerParams lp) {
 
   // ---- UP range b, then DOWN range b
   const unsigned tag = tag_l;
+  const int limit = limit_l;
   const int NG = mode == MODE_DEDUP ? U + S : n * (K + S);
   const int G = gridDim.x, b = blockIdx.x;
   if (AUTO && TC > 1 && mode == MODE_PERSLOT)
-    run_phases<WT, 1>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag);
+    run_phases<WT, 1>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag, limit);
   else
-    run_phases<WT, TC>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag);
+    run_phases<WT, TC>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag, limit);
 
   // ---- combine: one lane per (token, 4 columns), first workgroups only
   const int quads = p.d / 4;
   const int tasks = n * quads;
   if (b * kStreamBlock >= tasks) return;
-  wait_flags(lp.down_flags, 0, G - 1, tag, p.err);
+  wait_flags(lp.down_flags, 0, G - 1, tag, p.err, limit);
   if (b == 0 && tid == 0)  // every workgroup has read the epoch: retire this call's flags
     __hip_atomic_store(lp.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const unsigned ys_size = static_cast<unsigned>(static_cast<size_t>(nk) * p.d * 4);
@@ -319,9 +327,7 @@ static size_t slot_bytes(const FfnParams& p) {
 
 template <int WT, int TC, bool AUTO>
 static hipError_t launch_layer_t(const LayerParams& lp0, hipStream_t s) {
-  // sixteen wavefronts when the token tiles are small (the kernel then fits
-  // 128 VGPRs), else twelve
-  constexpr int NW = (MOE_TUNE_NW16 && TC <= 2 && WT != WT_FP8) ? 16 : 12;
+  constexpr int NW = kStreamWaves;
   constexpr int kStreamBlock = NW * kWave;
   const FfnParams& p = lp0.f;
   const void* fn = reinterpret_cast<const void*>(&layer_kernel<WT, TC, NW, AUTO>);
@@ -335,6 +341,16 @@ static hipError_t launch_layer_t(const LayerParams& lp0, hipStream_t s) {
   lp.f.lds_slots = 2 * slot <= smem ? 2 : 1;
   lp.f.lds_bytes = static_cast<long long>(smem);
   int grid = resident_blocks(fn, smem, kStreamBlock);
+  if (grid <= 0) return hipErrorInvalidConfiguration;
+  // the workgroups wait for one another, so the grid must fit the CUs this
+  // stream may use: a stream restricted by a CU mask gets a smaller grid
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0) {
+    const int avail = stream_cus(s);
+    if (avail > 0 && avail < cus) grid = grid / cus * avail;
+  }
   if (grid <= 0) return hipErrorInvalidConfiguration;
   if (grid > kMaxGrid) grid = kMaxGrid;
   hipLaunchKernelGGL((layer_kernel<WT, TC, NW, AUTO>), dim3(grid), dim3(kStreamBlock), smem, s, lp);

@@ -74,6 +74,58 @@ hipError_t launch_combine(const float* y_slots, const float* gates, const float*
   return hipGetLastError();
 }
 
+// Batched transpose [count][R][C] -> [count][C][R] of T elements through a
+// 64 x 64 LDS tile (one column of padding, so the transposed reads hit 64
+// different banks): the layout transform of moe_pack_weights.  blockIdx.z is
+// the matrix, blockIdx.y the tile row, blockIdx.x the tile column; every
+// access is bounds-checked, so R and C need not be multiples of 64.
+constexpr int kTile = 64;
+constexpr int kTileRows = 4;  // 256 threads: 64 columns x 4 rows per pass
+
+template <typename T>
+__global__ __launch_bounds__(kTile * kTileRows) void transpose_kernel(
+    const T* __restrict__ src, T* __restrict__ dst, int R, int C) {
+  __shared__ T tile[kTile][kTile + 1];
+  const size_t mat = static_cast<size_t>(R) * C;
+  const T* a = src + blockIdx.z * mat;
+  T* b = dst + blockIdx.z * mat;
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
+  for (int i = ty; i < kTile; i += kTileRows) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) tile[i][tx] = a[static_cast<size_t>(r) * C + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += kTileRows) {
+    const int c = c0 + i, r = r0 + tx;  // row c of the result holds column c of the source
+    if (c < C && r < R) b[static_cast<size_t>(c) * R + r] = tile[tx][i];
+  }
+}
+
+hipError_t launch_transpose(const void* src, void* dst, int count, int R, int C, int elem,
+                            hipStream_t s) {
+  if (count == 0 || R == 0 || C == 0) return hipSuccess;
+  const dim3 grid((C + kTile - 1) / kTile, (R + kTile - 1) / kTile, count);
+  const dim3 block(kTile * kTileRows);
+  switch (elem) {
+    case 1:
+      hipLaunchKernelGGL(transpose_kernel<uint8_t>, grid, block, 0, s,
+                         static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), R, C);
+      break;
+    case 2:
+      hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, block, 0, s,
+                         static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C);
+      break;
+    case 4:
+      hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, block, 0, s,
+                         static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), R, C);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Zero fill with a kernel (no memset node, so it is safe inside captured graphs).
 __global__ __launch_bounds__(kBlock) void fill_zero_kernel(uint32_t* __restrict__ p, size_t words) {
   const size_t stride = static_cast<size_t>(gridDim.x) * kBlock;

@@ -72,16 +72,18 @@ struct Sync {
   int grid;         // workgroups (UP range c = [nu_up*c/grid, nu_up*(c+1)/grid))
   int upg_up;       // UP units per group
   uint32_t* err;
+  int limit;        // polls before a wait gives up
 };
 
 // every lane polls its share of the flags until they hold the tag (bounded:
-// a wait that gives up records a time-out in the error word and goes on)
+// a wait that gives up after `limit` polls records a time-out in the error
+// word and goes on)
 __device__ __forceinline__ void wait_flags(const unsigned* flags, int c_lo, int c_hi, unsigned tag,
-                                           uint32_t* err) {
+                                           uint32_t* err, int limit) {
   for (int c = c_lo + static_cast<int>(threadIdx.x); c <= c_hi; c += static_cast<int>(blockDim.x)) {
     int spins = 0;
     while (coh_load_u32(flags + c) != tag) {
-      if (++spins > kSpinLimit) {
+      if (++spins > limit) {
         atomicOr(err, ERRBIT_TIMEOUT);
         break;
       }
@@ -98,7 +100,7 @@ __device__ __forceinline__ void wait_group_ready(const Sync& sy, int g) {
   const long long u1 = u0 + sy.upg_up - 1;
   const int c_lo = static_cast<int>(((u0 + 1) * sy.grid - 1) / sy.nu_up);
   const int c_hi = static_cast<int>(((u1 + 1) * sy.grid - 1) / sy.nu_up);
-  wait_flags(sy.up_flags, c_lo, c_hi, sy.tag, sy.err);
+  wait_flags(sy.up_flags, c_lo, c_hi, sy.tag, sy.err, sy.limit);
 }
 
 template <int WT>
@@ -411,12 +413,7 @@ __device__ __forceinline__ void wave_unit(int ua, int ub, int s, int wave, int r
 // dot-product path spends about 8*TC VALU operations per 16 weight bytes,
 // which at eight tokens approaches the memory time; one 4x4x4 MFMA block
 // product covers four rows, four tokens and four K elements per lane.
-#ifndef MOE_TUNE_MFMA
-#define MOE_TUNE_MFMA 1
-#endif
-constexpr bool use_mfma(int WT, int TC, int R) {
-  return MOE_TUNE_MFMA && WT != WT_F32 && TC >= 4 && R == 4;
-}
+constexpr bool use_mfma(int WT, int TC, int R) { return WT != WT_F32 && TC >= 4 && R == 4; }
 
 // Tile shapes shared by the two-kernel FFN and the one-launch pass (both must
 // run the same arithmetic): rows per wavefront R and load steps per chunk SPC
@@ -427,10 +424,10 @@ constexpr bool use_mfma(int WT, int TC, int R) {
 template <int WT, int TC>
 struct Tiles {
   static constexpr int TCU = (WT == WT_FP8 && TC > 8) ? 8 : (TC > 16 ? 16 : TC);
-  static constexpr int RU0 = WT == WT_FP8 ? 4 : kTuneRU;
-  static constexpr int SPCU0 = WT == WT_FP8 ? 1 : kTuneSPCU;
-  static constexpr int RD0 = kTuneRD;
-  static constexpr int SPCD0 = WT == WT_FP8 ? 1 : kTuneSPCD;
+  static constexpr int RU0 = WT == WT_FP8 ? 4 : kRowsUp;
+  static constexpr int SPCU0 = WT == WT_FP8 ? 1 : kStepsUp;
+  static constexpr int RD0 = kRowsDown;
+  static constexpr int SPCD0 = WT == WT_FP8 ? 1 : kStepsDown;
   static constexpr bool MFU = use_mfma(WT, TCU, 4), MFD = use_mfma(WT, TC, 4);
   static constexpr int RU = MFU ? 4 : RU0;
   static constexpr int SPCU = MFU ? SPCU0 * RU0 : SPCU0;
@@ -1139,9 +1136,6 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
         unit_info(un, sg, r0, rv);
         load_chunk<WT, TC, R, NMAT, SPC>(p, sg ? G1 : G0, r0, (sg ? v1 : v0) ? rv : 0, kn, rows,
                                          Kdim, lane, bl, sl);
-#ifdef MOE_TUNE_SCHED
-        __builtin_amdgcn_sched_barrier(0);
-#endif
       }
       int sg, r0, rv;
       unit_info(uc, sg, r0, rv);

@@ -342,3 +342,26 @@ def test_noalloc_validation_before_launch():
     need_ys = need + 32 * 8 * 16384 * 4
     assert need_ys > 16 << 20
     assert L.moe_workspace_size(big, 32, L.MOE_MODE_DEDUP) == need_ys
+
+
+def test_pack_weights_validation_before_launch():
+    fn = L.lib.moe_pack_weights
+    s = shape()
+    args = [C.byref(s), 4] + [FAKE] * 3 + [None] * 3 + [FAKE + 1024, FAKE + 2048, FAKE + 4096] + \
+        [None] * 3 + [None]
+    bad = list(args); bad[1] = 0            # no experts
+    assert fn(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[1] = 257
+    assert fn(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[8] = FAKE         # destination equals its source
+    assert fn(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[3] = FAKE + 1     # misaligned bf16 source
+    assert fn(*bad) == L.MOE_ERR_ARG
+    bad = list(args); bad[4] = None
+    assert fn(*bad) == L.MOE_ERR_ARG
+    s8 = shape(w_dtype="fp8_e4m3", d=2048, f=1024)
+    bad = list(args); bad[0] = C.byref(s8)  # fp8 without block scales
+    assert fn(*bad) == L.MOE_ERR_ARG
+    s_bad = shape(d=2044)
+    bad = list(args); bad[0] = C.byref(s_bad)
+    assert fn(*bad) == L.MOE_ERR_UNSUPPORTED
