@@ -145,7 +145,10 @@ void layer_kernel(LayerParams lp) {
   }
   __syncthreads();
   TopkLds* tk = reinterpret_cast<TopkLds*>(xs + kRouteTopkOffset);
-  const int team = n <= kWaves / 2 ? kWaves / n : 1;  // wavefronts per token
+  // wavefronts per token: up to 64 experts a few tokens share their rank
+  // counts among the idle wavefronts; more experts take K rounds of a
+  // wavefront maximum per token (route_token), which needs no team
+  const int team = E <= kWave && n <= kWaves / 2 ? kWaves / n : 1;
   if (team > 1) {
     // few tokens: the idle wavefronts share the rank counts
     const int t = wave / team, q = wave - t * team;

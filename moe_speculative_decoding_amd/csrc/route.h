@@ -79,16 +79,17 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
   return static_cast<int>(u);
 }
 
-// Per-wavefront LDS scratch of the top-K.
+// Per-wavefront LDS scratch of the top-K (the rank loop serves up to 64
+// experts; more take route_token_rounds, which keeps its keys in registers).
 struct TopkLds {
-  unsigned long long key[256];  // 64-bit keys of the token's experts (0 beyond E)
-  int part[256];                // a team member's partial ranks (route_team_*)
+  unsigned long long key[kWave];  // 64-bit keys of the token's experts (0 beyond E)
+  int part[kWave];                // a team member's partial ranks (route_team_*)
   int sel_id[8];
   float sel_l[8];
 };
 
-// One wavefront routes one token (`row` in LDS or global memory); lane l
-// holds experts l, l+64, ..., l+64*(J-1) (E <= 64*J <= 256).  Every expert
+// One wavefront routes one token (`row` in LDS or global memory) of at most
+// 64 experts; lane l holds expert l (J = 1).  Every expert
 // gets a 64-bit key (32-bit value key, then 255 - id, so a larger key is a
 // larger logit or, for equal logits, a lower id), and its rank is the number
 // of keys above it: the experts of rank < K are the top K, in order.  All
@@ -133,6 +134,21 @@ __device__ __forceinline__ void topk_count(const TopkLds& sc, int i0, int i1,
   }
 }
 
+// lane k (< K) takes the k-th selection of sc.sel_id / sc.sel_l and its gate:
+// the softmax over the K selected logits, whose first selection holds the
+// maximum
+__device__ __forceinline__ void topk_finish(int K, int lane, TopkLds& sc, int& my_id,
+                                            float& my_gate) {
+  __builtin_amdgcn_wave_barrier();
+  my_id = lane < K ? sc.sel_id[lane] : 0;
+  const float top = sc.sel_l[0];
+  const float l = lane < K ? sc.sel_l[lane] : top;
+  const float ex = lane < K ? expf(l - top) : 0.0f;
+  // lanes 0..K-1 are all in the first row of 16: its DPP sum is the total
+  my_gate = ex / row_sum_f32(ex);
+  __builtin_amdgcn_wave_barrier();  // the scratch may be reused by the next token
+}
+
 // the experts of rank < K in rank order, and lane k's gate
 template <int J>
 __device__ __forceinline__ void topk_select(const float (&val)[J], const int (&rank)[J], int E,
@@ -146,37 +162,80 @@ __device__ __forceinline__ void topk_select(const float (&val)[J], const int (&r
       sc.sel_l[rank[j]] = val[j];
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  my_id = lane < K ? sc.sel_id[lane] : 0;
-  const float top = sc.sel_l[0];
-  const float l = lane < K ? sc.sel_l[lane] : top;
-  const float ex = lane < K ? expf(l - top) : 0.0f;
-  // lanes 0..K-1 are all in the first row of 16: its DPP sum is the total
-  my_gate = ex / row_sum_f32(ex);
-  __builtin_amdgcn_wave_barrier();  // the scratch may be reused by the next token
+  topk_finish(K, lane, sc, my_id, my_gate);
 }
 
+// The same selection by K rounds of a wavefront-wide maximum, for more than
+// 64 experts: ranking every key costs E*E/64 comparisons per lane (the
+// routing of a 256-expert layer then takes microseconds), K rounds cost
+// K*(E/64 + a dozen cross-lane steps).  Round k takes the largest remaining
+// 32-bit value key and, among the experts holding it, the lowest id: the
+// expert the rank loop ranks k-th.  Lane l holds experts l, l+64, ...
 template <int J>
-__device__ __forceinline__ void route_token_j(const float* __restrict__ row, int E, int K, int lane,
-                                              TopkLds& sc, int& my_id, float& my_gate) {
+__device__ __forceinline__ void route_token_rounds(const float* __restrict__ row, int E, int K,
+                                                   int lane, TopkLds& sc, int& my_id,
+                                                   float& my_gate) {
   float val[J];
-  unsigned long long key[J];
-  topk_keys<J>(row, E, lane, sc, val, key);
-  int rank[J];
+  unsigned vk[J];
 #pragma unroll
-  for (int j = 0; j < J; ++j) rank[j] = 0;
-  topk_count<J>(sc, 0, J * kWave, key, rank);
-  topk_select<J>(val, rank, E, K, lane, sc, my_id, my_gate);
+  for (int j = 0; j < J; ++j) val[j] = row[min(lane + kWave * j, E - 1)];  // all loads first
+#pragma unroll
+  for (int j = 0; j < J; ++j) vk[j] = lane + kWave * j < E ? topk_key(val[j]) : 0u;
+  for (int k = 0; k < K; ++k) {
+    unsigned m = vk[0];
+#pragma unroll
+    for (int j = 1; j < J; ++j) m = max(m, vk[j]);
+    m = row_max_u32(m);
+    const unsigned top =
+        max(max(static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(m), 0)),
+                static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(m), 16))),
+            max(static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(m), 32)),
+                static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(m), 48))));
+    unsigned cand = 0xFFFFu;  // this lane's lowest expert holding the top key
+#pragma unroll
+    for (int j = J - 1; j >= 0; --j)
+      if (vk[j] == top) cand = static_cast<unsigned>(lane + kWave * j);
+    cand = row_min_u32(cand);
+    const unsigned id =
+        min(min(static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(cand), 0)),
+                static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(cand), 16))),
+            min(static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(cand), 32)),
+                static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(cand), 48))));
+    if (lane == static_cast<int>(id & 63u)) {
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (j == static_cast<int>(id >> 6)) {
+          vk[j] = 0u;  // taken
+          sc.sel_id[k] = static_cast<int>(id);
+          sc.sel_l[k] = val[j];
+        }
+    }
+  }
+  topk_finish(K, lane, sc, my_id, my_gate);
 }
 
+// up to 64 experts: lane l holds expert l
+__device__ __forceinline__ void route_token_rank(const float* __restrict__ row, int E, int K,
+                                                 int lane, TopkLds& sc, int& my_id,
+                                                 float& my_gate) {
+  float val[1];
+  unsigned long long key[1];
+  topk_keys<1>(row, E, lane, sc, val, key);
+  int rank[1] = {0};
+  topk_count<1>(sc, 0, kWave, key, rank);
+  topk_select<1>(val, rank, E, K, lane, sc, my_id, my_gate);
+}
+
+// up to 64 experts: rank every key (one comparison per key and lane); more:
+// K rounds of a wavefront maximum
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int K, int lane,
                                             TopkLds& sc, int& my_id, float& my_gate) {
   if (E <= kWave) {
-    route_token_j<1>(row, E, K, lane, sc, my_id, my_gate);
+    route_token_rank(row, E, K, lane, sc, my_id, my_gate);
   } else if (E <= 2 * kWave) {
-    route_token_j<2>(row, E, K, lane, sc, my_id, my_gate);
+    route_token_rounds<2>(row, E, K, lane, sc, my_id, my_gate);
   } else {
-    route_token_j<4>(row, E, K, lane, sc, my_id, my_gate);
+    route_token_rounds<4>(row, E, K, lane, sc, my_id, my_gate);
   }
 }
 
@@ -219,27 +278,16 @@ __device__ __forceinline__ void route_team_select_j(const float* __restrict__ ro
   topk_select<J>(val, rank, E, K, lane, team[0], my_id, my_gate);
 }
 
+// teams serve the rank loop only (E <= 64: one expert per lane)
 __device__ __forceinline__ void route_team_count(const float* __restrict__ row, int E, int lane,
                                                  int q, int S, TopkLds& sc) {
-  if (E <= kWave) {
-    route_team_count_j<1>(row, E, lane, q, S, sc);
-  } else if (E <= 2 * kWave) {
-    route_team_count_j<2>(row, E, lane, q, S, sc);
-  } else {
-    route_team_count_j<4>(row, E, lane, q, S, sc);
-  }
+  route_team_count_j<1>(row, E, lane, q, S, sc);
 }
 
 __device__ __forceinline__ void route_team_select(const float* __restrict__ row, int E, int K,
                                                   int lane, TopkLds* team, int S, int& my_id,
                                                   float& my_gate) {
-  if (E <= kWave) {
-    route_team_select_j<1>(row, E, K, lane, team, S, my_id, my_gate);
-  } else if (E <= 2 * kWave) {
-    route_team_select_j<2>(row, E, K, lane, team, S, my_id, my_gate);
-  } else {
-    route_team_select_j<4>(row, E, K, lane, team, S, my_id, my_gate);
-  }
+  route_team_select_j<1>(row, E, K, lane, team, S, my_id, my_gate);
 }
 
 // ------------------------------------------------------------------ union

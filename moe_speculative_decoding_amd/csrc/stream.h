@@ -591,7 +591,8 @@ __device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt,
     tok_h[threadIdx.x] = hrow;
     tok_y[threadIdx.x] = yrow;
   }
-  for (int v = threadIdx.x; v < TC * vpt; v += blockDim.x) {
+  // vector v of the slot: token v / vpt, elements from (v % vpt) * EPV
+  auto fetch = [&](int v) {
     const int tt = v / vpt;
     const int k = (v - tt * vpt) * EPV;
     u32x4 val = {0u, 0u, 0u, 0u};
@@ -610,8 +611,16 @@ __device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt,
         val = ld16(src + static_cast<size_t>(k) * T::XB);
       }
     }
-    st16(xs + static_cast<size_t>(v) * 16, val);
+    return val;
+  };
+  const int nv = TC * vpt, step = static_cast<int>(blockDim.x);
+  int v = threadIdx.x;
+  for (; v + step < nv; v += 2 * step) {  // two loads in flight before the stores
+    const u32x4 a = fetch(v), b = fetch(v + step);
+    st16(xs + static_cast<size_t>(v) * 16, a);
+    st16(xs + static_cast<size_t>(v + step) * 16, b);
   }
+  if (v < nv) st16(xs + static_cast<size_t>(v) * 16, fetch(v));
 }
 
 // End of a unit whose tile holds at most NT of its TC tokens (the partial
@@ -867,7 +876,10 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     tot += c;
     big |= c > TC;
   }
-  const int trows = tot;
+  // UP with more staged rows than tokens (groups sharing tokens): stage the
+  // n token rows once and let each group index them
+  const bool xtab = UP && tot > p.n;
+  const int trows = xtab ? p.n : tot;
   if (big || static_cast<long long>(trows) * Kpad * 2 > p.lds_bytes) return false;
 
   // the range table (the LDS the previous phase used is free: its last
@@ -900,7 +912,6 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     rt.yrow[j][t] = yrow;
   }
 
-  // first unit of this wavefront, prefetched before the waits and the staging
   const int nur = static_cast<int>(hi - lo);
   u32x4 b0[NMAT][SPC][1], b1[NMAT][SPC][1];
   float s0[NMAT][SPC], s1[NMAT][SPC];
@@ -917,33 +928,18 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     const int valid = G.shared || (G.e >= 0 && G.e < p.E);
     rv = (u < nur && valid) ? min(R, rows - r0) : 0;
   };
-  {
-    Group G;
-    int r0, rv;
-    unit_group(wave, G, r0, rv);
-    load_chunk<WT, TC, R, NMAT, SPC>(p, G, r0, rv, 0, rows, Kdim, lane, b0, s0);
-  }
-  if (UP && threadIdx.x == 0) {
-    for (int j = 0; j < ng; ++j) {
-      Group G;
-      group_at(p, mt, U, g0 + j, G);
-      if (!G.shared && (G.e < 0 || G.e >= p.E)) atomicOr(p.err, ERRBIT_BAD_IDS);
-    }
-  }
-  if (COH && !UP)
-    for (int j = 0; j < ng; ++j) wait_group_ready(sy, g0 + j);
-  __syncthreads();
-
-  // stage the table: the groups' rows of x (UP, bf16) or of H (DOWN: f32
-  // coherent loads rounded to bf16 in one launch, bf16 otherwise); zero
-  // beyond Kdim
-  {
+  // the staged table: rows of x (UP, bf16: token rows when xtab, else each
+  // group's tokens in turn) or each group's rows of H (DOWN: f32 coherent
+  // loads rounded to bf16 in one launch, bf16 otherwise); zero beyond Kdim.
+  // Two loads in flight per thread before their stores.
+  auto stage = [&]() {
     const int vpt = Kpad / 8;
-    for (int v = threadIdx.x; v < trows * vpt; v += blockDim.x) {
+    auto fetch = [&](int v) {
       const int row = v / vpt;
       const int k = (v - row * vpt) * 8;
       u32x4 val = {0u, 0u, 0u, 0u};
       if (k < Kdim) {
+        if (xtab) return ld16(p.x + (static_cast<size_t>(row) * Kdim + k) * 2);
         int j = 0;
         while (j + 1 < ng && rt.row0[j + 1] <= row) ++j;
         if (UP) {
@@ -958,8 +954,45 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
           }
         }
       }
-      st16(xs + static_cast<size_t>(v) * 16, val);
+      return val;
+    };
+    const int nv = trows * vpt, step = static_cast<int>(blockDim.x);
+    int v = threadIdx.x;
+    for (; v + step < nv; v += 2 * step) {
+      const u32x4 a = fetch(v), b = fetch(v + step);
+      st16(xs + static_cast<size_t>(v) * 16, a);
+      st16(xs + static_cast<size_t>(v + step) * 16, b);
     }
+    if (v < nv) st16(xs + static_cast<size_t>(v) * 16, fetch(v));
+  };
+  auto first_chunk = [&]() {
+    Group G;
+    int r0, rv;
+    unit_group(wave, G, r0, rv);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, G, r0, rv, 0, rows, Kdim, lane, b0, s0);
+  };
+  if (UP) {
+    // the table (written above) is read by the staging: publish it; the x
+    // rows are loaded before the first weight chunk, so their LDS stores do
+    // not wait behind it (loads complete in order)
+    __syncthreads();
+    stage();
+    __builtin_amdgcn_sched_barrier(0);
+    first_chunk();
+    if (threadIdx.x == 0) {
+      for (int j = 0; j < ng; ++j) {
+        Group G;
+        group_at(p, mt, U, g0 + j, G);
+        if (!G.shared && (G.e < 0 || G.e >= p.E)) atomicOr(p.err, ERRBIT_BAD_IDS);
+      }
+    }
+  } else {
+    // DOWN: the first chunk is in flight during the wait for the UP flags
+    first_chunk();
+    if (COH)
+      for (int j = 0; j < ng; ++j) wait_group_ready(sy, g0 + j);
+    __syncthreads();
+    stage();
   }
   if (threadIdx.x == 0) *claim = static_cast<int>(blockDim.x) >> 6;
   __syncthreads();
@@ -978,8 +1011,8 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     tga = (nt + 3) >> 2;
 #pragma unroll
     for (int g = 0; g < TG; ++g) {
-      const int t = min(4 * g + (lane & 3), nt - 1);
-      const int row = rt.row0[j] + (t < 0 ? 0 : t);
+      const int t = max(min(4 * g + (lane & 3), nt - 1), 0);
+      const int row = xtab ? rt.xrow[j][t] : rt.row0[j] + t;
       boff[g] = row * Kpad * 2;
     }
   };
@@ -1100,6 +1133,22 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
       return uni(v);
     };
     int u = wave, kc = 0;
+    auto stage_both = [&]() {
+      Walk w;
+      w.G = G0;
+      w.tile = 0;
+      stage_tokens<WT, TC, !UP, COH>(p, mt, w, Kdim, Kpad, xs, tok_h, tok_y);
+      if (g1 != g0) {
+        w.G = G1;
+        stage_tokens<WT, TC, !UP, COH>(p, mt, w, Kdim, Kpad, xs1, tok_h + TC, tok_y + TC);
+      }
+    };
+    // UP: the token rows (cached) are loaded before the first weight chunk,
+    // so their LDS stores do not wait behind it (loads complete in order)
+    // and the chunk is in flight across the barrier; DOWN: the chunk is in
+    // flight during the wait for the UP flags, H is staged after it
+    if (UP) stage_both();
+    __builtin_amdgcn_sched_barrier(0);  // keep the weight loads behind the staging loads
     {
       int sg, r0, rv;
       unit_info(u, sg, r0, rv);
@@ -1110,16 +1159,7 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
       wait_group_ready(sy, g0);
       if (g1 != g0) wait_group_ready(sy, g1);
     }
-    {
-      Walk w;
-      w.G = G0;
-      w.tile = 0;
-      stage_tokens<WT, TC, !UP, COH>(p, mt, w, Kdim, Kpad, xs, tok_h, tok_y);
-      if (g1 != g0) {
-        w.G = G1;
-        stage_tokens<WT, TC, !UP, COH>(p, mt, w, Kdim, Kpad, xs1, tok_h + TC, tok_y + TC);
-      }
-    }
+    if (!UP) stage_both();
     if (threadIdx.x == 0) *claim = static_cast<int>(blockDim.x) >> 6;
     __syncthreads();
     // One half-step prefetches chunk (un, kn) into one buffer and multiplies
