@@ -333,6 +333,15 @@ static hipError_t launch_layer_t(const LayerParams& lp0, hipStream_t s) {
   constexpr int NW = kStreamWaves;
   constexpr int kStreamBlock = NW * kWave;
   const FfnParams& p = lp0.f;
+  // the coherent buffer loads (coh_ld16) take 32-bit byte offsets: the
+  // combine reads y_slots up to slot row n*K + 7 and y_shared up to row
+  // n*S + 3, the DOWN staging H up to row n*(K+S) (+16 bytes); all must stay
+  // below 2^31 (the num_records of H's resource)
+  const unsigned long long kOffLimit = 0x7fffffffull;
+  if ((static_cast<unsigned long long>(p.n) * p.K + 8) * p.d * 4 > kOffLimit ||
+      (static_cast<unsigned long long>(p.n) * p.S + 4) * p.d * 4 > kOffLimit ||
+      static_cast<unsigned long long>(p.n) * (p.K + p.S) * p.f * 4 + 32 > kOffLimit)
+    return hipErrorInvalidValue;
   const void* fn = reinterpret_cast<const void*>(&layer_kernel<WT, TC, NW, AUTO>);
   size_t slot = slot_bytes<WT, TC>(p);
   if (AUTO) slot = std::max(slot, slot_bytes<WT, 1>(p));

@@ -36,8 +36,17 @@ __device__ __forceinline__ unsigned coh_load_u32(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // 16 bytes at base + off with a device-scope buffer load (bytes at or beyond
-// `size` read as zero)
+// `size` read as zero).  The raw buffer load takes a 32-bit byte offset and,
+// with swizzling off and stride 0, returns zero for offset >= num_records
+// without touching memory; the launcher checks that every offset the pass
+// computes fits 31 bits.  The auxiliary operand of gfx940-family buffer
+// instructions holds sc0 (bit 0), nt (bit 1), swz (bit 3) and sc1 (bit 4):
+// bit 3 is not a cache policy but turns on swizzled addressing, under which
+// the range check applies to the record index (0 for a raw load) rather than
+// the byte offset, so an out-of-range offset would be dereferenced.
 constexpr int kAuxSc1 = 16;  // cache-policy operand: sc1
+constexpr int kAuxPolicyBits = 0x1 | 0x2 | 0x10;  // sc0, nt, sc1
+static_assert((kAuxSc1 & ~kAuxPolicyBits) == 0, "aux operand: cache-policy bits only (no swz)");
 __device__ __forceinline__ u32x4 coh_ld16(const void* base, unsigned off, unsigned size) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(base), static_cast<short>(0), static_cast<int>(size), 0x00020000);
@@ -427,7 +436,10 @@ struct Tiles {
   static constexpr int RU0 = WT == WT_FP8 ? 4 : kRowsUp;
   static constexpr int SPCU0 = WT == WT_FP8 ? 1 : kStepsUp;
   static constexpr int RD0 = kRowsDown;
-  static constexpr int SPCD0 = WT == WT_FP8 ? 1 : kStepsDown;
+  // fp8 DOWN: two load steps per chunk, the UP phase's bytes in flight per
+  // wavefront (one step left the DOWN phase ~18% below the UP phase's
+  // bandwidth); the 32-token tile keeps one (its accumulators need the room)
+  static constexpr int SPCD0 = WT == WT_FP8 ? (TC >= 32 ? 1 : 2) : kStepsDown;
   static constexpr bool MFU = use_mfma(WT, TCU, 4), MFD = use_mfma(WT, TC, 4);
   static constexpr int RU = MFU ? 4 : RU0;
   static constexpr int SPCU = MFU ? SPCU0 * RU0 : SPCU0;
