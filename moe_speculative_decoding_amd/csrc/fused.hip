@@ -56,12 +56,25 @@ constexpr size_t kRouteLogitsOffset = kRouteTopkOffset + kMaxStreamWaves * sizeo
 static_assert(sizeof(BudgetLds) <= kMaxStreamWaves * sizeof(TopkLds),
               "the budget tables reuse the top-K scratch");
 
+// DOWN range [lo, hi) with the tile shapes of token tile TC
+template <int WT, int TC>
+__device__ __forceinline__ void run_down(const FfnParams& p, const Meta& mt, int U, long long lo,
+                                         long long hi, uint8_t* xs, int* tok_h, float** tok_y,
+                                         RangeTab& rt, int* claim, const Sync& sy) {
+  using Tl = Tiles<WT, TC>;
+  run_range<WT, TC, Tl::RD, 1, Tl::SPCD, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, claim, sy);
+}
+
 // UP range b, then DOWN range b, with the tile shapes of token tile TC (the
-// two-kernel FFN's shapes for the same tile, so both run the same arithmetic)
+// two-kernel FFN's shapes for the same tile, so both run the same arithmetic;
+// a unit's sums do not depend on the tile that holds its tokens, so a pass
+// whose groups all fit a smaller DOWN tile runs that one, which keeps more
+// weight bytes in flight)
 template <int WT, int TC>
 __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt, int U, int NG,
                                            uint8_t* xs, int* tok_h, float** tok_y, RangeTab& rt,
-                                           int* claim, unsigned tag, int limit) {
+                                           int* claim, int* cpre, int* cpre_d, unsigned tag,
+                                           int limit) {
   using Tl = Tiles<WT, TC>;
   const FfnParams& p = lp.f;
   const int upg_u = units_per_group(p.f, Tl::RU);
@@ -69,9 +82,24 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
   const long long NUu = static_cast<long long>(NG) * upg_u;
   const long long NUd = static_cast<long long>(NG) * upg_d;
   const int G = gridDim.x, b = blockIdx.x;
-  const Sync sy{lp.up_flags, tag, NUu, G, upg_u, p.err, limit};
+  Sync sy{lp.up_flags, tag, NUu, G, upg_u, p.err, limit, nullptr, 0};
+  // a deduplicating pass of more tokens than the small tiles hold splits the
+  // units by cost (stream.h, phase_costs); otherwise by count
+  const bool weighted = TC >= 16 && mt.mode == MODE_DEDUP && NG <= kCostGroups;
+  long long ctot_d = 0;
+  int maxcnt = TC;
+  if (weighted) {
+    sy.ctot = phase_costs<Tl::TCU, true>(p, mt, U, NG, upg_u, cpre);
+    sy.cpre = cpre;
+    ctot_d = phase_costs<TC, false>(p, mt, U, NG, upg_d, cpre_d, cpre_d + kCostGroups + 1);
+    maxcnt = cpre_d[kCostGroups + 1];
+  }
   {
-    const long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
+    long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
+    if (sy.cpre != nullptr) {
+      lo = weighted_first_unit(cpre, NG, upg_u, sy.ctot, G, b, NUu);
+      hi = weighted_first_unit(cpre, NG, upg_u, sy.ctot, G, b + 1, NUu);
+    }
     if (lo < hi)
       run_range<WT, Tl::TCU, Tl::RU, 2, Tl::SPCU, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt,
                                                          claim, sy);
@@ -81,10 +109,22 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
       __hip_atomic_store(lp.up_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   {
-    const long long lo = NUd * b / G, hi = NUd * (b + 1) / G;
-    if (lo < hi)
-      run_range<WT, TC, Tl::RD, 1, Tl::SPCD, true>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, claim,
-                                                    sy);
+    long long lo = NUd * b / G, hi = NUd * (b + 1) / G;
+    if (weighted) {
+      lo = weighted_first_unit(cpre_d, NG, upg_d, ctot_d, G, b, NUd);
+      hi = weighted_first_unit(cpre_d, NG, upg_d, ctot_d, G, b + 1, NUd);
+    }
+    if (lo < hi) {
+      static_assert(Tiles<WT, 8>::RD == Tl::RD && Tiles<WT, 16>::RD == Tl::RD,
+                    "DOWN tiles of one pass share the unit size");
+      if (TC >= 16 && maxcnt <= 8) {
+        run_down<WT, (TC >= 16 ? 8 : TC)>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, claim, sy);
+      } else if (TC >= 32 && maxcnt <= 16) {
+        run_down<WT, (TC >= 32 ? 16 : TC)>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, claim, sy);
+      } else {
+        run_down<WT, TC>(p, mt, U, lo, hi, xs, tok_h, tok_y, rt, claim, sy);
+      }
+    }
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0)
@@ -109,6 +149,8 @@ void layer_kernel(LayerParams lp) {
   __shared__ int U_l;
   __shared__ uint8_t drop_l[kMaxSlots / 8];  // expert budget: bit k of token t = slot dropped
   __shared__ int claim;  // next unit of the running phase (stream.h)
+  __shared__ int cpre[kCostGroups + 1];    // weighted UP partition (stream.h)
+  __shared__ int cpre_d[kCostGroups + 2];  // weighted DOWN partition, then the largest group
   __shared__ RangeTab rt;
   const FfnParams& p = lp.f;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -240,9 +282,9 @@ void layer_kernel(LayerParams lp) {
   const int NG = mode == MODE_DEDUP ? U + S : n * (K + S);
   const int G = gridDim.x, b = blockIdx.x;
   if (AUTO && TC > 1 && mode == MODE_PERSLOT)
-    run_phases<WT, 1>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag, limit);
+    run_phases<WT, 1>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, cpre, cpre_d, tag, limit);
   else
-    run_phases<WT, TC>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, tag, limit);
+    run_phases<WT, TC>(lp, mt, U, NG, xs, tok_h, tok_y, rt, &claim, cpre, cpre_d, tag, limit);
 
   // ---- combine: one lane per (token, 4 columns), first workgroups only
   const int quads = p.d / 4;

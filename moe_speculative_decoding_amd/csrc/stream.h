@@ -82,6 +82,8 @@ struct Sync {
   int upg_up;       // UP units per group
   uint32_t* err;
   int limit;        // polls before a wait gives up
+  const int* cpre;  // weighted UP partition (up_partition), or nullptr
+  long long ctot;   // its total cost
 };
 
 // every lane polls its share of the flags until they hold the tag (bounded:
@@ -104,11 +106,21 @@ __device__ __forceinline__ void wait_flags(const unsigned* flags, int c_lo, int 
 
 // DOWN of group g may start once the workgroups owning g's UP units are done
 __device__ __forceinline__ void wait_group_ready(const Sync& sy, int g) {
-  // owner of UP unit u: the largest c with floor(nu_up * c / grid) <= u
-  const long long u0 = static_cast<long long>(g) * sy.upg_up;
-  const long long u1 = u0 + sy.upg_up - 1;
-  const int c_lo = static_cast<int>(((u0 + 1) * sy.grid - 1) / sy.nu_up);
-  const int c_hi = static_cast<int>(((u1 + 1) * sy.grid - 1) / sy.nu_up);
+  int c_lo, c_hi;
+  if (sy.cpre != nullptr) {
+    // weighted: the owner of unit u is floor(P(u) * grid / ctot), P(u) the
+    // cost of the units before u (group g's units cost w each)
+    const long long p0 = sy.cpre[g], p1 = sy.cpre[g + 1];
+    const long long w = (p1 - p0) / sy.upg_up;
+    c_lo = static_cast<int>(p0 * sy.grid / sy.ctot);
+    c_hi = static_cast<int>((p1 - w) * sy.grid / sy.ctot);
+  } else {
+    // owner of UP unit u: the largest c with floor(nu_up * c / grid) <= u
+    const long long u0 = static_cast<long long>(g) * sy.upg_up;
+    const long long u1 = u0 + sy.upg_up - 1;
+    c_lo = static_cast<int>(((u0 + 1) * sy.grid - 1) / sy.nu_up);
+    c_hi = static_cast<int>(((u1 + 1) * sy.grid - 1) / sy.nu_up);
+  }
   wait_flags(sy.up_flags, c_lo, c_hi, sy.tag, sy.err, sy.limit);
 }
 
@@ -270,6 +282,94 @@ __device__ __forceinline__ void zero_unrouted_rows(const FfnParams& p, const Met
     const long long r = i / p.d;
     p.y_slots[static_cast<size_t>(mt.c[first + r]) * p.d + (i - r * p.d)] = 0.0f;
   }
+}
+
+// Weighted partition of the one-launch pass.  A unit of a group of many
+// tokens can cost more than its bytes:
+//   - UP: a group of more tokens than the UP tile takes the general path,
+//     which streams the group's rows once per token tile, at about 2.3 times
+//     a one-tile unit's time for two tiles (measured on 32-node draft trees);
+//     one-tile units cost the same whatever their tokens (two 4-token groups
+//     of matrix-core work hide under the loads);
+//   - DOWN: every four tokens of the tile add matrix-core and scaling work
+//     per weight byte, about a fifth of a one-token unit's time each.
+// For a deduplicating pass of more tokens than the small tiles hold, a unit
+// of group g costs w_g (UP: 8 for one tile, 9 per tile beyond; DOWN:
+// 3 + ceil(tokens / 4)), and workgroup c owns the units u with
+// floor(P(u) * G / ctot) = c, P(u) the cost of the units before u: equal
+// shares of the work, not of the bytes.  cpre[g] = cost of the units of
+// groups before g (g = 0..NG), built by wavefront 0; returns ctot.
+constexpr int kCostGroups = kMaxSlots + 8;  // U + S <= 256 + 4
+template <int TCP, bool UP>
+__device__ __forceinline__ int unit_cost(int cnt) {
+  if (UP) return cnt <= TCP ? 8 : 9 * ((cnt + TCP - 1) / TCP);
+  int w = 0;
+  for (int t = 0; t < cnt; t += TCP) {
+    const int c = cnt - t < TCP ? cnt - t : TCP;
+    w += 3 + (c + 3) / 4;
+  }
+  return w > 0 ? w : 4;
+}
+// (and *maxcnt = the largest group's token count, when maxcnt is set)
+template <int TCP, bool UP>
+__device__ __forceinline__ long long phase_costs(const FfnParams& p, const Meta& mt, int U, int NG,
+                                                 int upg, int* cpre, int* maxcnt = nullptr) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int carry = 0, mc = 0;
+    if (lane == 0) cpre[0] = 0;
+    for (int base = 0; base < NG; base += kWave) {
+      const int g = base + lane;
+      int w = 0;
+      if (g < NG) {
+        const int cnt = g < U ? mt.a[g + 1] - mt.a[g] : p.n;
+        mc = cnt > mc ? cnt : mc;
+        w = unit_cost<TCP, UP>(cnt) * upg;
+      }
+      // inclusive scan across the wavefront
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(w, o);
+        if (lane >= o) w += v;
+      }
+      if (g < NG) cpre[g + 1] = carry + w;
+      carry += __shfl(w, kWave - 1);
+    }
+    if (maxcnt != nullptr) {
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const int v = __shfl_xor(mc, o);
+        mc = v > mc ? v : mc;
+      }
+      if (lane == 0) *maxcnt = mc;
+    }
+  }
+  __syncthreads();
+  return cpre[NG];
+}
+
+// first unit of workgroup c under the weighted partition: the first u with
+// P(u) * G >= ctot * c (nu for c = G)
+__device__ __forceinline__ long long weighted_first_unit(const int* cpre, int NG, int upg, long long ctot,
+                                                   int G, int c, long long nu) {
+  if (c >= G) return nu;
+  const long long X = ctot * c;
+  // the first group whose last unit qualifies ((cpre[g+1] - w_g) grows with g)
+  int a = 0, z = NG;
+  while (a < z) {
+    const int m = (a + z) >> 1;
+    const long long w = (cpre[m + 1] - cpre[m]) / upg;
+    if ((static_cast<long long>(cpre[m + 1]) - w) * G >= X) {
+      z = m;
+    } else {
+      a = m + 1;
+    }
+  }
+  if (a >= NG) return nu;
+  const long long w = (cpre[a + 1] - cpre[a]) / upg;
+  const long long need = X - static_cast<long long>(cpre[a]) * G;
+  const long long t = need <= 0 ? 0 : (need + w * G - 1) / (w * G);
+  return static_cast<long long>(a) * upg + t;
 }
 
 // token j of a group: its row in x, its row in H and its output row
@@ -1078,20 +1178,13 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
 }
 
 // ------------------------------------------------------------ one range
-// Streams units [lo, hi) of one phase.  UP (NMAT = 2) reads W_gate and W_up
-// rows against the tokens x; DOWN (NMAT = 1) reads W_down rows against H.
-// COH: H and the outputs are exchanged between workgroups of one launch
-// (H in f32 with coherent stores and loads, and each DOWN group waits for the
-// flags of the workgroups that own its UP units); otherwise a kernel boundary
-// separates them.
+// Streams units [lo, hi) of one phase on the dot-product paths (tiles of one
+// or two tokens, and ranges the matrix-core range table does not take).
 template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
-__device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, int U, long long lo,
-                                          long long hi, uint8_t* xs, int* tok_h, float** tok_y,
-                                          RangeTab& rt, int* claim, const Sync& sy) {
+__device__ __forceinline__ void run_range_dot(const FfnParams& p, const Meta& mt, int U,
+                                              long long lo, long long hi, uint8_t* xs, int* tok_h,
+                                              float** tok_y, int* claim, const Sync& sy) {
   using C = StreamCfg<WT, TC, R, NMAT, SPC>;
-  if constexpr (C::MF) {
-    if (run_range_mf<WT, TC, R, NMAT, SPC, COH>(p, mt, U, lo, hi, xs, rt, claim, sy)) return;
-  }
   constexpr bool UP = NMAT == 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = UP ? p.f : p.d;
@@ -1276,6 +1369,22 @@ __device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, in
     cur = nxt;
     walk_next<TC>(p, mt, U, nxt, nchunks, lo, hi, upg);
   }
+}
+
+// Streams units [lo, hi) of one phase.  UP (NMAT = 2) reads W_gate and W_up
+// rows against the tokens x; DOWN (NMAT = 1) reads W_down rows against H.
+// COH: H and the outputs are exchanged between workgroups of one launch
+// (H in f32 with coherent stores and loads, and each DOWN group waits for the
+// flags of the workgroups that own its UP units); otherwise a kernel boundary
+// separates them.
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
+__device__ __forceinline__ void run_range(const FfnParams& p, const Meta& mt, int U, long long lo,
+                                          long long hi, uint8_t* xs, int* tok_h, float** tok_y,
+                                          RangeTab& rt, int* claim, const Sync& sy) {
+  if constexpr (StreamCfg<WT, TC, R, NMAT, SPC>::MF) {
+    if (run_range_mf<WT, TC, R, NMAT, SPC, COH>(p, mt, U, lo, hi, xs, rt, claim, sy)) return;
+  }
+  run_range_dot<WT, TC, R, NMAT, SPC, COH>(p, mt, U, lo, hi, xs, tok_h, tok_y, claim, sy);
 }
 
 }  // namespace moe
