@@ -742,7 +742,7 @@ __device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt,
 template <int WT, int TC, int R, int NMAT, int SPC, bool COH, int NT>
 __device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int r0, int rv, int rows,
                                             int lane, const int* tok_h, float* const* tok_y,
-                                            float* acc) {
+                                            float* acc, float* yb = nullptr, int ystride = 0) {
   constexpr int V = NMAT * R * NT;
   constexpr int SH = 6 - ilog2(V);
   static_assert(NT <= TC && (V & (V - 1)) == 0 && V <= 64 && (NMAT == 1 || V >= 2),
@@ -765,7 +765,9 @@ __device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int r0, 
         const float a = v[0];
         const float h = a / (1.0f + expf(-a)) * u;
         const size_t off = static_cast<size_t>(tok_h[tt]) * rows + r0 + r;
-        if (COH) {
+        if (yb != nullptr) {
+          yb[tt * ystride + r0 + r] = h;
+        } else if (COH) {
           coh_store(reinterpret_cast<float*>(p.H) + off, h);
         } else if (WTraits<WT>::XB == 4) {
           reinterpret_cast<float*>(p.H)[off] = h;
@@ -779,7 +781,9 @@ __device__ __forceinline__ void finish_unit(const FfnParams& p, int nt, int r0, 
       const int idx = lane >> SH;
       const int r = idx / NT, tt = idx - (idx / NT) * NT;
       if (r < rv && tt < nt) {
-        if (COH) {
+        if (yb != nullptr) {
+          yb[tt * ystride + r0 + r] = v[0];
+        } else if (COH) {
           coh_store(tok_y[tt] + r0 + r, v[0]);
         } else {
           tok_y[tt][r0 + r] = v[0];
@@ -866,11 +870,14 @@ __device__ __forceinline__ void mul_chunk_mf(int kc, int lane, const uint8_t* xs
 // token group) across lanes (bits 5 and 4 by halving, then bits 3 and 2), so
 // lane l with bits 2 and 3 clear holds row 2*bit5 + bit4, token l & 3; the
 // gate and up sums of one (row, token) land in the same lane.  Token t of the
-// unit's group (t < nt) writes H row hrows[t] (UP) or output row yrows[t].
+// unit's group (t < nt) writes H row hrows[t] (UP) or output row yrows[t]
+// (DOWN); with an LDS output buffer yb, row r of token t goes to
+// yb[t * ystride + r] instead.
 template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
 __device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int tga, int r0, int rv,
                                                int rows, int lane, const int* hrows,
-                                               float* const* yrows, float* acc) {
+                                               float* const* yrows, float* acc,
+                                               float* yb = nullptr, int ystride = 0) {
   constexpr int TG = TC / 4;
   const bool h5 = (lane & 32) != 0, h4 = (lane & 16) != 0;
   float res[NMAT][TG];
@@ -905,13 +912,17 @@ __device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int t
       const float a = res[0][g];
       const float h = a / (1.0f + expf(-a)) * res[NMAT - 1][g];
       const size_t off = static_cast<size_t>(hrows[tt]) * rows + r0 + r;
-      if (COH) {
+      if (yb != nullptr) {
+        yb[tt * ystride + r0 + r] = h;
+      } else if (COH) {
         coh_store(reinterpret_cast<float*>(p.H) + off, h);
       } else {
         reinterpret_cast<uint16_t*>(p.H)[off] = f32_to_bf16_bits(h);
       }
     } else {
-      if (COH) {
+      if (yb != nullptr) {
+        yb[tt * ystride + r0 + r] = res[0][g];
+      } else if (COH) {
         coh_store(yrows[tt] + r0 + r, res[0][g]);
       } else {
         yrows[tt][r0 + r] = res[0][g];
@@ -928,7 +939,8 @@ __device__ __forceinline__ void mul_finish(int nt, bool last, int kc, int Kpad, 
                                            const u32x4 (&buf)[NMAT][SPC][StreamCfg<WT, TC, R, NMAT, SPC>::LR],
                                            const float (&sc)[NMAT][SPC], float* acc,
                                            const FfnParams& p, int r0, int rv, int rows,
-                                           const int* tok_h, float* const* tok_y) {
+                                           const int* tok_h, float* const* tok_y,
+                                           float* yb = nullptr, int ys = 0) {
   if constexpr (StreamCfg<WT, TC, R, NMAT, SPC>::MF) {
     // tokens staged as one tile [TC][Kpad]: token 4g + q in row 4g + q
     int boff[TC / 4];
@@ -937,10 +949,12 @@ __device__ __forceinline__ void mul_finish(int nt, bool last, int kc, int Kpad, 
     mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, lane, xs, boff, TC / 4, buf, sc, acc);
     if (last)
       finish_unit_mf<WT, TC, R, NMAT, SPC, COH>(p, nt, TC / 4, r0, rv, rows, lane, tok_h, tok_y,
-                                                acc);
+                                                acc, yb, ys);
   } else {
     mul_chunk_nt<WT, TC, R, NMAT, SPC, TC>(kc, Kpad, lane, xs, buf, sc, acc);
-    if (last) finish_unit<WT, TC, R, NMAT, SPC, COH, TC>(p, nt, r0, rv, rows, lane, tok_h, tok_y, acc);
+    if (last)
+      finish_unit<WT, TC, R, NMAT, SPC, COH, TC>(p, nt, r0, rv, rows, lane, tok_h, tok_y, acc, yb,
+                                                 ys);
   }
 }
 
@@ -954,6 +968,9 @@ constexpr int kRangeGroups = 8;  // groups one range may touch on this path
 struct RangeTab {
   int ustart[kRangeGroups + 1];  // first unit of group j, relative to the range
   int cnt[kRangeGroups];         // tokens of group j
+  int ylo[kRangeGroups];         // DOWN output buffer: first row of group j in the range,
+  int ylen[kRangeGroups];        //   its rows in the range,
+  int yoff[kRangeGroups];        //   and its first float in the buffer
   int row0[kRangeGroups];        // first row of group j in the staged table
   int xrow[kRangeGroups][32];    // row of x of token t of group j
   int hrow[kRangeGroups][32];    // H row of token t of group j
@@ -994,6 +1011,33 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
   const int trows = xtab ? p.n : tot;
   if (big || static_cast<long long>(trows) * Kpad * 2 > p.lds_bytes) return false;
 
+  // rows of group j inside the range: [ylo, ylo + ylen)
+  auto out_rows = [&](int j, int& ylo, int& ylen) {
+    const long long gs = static_cast<long long>(g0 + j) * upg;
+    const int ulo = static_cast<int>((gs > lo ? gs : lo) - gs);
+    const int uhi = static_cast<int>((hi < gs + upg ? hi : gs + upg) - gs);
+    ylo = ulo * R;
+    ylen = min(rows, uhi * R) - ylo;
+  };
+  // One-launch pass: the unit outputs (H rows, or slot output rows) collect
+  // in LDS after the table and go out with device-scope stores at the end of
+  // the range.  In the loop, each such store would hold back the weight loads
+  // issued after it until memory acknowledged it (loads and stores complete
+  // in order); without the room, they go out directly.
+  float* ybuf = nullptr;
+  if (COH) {
+    const long long tb = (static_cast<long long>(trows) * Kpad * 2 + 15) / 16 * 16;
+    long long yfl = 0;
+    for (int j = 0; j < ng; ++j) {
+      Group G;
+      group_at(p, mt, U, g0 + j, G);
+      int ylo, ylen;
+      out_rows(j, ylo, ylen);
+      yfl += static_cast<long long>(uni(G.cnt)) * ylen;
+    }
+    if (tb + yfl * 4 <= p.lds_bytes) ybuf = reinterpret_cast<float*>(xs + tb);
+  }
+
   // the range table (the LDS the previous phase used is free: its last
   // barrier has passed)
   if (static_cast<int>(threadIdx.x) < ng) {
@@ -1003,13 +1047,21 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     const long long gs = static_cast<long long>(g0 + j) * upg;
     rt.ustart[j] = static_cast<int>((gs > lo ? gs : lo) - lo);
     rt.cnt[j] = G.cnt;
-    int r = 0;  // rows of the groups before j
+    int r = 0, yo = 0;  // rows of the groups before j, and their outputs
     for (int i = 0; i < j; ++i) {
       Group Gi;
       group_at(p, mt, U, g0 + i, Gi);
       r += Gi.cnt;
+      int ylo, ylen;
+      out_rows(i, ylo, ylen);
+      yo += Gi.cnt * ylen;
     }
     rt.row0[j] = r;
+    int ylo, ylen;
+    out_rows(j, ylo, ylen);
+    rt.ylo[j] = ylo;
+    rt.ylen[j] = ylen;
+    rt.yoff[j] = yo;
     if (j == ng - 1) rt.ustart[ng] = static_cast<int>(hi - lo);
   }
   for (int i = threadIdx.x; i < ng * 32; i += blockDim.x) {
@@ -1109,13 +1161,19 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
   if (threadIdx.x == 0) *claim = static_cast<int>(blockDim.x) >> 6;
   __syncthreads();
 
-  // unit u: group j of the range, its rows, and the B rows of its tokens
-  auto unit_tab = [&](int u, int& j, int& r0, int& rv, int& nt, int& tga, int (&boff)[TG]) {
+  // unit u: group j of the range, its rows, the B rows of its tokens and
+  // where its outputs go in the LDS buffer
+  auto unit_tab = [&](int u, int& j, int& r0, int& rv, int& nt, int& tga, int (&boff)[TG],
+                      float*& yb, int& ys) {
     j = 0;
 #pragma unroll
     for (int i = 1; i < kRangeGroups; ++i)
       if (i < ng && rt.ustart[i] <= u) j = i;
     j = uni(j);
+    if (ybuf != nullptr) {
+      yb = ybuf + rt.yoff[j] - rt.ylo[j];
+      ys = rt.ylen[j];
+    }
     const long long gu = lo + (u < nur ? u : 0);
     r0 = static_cast<int>(gu - static_cast<long long>(g0 + j) * upg) * R;
     rv = u < nur ? min(R, rows - r0) : 0;
@@ -1129,8 +1187,9 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     }
   };
   int u = wave, kc = 0;
-  int j, r0, rv, nt, tga, boff[TG];
-  unit_tab(u, j, r0, rv, nt, tga, boff);
+  int j, r0, rv, nt, tga, boff[TG], ys = 0;
+  float* yb = nullptr;
+  unit_tab(u, j, r0, rv, nt, tga, boff, yb, ys);
   auto half = [&](int un, int kn, u32x4 (&bl)[NMAT][SPC][1], float (&sl)[NMAT][SPC],
                   const u32x4 (&bm)[NMAT][SPC][1], const float (&sm)[NMAT][SPC]) {
     {
@@ -1142,7 +1201,7 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, lane, xs, boff, tga, bm, sm, acc);
     if (kc == nchunks - 1)
       finish_unit_mf<WT, TC, R, NMAT, SPC, COH>(p, nt, tga, r0, rv, rows, lane, rt.hrow[j],
-                                                rt.yrow[j], acc);
+                                                rt.yrow[j], acc, yb, ys);
   };
   auto take = [&]() {
     int v = 0;
@@ -1157,7 +1216,7 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
   while (true) {
     half(un, kn, b1, s1, b0, s0);
     if (un >= nur) break;
-    if (kn == 0) unit_tab(un, j, r0, rv, nt, tga, boff);
+    if (kn == 0) unit_tab(un, j, r0, rv, nt, tga, boff, yb, ys);
     u = un;
     kc = kn;
     if (++kn == nchunks) {
@@ -1166,12 +1225,24 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     }
     half(un, kn, b0, s0, b1, s1);
     if (un >= nur) break;
-    if (kn == 0) unit_tab(un, j, r0, rv, nt, tga, boff);
+    if (kn == 0) unit_tab(un, j, r0, rv, nt, tga, boff, yb, ys);
     u = un;
     kc = kn;
     if (++kn == nchunks) {
       kn = 0;
       un = take();
+    }
+  }
+  if (ybuf != nullptr) {
+    __syncthreads();  // every unit's outputs are in the buffer
+    for (int jj = 0; jj < ng; ++jj) {
+      const int c = rt.cnt[jj], len = rt.ylen[jj], y0 = rt.ylo[jj], off = rt.yoff[jj];
+      for (int i = threadIdx.x; i < c * len; i += blockDim.x) {
+        const int t = i / len, r = i - t * len;
+        float* dst = UP ? reinterpret_cast<float*>(p.H) + static_cast<size_t>(rt.hrow[jj][t]) * rows
+                        : rt.yrow[jj][t];
+        coh_store(dst + y0 + r, ybuf[off + i]);
+      }
     }
   }
   return true;
@@ -1221,6 +1292,27 @@ __device__ __forceinline__ void run_range_dot(const FfnParams& p, const Meta& mt
     const long long g1lo = static_cast<long long>(g0 + 1) * upg;  // first unit of g1
     const size_t slot_bytes = static_cast<size_t>(TC) * Kpad * C::T::XB;
     uint8_t* xs1 = xs + (g1 != g0 ? slot_bytes : 0);
+    // one-launch pass, DOWN: the slot outputs collect in LDS after the token
+    // slots and go out at the end of the range (as on the matrix-core path):
+    // rows [ylo_s, ylo_s + ylen_s) of group g0 (s = 0) and g1 (s = 1).  (UP
+    // writes H directly here: its units span several chunks, and the end of
+    // an UP range is what the DOWN waits are for; measured slower buffered.)
+    float* ybuf = nullptr;
+    int ylo0 = 0, ylen0 = 0, ylo1 = 0, ylen1 = 0;
+    if (COH && !UP) {
+      auto rows_in = [&](long long gs, int& ylo, int& ylen) {
+        const int ulo = static_cast<int>((gs > lo ? gs : lo) - gs);
+        const int uhi = static_cast<int>((hi < gs + upg ? hi : gs + upg) - gs);
+        ylo = ulo * R;
+        ylen = min(rows, uhi * R) - ylo;
+      };
+      rows_in(g1lo - upg, ylo0, ylen0);
+      if (g1 != g0) rows_in(g1lo, ylo1, ylen1);
+      const long long base = ((g1 != g0 ? 2 : 1) * static_cast<long long>(slot_bytes) + 15) / 16 * 16;
+      const long long need = base + 4LL * (static_cast<long long>(G0.cnt) * ylen0 +
+                                           (g1 != g0 ? static_cast<long long>(G1.cnt) * ylen1 : 0));
+      if (need <= p.lds_bytes) ybuf = reinterpret_cast<float*>(xs + base);
+    }
     // Units are handed out dynamically: wavefront w starts with unit w and
     // then takes the next unclaimed unit from the workgroup's LDS counter, so
     // the wavefronts of the CU finish together however the hardware shares
@@ -1284,9 +1376,12 @@ __device__ __forceinline__ void run_range_dot(const FfnParams& p, const Meta& mt
       }
       int sg, r0, rv;
       unit_info(uc, sg, r0, rv);
+      float* yb = nullptr;
+      if (ybuf != nullptr) yb = sg ? ybuf + G0.cnt * ylen0 - ylo1 : ybuf - ylo0;
       mul_finish<WT, TC, R, NMAT, SPC, COH>(sg ? G1.cnt : G0.cnt, kcc == nchunks - 1, kcc, Kpad,
                                             lane, sg ? xs1 : xs, bm, sm, acc, p, r0, rv, rows,
-                                            tok_h + (sg ? TC : 0), tok_y + (sg ? TC : 0));
+                                            tok_h + (sg ? TC : 0), tok_y + (sg ? TC : 0), yb,
+                                            sg ? ylen1 : ylen0);
     };
     int un = u, kn = kc + 1;
     if (kn == nchunks) {
@@ -1309,6 +1404,20 @@ __device__ __forceinline__ void run_range_dot(const FfnParams& p, const Meta& mt
       if (++kn == nchunks) {
         kn = 0;
         un = take();
+      }
+    }
+    if (ybuf != nullptr) {
+      __syncthreads();  // every unit's outputs are in the buffer
+      for (int sg = 0; sg < (g1 != g0 ? 2 : 1); ++sg) {
+        const int c = sg ? G1.cnt : G0.cnt, len = sg ? ylen1 : ylen0, y0 = sg ? ylo1 : ylo0;
+        const float* src = ybuf + (sg ? G0.cnt * ylen0 : 0);
+        for (int i = threadIdx.x; i < c * len; i += blockDim.x) {
+          const int t = i / len, r = i - t * len;
+          float* dst = UP ? reinterpret_cast<float*>(p.H) +
+                                static_cast<size_t>(tok_h[sg * TC + t]) * rows
+                          : tok_y[sg * TC + t];
+          coh_store(dst + y0 + r, src[i]);
+        }
       }
     }
     return;
