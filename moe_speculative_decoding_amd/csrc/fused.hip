@@ -95,7 +95,7 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
     maxcnt = cpre_d[kCostGroups + 1];
   }
   {
-    long long lo = NUu * b / G, hi = NUu * (b + 1) / G;
+    long long lo = div_small(NUu * b, G), hi = div_small(NUu * (b + 1), G);
     if (sy.cpre != nullptr) {
       lo = weighted_first_unit(cpre, NG, upg_u, sy.ctot, G, b, NUu);
       hi = weighted_first_unit(cpre, NG, upg_u, sy.ctot, G, b + 1, NUu);
@@ -109,7 +109,7 @@ __device__ __forceinline__ void run_phases(const LayerParams& lp, const Meta& mt
       __hip_atomic_store(lp.up_flags + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   {
-    long long lo = NUd * b / G, hi = NUd * (b + 1) / G;
+    long long lo = div_small(NUd * b, G), hi = div_small(NUd * (b + 1), G);
     if (weighted) {
       lo = weighted_first_unit(cpre_d, NG, upg_d, ctot_d, G, b, NUd);
       hi = weighted_first_unit(cpre_d, NG, upg_d, ctot_d, G, b + 1, NUd);
@@ -167,6 +167,17 @@ void layer_kernel(LayerParams lp) {
   __shared__ int limit_l;
   const unsigned tag_v = coh_load_u32(lp.epoch);  // one request per wavefront
   const unsigned spin_v = *lp.spin;
+  {
+    // touch every 64-byte line of the argument block now, so the scalar
+    // loads of the streaming set-up hit the scalar cache instead of each
+    // waiting about a microsecond on its first line
+    const unsigned* kw = reinterpret_cast<const unsigned*>(&lp);
+#pragma unroll
+    for (int i = 0; i < static_cast<int>(sizeof(LayerParams) / 4); i += 16) {
+      const unsigned v = kw[i];
+      asm volatile("" ::"s"(v));
+    }
+  }
   {
     // eight loads per lane in flight at once (clamped in bounds), then the stores
     constexpr int kPer = 8;

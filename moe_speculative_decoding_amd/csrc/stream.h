@@ -70,6 +70,20 @@ __device__ __forceinline__ u32x4 coh_h_to_staged(const uint8_t* H, size_t off) {
   return r;
 }
 
+// floor(a / b) for 0 <= a < 2^52 and 0 < b < 2^31 without the 64-bit
+// integer division routine (a few hundred instructions, paid at the start of
+// every phase): the rounded double quotient is within one of the floor,
+// which exact integer products then correct
+__device__ __forceinline__ long long div_small(long long a, long long b) {
+  long long q = static_cast<long long>(static_cast<double>(a) / static_cast<double>(b));
+  if (q * b > a) {
+    --q;
+  } else if ((q + 1) * b <= a) {
+    ++q;
+  }
+  return q;
+}
+
 // Hand-over inside one launch: workgroup c publishes the end of its UP range
 // by storing the call's tag in up_flags[c].  The tag is one more than the
 // epoch word the launch read at its start, so flags of earlier calls never
@@ -118,8 +132,8 @@ __device__ __forceinline__ void wait_group_ready(const Sync& sy, int g) {
     // owner of UP unit u: the largest c with floor(nu_up * c / grid) <= u
     const long long u0 = static_cast<long long>(g) * sy.upg_up;
     const long long u1 = u0 + sy.upg_up - 1;
-    c_lo = static_cast<int>(((u0 + 1) * sy.grid - 1) / sy.nu_up);
-    c_hi = static_cast<int>(((u1 + 1) * sy.grid - 1) / sy.nu_up);
+    c_lo = static_cast<int>(div_small((u0 + 1) * sy.grid - 1, sy.nu_up));
+    c_hi = static_cast<int>(div_small((u1 + 1) * sy.grid - 1, sy.nu_up));
   }
   wait_flags(sy.up_flags, c_lo, c_hi, sy.tag, sy.err, sy.limit);
 }
@@ -402,6 +416,7 @@ __device__ __forceinline__ void token_of(const FfnParams& p, const Meta& mt, con
 
 // a value every lane holds the same, kept in a scalar register
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 
 // ------------------------------------------------------------ the walk
 // One phase (up: gate/up rows, or down rows) is a list of units: (group g,
@@ -994,8 +1009,10 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
   const int nchunks = (Kdim + C::CH - 1) / C::CH;
   const int Kpad = nchunks * C::CH;
   const int upg = units_per_group(rows, R);
-  const int g0 = uni(static_cast<int>(lo / upg));
-  const int ng = uni(static_cast<int>((hi - 1) / upg)) - g0 + 1;
+  // unit indices fit 31 bits (the launcher bounds n, K, S and f)
+  const int g0 = uni(static_cast<int>(static_cast<unsigned>(lo) / static_cast<unsigned>(upg)));
+  const int ng = uni(static_cast<int>(static_cast<unsigned>(hi - 1) / static_cast<unsigned>(upg))) -
+                 g0 + 1;
   if (ng > kRangeGroups) return false;
   int tot = 0, big = 0;
   for (int j = 0; j < ng; ++j) {
@@ -1274,8 +1291,8 @@ __device__ __forceinline__ void run_range_dot(const FfnParams& p, const Meta& mt
   // tile, and LDS has two token slots: stage both up front, then stream with
   // no load other than the weights (a load that must be waited for would,
   // with in-order completion, drain the weight prefetch).
-  const int g0 = uni(static_cast<int>(lo / upg));
-  const int g1 = uni(static_cast<int>((hi - 1) / upg));
+  const int g0 = uni(static_cast<int>(static_cast<unsigned>(lo) / static_cast<unsigned>(upg)));
+  const int g1 = uni(static_cast<int>(static_cast<unsigned>(hi - 1) / static_cast<unsigned>(upg)));
   Group G0, G1;
   group_at(p, mt, U, g0, G0);
   group_at(p, mt, U, g1, G1);
