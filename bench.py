@@ -61,8 +61,9 @@ def parse():
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the OLMoE, Qwen3, DeepSeek-V2-Lite and tree points and the "
                          "budget and selection sweeps")
-    ap.add_argument("--workload", choices=("dsv3", "olmoe"), default="dsv3",
-                    help="the workload of --profile-step / --counters")
+    ap.add_argument("--workload", choices=("dsv3", "olmoe", "dsv3tree"), default="dsv3",
+                    help="the workload of --profile-step / --counters (dsv3tree: the "
+                         "DeepSeek-V3-shaped layer with 32-node draft trees, 2 layers)")
     ap.add_argument("--profile-step", action="store_true",
                     help="replay only the one-launch step graph of --workload (for a kernel "
                          "trace whose layer_kernel dispatches are the step's launches)")
@@ -533,14 +534,20 @@ def main():
     torch.cuda.set_device(0)
     DEDUP, SLOT = L.MOE_MODE_DEDUP, L.MOE_MODE_PERSLOT
 
+    tree = False
+    if args.workload == "dsv3tree" and not (args.counters or args.profile_step):
+        print("--workload dsv3tree is for --counters and --profile-step", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "olmoe":
         cfg, nlayers, routings, ns = OLMOE, args.olmoe_layers, ("markov:0.5",), (1, 2, 4, 8)
+    elif args.workload == "dsv3tree":
+        cfg, nlayers, routings, ns, tree = DSV3, 2, ("markov:0.5", "iid"), (32,), True
     else:
         cfg, nlayers, routings, ns = DSV3, args.layers, HEADLINE_ROUTINGS, HEADLINE_NS
     log("generating %d layers of %s weights on the device" % (nlayers, cfg.name))
     run = Runner(cfg, nlayers, dev)
     keys = [(routing, n) for routing in routings for n in ns]
-    by_key = {k: run.ops(*k) for k in keys}
+    by_key = {k: run.ops(*k, tree=tree) for k in keys}
     ops = [op for k in keys for op in by_key[k]]
     light = args.profile_step or args.counters
     # (profile-step mode: deduplicating launches only, so the kernel trace
