@@ -219,6 +219,33 @@ def test_ffn_dsv3_expert_shape_tree32():
     run_case(make_case(DSV3_E16, 32, "markov:0.5", seed=0, tree=True))
 
 
+# 32 tokens on the fp8 path whose union holds groups of 12 and 10 tokens and
+# many of 1-8: the one-launch pass splits its ranges by cost (the two large
+# groups exceed the 8-token UP tile and take the general path, one pass per
+# tile), and its DOWN phase runs the 16-token tile although the pass is
+# compiled for 32; the chain of entry points runs the 32-token DOWN tile, and
+# the two must agree bit for bit (run_case) and with the oracle
+FP8_SMALL = LayerConfig(name="fp8_small", cfg_id=84, E=32, K=4, d=512, f=256, S=0,
+                        w_dtype="fp8_e4m3", x_dtype="bf16", n_values=(32,),
+                        routing=("iid",), tolerance=3e-2)
+
+
+def test_ffn_fp8_groups_beyond_the_up_tile():
+    import dataclasses
+    case = make_case(FP8_SMALL, 32, "iid", seed=3)
+    lg = case.logits.copy()
+    lg[:, 0] = -10.0
+    lg[:, 1] = -10.0
+    lg[:12, 0] = 10.0
+    lg[12:22, 1] = 10.0
+    case = dataclasses.replace(case, logits=lg)
+    ref = oracle.verify_op(case, "dedup")
+    un = ref["union"]
+    counts = np.diff(np.asarray(un["offsets"][:int(un["U"]) + 1]))
+    assert counts.max() == 12 and sorted(counts)[-2] == 10
+    run_case(case, ref=ref)
+
+
 # ------------------------------------------------------- invalid expert ids
 def test_perslot_bad_id_gives_zero_row_and_error():
     from moe_speculative_decoding_amd.layer import VerifyBuffers
