@@ -96,7 +96,7 @@ struct Sync {
   int upg_up;       // UP units per group
   uint32_t* err;
   int limit;        // polls before a wait gives up
-  const int* cpre;  // weighted UP partition (up_partition), or nullptr
+  const int* cpre;  // weighted UP partition (phase_costs), or nullptr
   long long ctot;   // its total cost
 };
 
@@ -126,8 +126,8 @@ __device__ __forceinline__ void wait_group_ready(const Sync& sy, int g) {
     // cost of the units before u (group g's units cost w each)
     const long long p0 = sy.cpre[g], p1 = sy.cpre[g + 1];
     const long long w = (p1 - p0) / sy.upg_up;
-    c_lo = static_cast<int>(p0 * sy.grid / sy.ctot);
-    c_hi = static_cast<int>((p1 - w) * sy.grid / sy.ctot);
+    c_lo = static_cast<int>(div_small(p0 * sy.grid, sy.ctot));
+    c_hi = static_cast<int>(div_small((p1 - w) * sy.grid, sy.ctot));
   } else {
     // owner of UP unit u: the largest c with floor(nu_up * c / grid) <= u
     const long long u0 = static_cast<long long>(g) * sy.upg_up;
@@ -364,8 +364,9 @@ __device__ __forceinline__ long long phase_costs(const FfnParams& p, const Meta&
 
 // first unit of workgroup c under the weighted partition: the first u with
 // P(u) * G >= ctot * c (nu for c = G)
-__device__ __forceinline__ long long weighted_first_unit(const int* cpre, int NG, int upg, long long ctot,
-                                                   int G, int c, long long nu) {
+__device__ __forceinline__ long long weighted_first_unit(const int* cpre, int NG, int upg,
+                                                         long long ctot, int G, int c,
+                                                         long long nu) {
   if (c >= G) return nu;
   const long long X = ctot * c;
   // the first group whose last unit qualifies ((cpre[g+1] - w_g) grows with g)
@@ -417,18 +418,19 @@ __device__ __forceinline__ void token_of(const FfnParams& p, const Meta& mt, con
 // a value every lane holds the same, kept in a scalar register
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-
 // ------------------------------------------------------------ the walk
 // One phase (up: gate/up rows, or down rows) is a list of units: (group g,
 // block of R rows), groups in order, row blocks in order.  Workgroup b owns
 // the contiguous unit range [b*NU/G, (b+1)*NU/G), so every workgroup streams
 // the same bytes to within one unit of R rows (a unit per wavefront, not per
 // workgroup: coarser units left workgroups with one or two of them, and the
-// ones with two set the phase's time).  Inside a group segment of the range
-// the four wavefronts take consecutive units, one step of four units at a
-// time; the walk goes chunk by chunk (K split in chunks of SPC load steps):
-// for each group segment, for each token tile of that group, for each step,
-// for each chunk.  The walk is the same for every lane of the workgroup.
+// ones with two set the phase's time); passes with groups of many tokens
+// split by cost instead (phase_costs).  On the general path, inside a group
+// segment of the range the wavefronts take consecutive units, one unit each
+// per step; the walk goes chunk by chunk (K split in chunks of SPC load
+// steps): for each group segment, for each token tile of that group, for
+// each step, for each chunk.  The walk is the same for every lane of the
+// workgroup.
 
 // units (blocks of R rows) of one group
 __host__ __device__ constexpr int units_per_group(int rows, int R) { return (rows + R - 1) / R; }
