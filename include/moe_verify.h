@@ -415,6 +415,21 @@ moe_status moe_byte_counts(const moe_shape* shape, int32_t n, int32_t U,
  * moe_verify_layer_noalloc scratch (MOE_OK if no such call ran there). */
 moe_status moe_get_error(void* ws, moe_stream_t stream);
 
+/* Diagnostic, host-only: the unit partition the one-launch pass uses for one
+ * phase, computed with the same code on the host.  counts[ng] (host) are the
+ * tokens of each group (0..32); tile = 0 splits the ng * upg units evenly
+ * over `grid` workgroups, tile = 8, 16 or 32 splits them by the cost a unit
+ * of a group of that many tokens has with that token tile (up != 0: the UP
+ * phase, else DOWN), as deduplicating passes of more than 8 tokens do.
+ * Outputs (host): first_unit[grid + 1], workgroup c owning units
+ * [first_unit[c], first_unit[c + 1]); optionally owner_lo[ng], owner_hi[ng],
+ * the first and last workgroup owning a unit of each group, as the DOWN
+ * phase's waits compute them (both NULL or both set).  upg = units per
+ * group, 1..16384; grid 1..4096; ng 1..264.  Errors: MOE_ERR_ARG. */
+moe_status moe_unit_partition(const int32_t* counts, int32_t ng, int32_t tile, int32_t up,
+                              int32_t upg, int32_t grid, int64_t* first_unit, int32_t* owner_lo,
+                              int32_t* owner_hi);
+
 /* Diagnostic: decode `count` E4M3FN codes (device) to f32 (device) with the
  * same conversion the fp8 FFN kernels use. */
 moe_status moe_decode_fp8(const uint8_t* codes, float* out, int64_t count,

@@ -86,6 +86,7 @@ _SIG = {
     "moe_byte_counts": (_I, [C.POINTER(moe_shape), _I, _I, C.POINTER(C.c_uint64),
                              C.POINTER(C.c_uint64)]),
     "moe_get_error": (_I, [_P, _P]),
+    "moe_unit_partition": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_decode_fp8": (_I, [_P, _P, C.c_int64, _P]),
     "moe_status_str": (C.c_char_p, [_I]),
     "moe_last_hip_error": (_I, []),
@@ -269,6 +270,21 @@ def moe_get_error(ws, stream=None) -> int:
     """Status of the device error word (also returned, not raised); ws=None reads
     the error word of moe_verify_layer_noalloc's scratch on the current device."""
     return int(lib.moe_get_error(ptr(ws), _stream(stream)))
+
+
+def moe_unit_partition(counts, tile: int, up: bool, upg: int, grid: int):
+    """The one-launch pass's unit partition of one phase, computed on the host:
+    (first_unit [grid + 1], owner_lo [ng], owner_hi [ng]) as numpy arrays."""
+    import numpy as np
+    cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    ng = int(cnt.size)
+    first = np.zeros(grid + 1, dtype=np.int64)
+    lo = np.zeros(max(ng, 1), dtype=np.int32)
+    hi = np.zeros(max(ng, 1), dtype=np.int32)
+    _check(lib.moe_unit_partition(cnt.ctypes.data, ng, tile, 1 if up else 0, upg, grid,
+                                  first.ctypes.data, lo.ctypes.data, hi.ctypes.data),
+           "moe_unit_partition")
+    return first, lo[:ng], hi[:ng]
 
 
 def moe_decode_fp8(codes, out, count, stream=None) -> None:

@@ -5,8 +5,10 @@
 #include "moe_verify.h"
 
 #include <mutex>
+#include <vector>
 
 #include "common.h"
+#include "partition.h"
 
 // moe_verify_layer_noalloc keeps its workspace (control block, hand-over
 // flags, H and the slot outputs the caller keeps none of) in this array.
@@ -636,6 +638,32 @@ moe_status moe_get_error(void* ws, moe_stream_t stream) {
   if (word & moe::ERRBIT_BAD_IDS) return MOE_ERR_BAD_IDS;
   if (word & moe::ERRBIT_BAD_TREE) return MOE_ERR_BAD_TREE;
   return MOE_ERR_TIMEOUT;
+}
+
+moe_status moe_unit_partition(const int32_t* counts, int32_t ng, int32_t tile, int32_t up,
+                              int32_t upg, int32_t grid, int64_t* first_unit, int32_t* owner_lo,
+                              int32_t* owner_hi) {
+  if (counts == nullptr || first_unit == nullptr || ng < 1 || ng > moe::kCostGroups ||
+      upg < 1 || upg > 16384 || grid < 1 || grid > moe::kMaxGrid ||
+      (tile != 0 && tile != 8 && tile != 16 && tile != 32) || (owner_lo == nullptr) != (owner_hi == nullptr))
+    return MOE_ERR_ARG;
+  for (int g = 0; g < ng; ++g)
+    if (counts[g] < 0 || counts[g] > 32) return MOE_ERR_ARG;
+  const long long nu = static_cast<long long>(ng) * upg;
+  std::vector<int> cpre(static_cast<size_t>(ng) + 1, 0);
+  long long ctot = nu;
+  if (tile > 0) {
+    for (int g = 0; g < ng; ++g) cpre[g + 1] = cpre[g] + moe::unit_cost(counts[g], tile, up != 0) * upg;
+    ctot = cpre[ng];
+  }
+  for (int c = 0; c <= grid; ++c)
+    first_unit[c] = tile > 0 ? moe::weighted_first_unit(cpre.data(), ng, upg, ctot, grid, c, nu)
+                             : moe::div_small(nu * c, grid);
+  if (owner_lo != nullptr)
+    for (int g = 0; g < ng; ++g)
+      moe::group_owners(tile > 0 ? cpre.data() : nullptr, ctot, nu, grid, upg, g, owner_lo[g],
+                        owner_hi[g]);
+  return MOE_OK;
 }
 
 moe_status moe_decode_fp8(const uint8_t* codes, float* out, int64_t count, moe_stream_t stream) {

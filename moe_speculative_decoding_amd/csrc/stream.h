@@ -21,6 +21,7 @@
 #pragma once
 
 #include "common.h"
+#include "partition.h"
 
 namespace moe {
 
@@ -70,20 +71,6 @@ __device__ __forceinline__ u32x4 coh_h_to_staged(const uint8_t* H, size_t off) {
   return r;
 }
 
-// floor(a / b) for 0 <= a < 2^52 and 0 < b < 2^31 without the 64-bit
-// integer division routine (a few hundred instructions, paid at the start of
-// every phase): the rounded double quotient is within one of the floor,
-// which exact integer products then correct
-__device__ __forceinline__ long long div_small(long long a, long long b) {
-  long long q = static_cast<long long>(static_cast<double>(a) / static_cast<double>(b));
-  if (q * b > a) {
-    --q;
-  } else if ((q + 1) * b <= a) {
-    ++q;
-  }
-  return q;
-}
-
 // Hand-over inside one launch: workgroup c publishes the end of its UP range
 // by storing the call's tag in up_flags[c].  The tag is one more than the
 // epoch word the launch read at its start, so flags of earlier calls never
@@ -121,20 +108,7 @@ __device__ __forceinline__ void wait_flags(const unsigned* flags, int c_lo, int 
 // DOWN of group g may start once the workgroups owning g's UP units are done
 __device__ __forceinline__ void wait_group_ready(const Sync& sy, int g) {
   int c_lo, c_hi;
-  if (sy.cpre != nullptr) {
-    // weighted: the owner of unit u is floor(P(u) * grid / ctot), P(u) the
-    // cost of the units before u (group g's units cost w each)
-    const long long p0 = sy.cpre[g], p1 = sy.cpre[g + 1];
-    const long long w = (p1 - p0) / sy.upg_up;
-    c_lo = static_cast<int>(div_small(p0 * sy.grid, sy.ctot));
-    c_hi = static_cast<int>(div_small((p1 - w) * sy.grid, sy.ctot));
-  } else {
-    // owner of UP unit u: the largest c with floor(nu_up * c / grid) <= u
-    const long long u0 = static_cast<long long>(g) * sy.upg_up;
-    const long long u1 = u0 + sy.upg_up - 1;
-    c_lo = static_cast<int>(div_small((u0 + 1) * sy.grid - 1, sy.nu_up));
-    c_hi = static_cast<int>(div_small((u1 + 1) * sy.grid - 1, sy.nu_up));
-  }
+  group_owners(sy.cpre, sy.ctot, sy.nu_up, sy.grid, sy.upg_up, g, c_lo, c_hi);
   wait_flags(sy.up_flags, c_lo, c_hi, sy.tag, sy.err, sy.limit);
 }
 
@@ -313,17 +287,7 @@ __device__ __forceinline__ void zero_unrouted_rows(const FfnParams& p, const Met
 // floor(P(u) * G / ctot) = c, P(u) the cost of the units before u: equal
 // shares of the work, not of the bytes.  cpre[g] = cost of the units of
 // groups before g (g = 0..NG), built by wavefront 0; returns ctot.
-constexpr int kCostGroups = kMaxSlots + 8;  // U + S <= 256 + 4
-template <int TCP, bool UP>
-__device__ __forceinline__ int unit_cost(int cnt) {
-  if (UP) return cnt <= TCP ? 8 : 9 * ((cnt + TCP - 1) / TCP);
-  int w = 0;
-  for (int t = 0; t < cnt; t += TCP) {
-    const int c = cnt - t < TCP ? cnt - t : TCP;
-    w += 3 + (c + 3) / 4;
-  }
-  return w > 0 ? w : 4;
-}
+static_assert(kCostGroups >= kMaxSlots + 4, "cost tables hold U + S groups");
 // (and *maxcnt = the largest group's token count, when maxcnt is set)
 template <int TCP, bool UP>
 __device__ __forceinline__ long long phase_costs(const FfnParams& p, const Meta& mt, int U, int NG,
@@ -338,7 +302,7 @@ __device__ __forceinline__ long long phase_costs(const FfnParams& p, const Meta&
       if (g < NG) {
         const int cnt = g < U ? mt.a[g + 1] - mt.a[g] : p.n;
         mc = cnt > mc ? cnt : mc;
-        w = unit_cost<TCP, UP>(cnt) * upg;
+        w = unit_cost(cnt, TCP, UP) * upg;
       }
       // inclusive scan across the wavefront
 #pragma unroll
@@ -360,31 +324,6 @@ __device__ __forceinline__ long long phase_costs(const FfnParams& p, const Meta&
   }
   __syncthreads();
   return cpre[NG];
-}
-
-// first unit of workgroup c under the weighted partition: the first u with
-// P(u) * G >= ctot * c (nu for c = G)
-__device__ __forceinline__ long long weighted_first_unit(const int* cpre, int NG, int upg,
-                                                         long long ctot, int G, int c,
-                                                         long long nu) {
-  if (c >= G) return nu;
-  const long long X = ctot * c;
-  // the first group whose last unit qualifies ((cpre[g+1] - w_g) grows with g)
-  int a = 0, z = NG;
-  while (a < z) {
-    const int m = (a + z) >> 1;
-    const long long w = (cpre[m + 1] - cpre[m]) / upg;
-    if ((static_cast<long long>(cpre[m + 1]) - w) * G >= X) {
-      z = m;
-    } else {
-      a = m + 1;
-    }
-  }
-  if (a >= NG) return nu;
-  const long long w = (cpre[a + 1] - cpre[a]) / upg;
-  const long long need = X - static_cast<long long>(cpre[a]) * G;
-  const long long t = need <= 0 ? 0 : (need + w * G - 1) / (w * G);
-  return static_cast<long long>(a) * upg + t;
 }
 
 // token j of a group: its row in x, its row in H and its output row
