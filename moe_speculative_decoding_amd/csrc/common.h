@@ -19,6 +19,10 @@ constexpr int kBlock = 256;  // 4 waves
 // CU of twelve wavefronts (three per SIMD, at most 168 VGPRs) that share the
 // CU's work through an LDS counter.
 constexpr int kStreamWaves = 12;
+// Their block size as a constant: device code that reads blockDim.x gets it
+// through a global load, and the wait for that load (loads complete in
+// order) would first drain every weight load in flight.
+constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kMaxStreamWaves = 16;  // routing scratch is sized for up to this many
 
 enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };

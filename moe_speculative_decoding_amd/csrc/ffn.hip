@@ -22,6 +22,7 @@ namespace moe {
 template <int WT, int TC, int R, int NMAT, int SPC, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void ffn_stream_kernel(FfnParams p) {
+  static_assert(NW == kStreamWaves, "the streaming core runs kStreamThreads threads");
   constexpr bool UP = NMAT == 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   __shared__ int tok_h[2 * TC];

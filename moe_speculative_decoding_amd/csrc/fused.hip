@@ -139,6 +139,7 @@ template <int WT, int TC, int NW, bool AUTO>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void layer_kernel(LayerParams lp) {
   constexpr int kWaves = NW, kStreamBlock = NW * kWave;
+  static_assert(NW == kStreamWaves, "the streaming core runs kStreamThreads threads");
   constexpr int TCM = TC;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   __shared__ int tok_h[2 * TCM];

@@ -92,7 +92,7 @@ struct Sync {
 // word and goes on)
 __device__ __forceinline__ void wait_flags(const unsigned* flags, int c_lo, int c_hi, unsigned tag,
                                            uint32_t* err, int limit) {
-  for (int c = c_lo + static_cast<int>(threadIdx.x); c <= c_hi; c += static_cast<int>(blockDim.x)) {
+  for (int c = c_lo + static_cast<int>(threadIdx.x); c <= c_hi; c += kStreamThreads) {
     int spins = 0;
     while (coh_load_u32(flags + c) != tag) {
       if (++spins > limit) {
@@ -251,11 +251,11 @@ __device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
   const int nk = p.n * p.K;
   if (threadIdx.x == 0) m.mode = p.mode;
   if (p.mode == MODE_DEDUP) {
-    for (int i = threadIdx.x; i <= p.ucap; i += blockDim.x) m.a[i] = p.offsets[i];
-    for (int i = threadIdx.x; i < p.ucap; i += blockDim.x) m.b[i] = p.union_ids[i];
-    for (int i = threadIdx.x; i < nk; i += blockDim.x) m.c[i] = p.perm[i];
+    for (int i = threadIdx.x; i <= p.ucap; i += kStreamThreads) m.a[i] = p.offsets[i];
+    for (int i = threadIdx.x; i < p.ucap; i += kStreamThreads) m.b[i] = p.union_ids[i];
+    for (int i = threadIdx.x; i < nk; i += kStreamThreads) m.c[i] = p.perm[i];
   } else {
-    for (int i = threadIdx.x; i < nk; i += blockDim.x) m.a[i] = p.ids[i];
+    for (int i = threadIdx.x; i < nk; i += kStreamThreads) m.a[i] = p.ids[i];
   }
 }
 
@@ -265,8 +265,8 @@ __device__ __forceinline__ void load_meta(const FfnParams& p, Meta& m) {
 __device__ __forceinline__ void zero_unrouted_rows(const FfnParams& p, const Meta& mt, int U) {
   const int nk = p.n * p.K, first = mt.a[U];
   const long long total = static_cast<long long>(nk - first) * p.d;
-  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<long long>(gridDim.x) * blockDim.x) {
+  for (long long i = static_cast<long long>(blockIdx.x) * kStreamThreads + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * kStreamThreads) {
     const long long r = i / p.d;
     p.y_slots[static_cast<size_t>(mt.c[first + r]) * p.d + (i - r * p.d)] = 0.0f;
   }
@@ -436,7 +436,7 @@ __device__ __forceinline__ void walk_group(const FfnParams& p, const Meta& mt, i
   const long long glo = static_cast<long long>(g) * upg;
   w.ua = uni(static_cast<int>((lo > glo ? lo : glo) - glo));
   w.ub = uni(static_cast<int>((hi < glo + upg ? hi : glo + upg) - glo));
-  const int nw = static_cast<int>(blockDim.x) >> 6;
+  const int nw = kStreamWaves;
   w.nsteps = (w.ub - w.ua + nw - 1) / nw;
   w.s = 0;
   w.kc = 0;
@@ -464,7 +464,7 @@ __device__ __forceinline__ void walk_next(const FfnParams& p, const Meta& mt, in
 template <int R>
 __device__ __forceinline__ void wave_unit(int ua, int ub, int s, int wave, int rows, int& r0,
                                           int& rv) {
-  const int unit = ua + s * (static_cast<int>(blockDim.x) >> 6) + wave;
+  const int unit = ua + s * kStreamWaves + wave;
   r0 = unit * R;
   rv = unit < ub ? min(R, rows - r0) : 0;
 }
@@ -681,7 +681,7 @@ __device__ __forceinline__ void stage_tokens(const FfnParams& p, const Meta& mt,
     }
     return val;
   };
-  const int nv = TC * vpt, step = static_cast<int>(blockDim.x);
+  const int nv = TC * vpt, step = kStreamThreads;
   int v = threadIdx.x;
   for (; v + step < nv; v += 2 * step) {  // two loads in flight before the stores
     const u32x4 a = fetch(v), b = fetch(v + step);
@@ -1022,7 +1022,7 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     rt.yoff[j] = yo;
     if (j == ng - 1) rt.ustart[ng] = static_cast<int>(hi - lo);
   }
-  for (int i = threadIdx.x; i < ng * 32; i += blockDim.x) {
+  for (int i = threadIdx.x; i < ng * 32; i += kStreamThreads) {
     const int j = i >> 5, t = i & 31;
     Group G;
     group_at(p, mt, U, g0 + j, G);
@@ -1078,7 +1078,7 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
       }
       return val;
     };
-    const int nv = trows * vpt, step = static_cast<int>(blockDim.x);
+    const int nv = trows * vpt, step = kStreamThreads;
     int v = threadIdx.x;
     for (; v + step < nv; v += 2 * step) {
       const u32x4 a = fetch(v), b = fetch(v + step);
@@ -1116,7 +1116,7 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     __syncthreads();
     stage();
   }
-  if (threadIdx.x == 0) *claim = static_cast<int>(blockDim.x) >> 6;
+  if (threadIdx.x == 0) *claim = kStreamWaves;
   __syncthreads();
 
   // unit u: group j of the range, its rows, the B rows of its tokens and
@@ -1195,7 +1195,7 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     __syncthreads();  // every unit's outputs are in the buffer
     for (int jj = 0; jj < ng; ++jj) {
       const int c = rt.cnt[jj], len = rt.ylen[jj], y0 = rt.ylo[jj], off = rt.yoff[jj];
-      for (int i = threadIdx.x; i < c * len; i += blockDim.x) {
+      for (int i = threadIdx.x; i < c * len; i += kStreamThreads) {
         const int t = i / len, r = i - t * len;
         float* dst = UP ? reinterpret_cast<float*>(p.H) + static_cast<size_t>(rt.hrow[jj][t]) * rows
                         : rt.yrow[jj][t];
@@ -1315,7 +1315,7 @@ __device__ __forceinline__ void run_range_dot(const FfnParams& p, const Meta& mt
       if (g1 != g0) wait_group_ready(sy, g1);
     }
     if (!UP) stage_both();
-    if (threadIdx.x == 0) *claim = static_cast<int>(blockDim.x) >> 6;
+    if (threadIdx.x == 0) *claim = kStreamWaves;
     __syncthreads();
     // One half-step prefetches chunk (un, kn) into one buffer and multiplies
     // chunk (u, kc) from the other.  The loop runs whole pairs of half-steps,
@@ -1369,7 +1369,7 @@ __device__ __forceinline__ void run_range_dot(const FfnParams& p, const Meta& mt
       for (int sg = 0; sg < (g1 != g0 ? 2 : 1); ++sg) {
         const int c = sg ? G1.cnt : G0.cnt, len = sg ? ylen1 : ylen0, y0 = sg ? ylo1 : ylo0;
         const float* src = ybuf + (sg ? G0.cnt * ylen0 : 0);
-        for (int i = threadIdx.x; i < c * len; i += blockDim.x) {
+        for (int i = threadIdx.x; i < c * len; i += kStreamThreads) {
           const int t = i / len, r = i - t * len;
           float* dst = UP ? reinterpret_cast<float*>(p.H) +
                                 static_cast<size_t>(tok_h[sg * TC + t]) * rows
