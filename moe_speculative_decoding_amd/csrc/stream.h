@@ -828,8 +828,9 @@ __device__ __forceinline__ void mul_chunk_mf(int kc, int lane, const uint8_t* xs
 // gate and up sums of one (row, token) land in the same lane.  Token t of the
 // unit's group (t < nt) writes H row hrows[t] (UP) or output row yrows[t]
 // (DOWN); with an LDS output buffer yb, row r of token t goes to
-// yb[t * ystride + r] instead.
-template <int WT, int TC, int R, int NMAT, int SPC, bool COH>
+// yb[t * ystride + r] instead.  BUF: yb is always given, and no global store
+// is compiled in (the one-launch streaming loop).
+template <int WT, int TC, int R, int NMAT, int SPC, bool COH, bool BUF = false>
 __device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int tga, int r0, int rv,
                                                int rows, int lane, const int* hrows,
                                                float* const* yrows, float* acc,
@@ -868,7 +869,7 @@ __device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int t
       const float a = res[0][g];
       const float h = a / (1.0f + expf(-a)) * res[NMAT - 1][g];
       const size_t off = static_cast<size_t>(hrows[tt]) * rows + r0 + r;
-      if (yb != nullptr) {
+      if (BUF || yb != nullptr) {
         yb[tt * ystride + r0 + r] = h;
       } else if (COH) {
         coh_store(reinterpret_cast<float*>(p.H) + off, h);
@@ -876,7 +877,7 @@ __device__ __forceinline__ void finish_unit_mf(const FfnParams& p, int nt, int t
         reinterpret_cast<uint16_t*>(p.H)[off] = f32_to_bf16_bits(h);
       }
     } else {
-      if (yb != nullptr) {
+      if (BUF || yb != nullptr) {
         yb[tt * ystride + r0 + r] = res[0][g];
       } else if (COH) {
         coh_store(yrows[tt] + r0 + r, res[0][g]);
@@ -979,9 +980,12 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
   };
   // One-launch pass: the unit outputs (H rows, or slot output rows) collect
   // in LDS after the table and go out with device-scope stores at the end of
-  // the range.  In the loop, each such store would hold back the weight loads
-  // issued after it until memory acknowledged it (loads and stores complete
-  // in order); without the room, they go out directly.
+  // the range, so the streaming loop holds no global store.  A store there
+  // would hold back the weight loads issued after it until memory
+  // acknowledged it (loads and stores complete in order), and the compiler,
+  // which counts stores and loads on one counter, would wait for every load
+  // in flight before each multiply (the prefetch drained every step).  A
+  // range without room for the buffer takes the dot-product path.
   float* ybuf = nullptr;
   if (COH) {
     const long long tb = (static_cast<long long>(trows) * Kpad * 2 + 15) / 16 * 16;
@@ -994,6 +998,7 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
       yfl += static_cast<long long>(uni(G.cnt)) * ylen;
     }
     if (tb + yfl * 4 <= p.lds_bytes) ybuf = reinterpret_cast<float*>(xs + tb);
+    if (ybuf == nullptr) return false;
   }
 
   // the range table (the LDS the previous phase used is free: its last
@@ -1040,13 +1045,15 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
   float acc[C::NACC];
 #pragma unroll
   for (int i = 0; i < C::NACC; ++i) acc[i] = 0.0f;
+  // (32-bit unit arithmetic: the 64-bit division routine in the loop holds
+  // a wait for every load in flight on its slow path)
   auto unit_group = [&](int u, Group& G, int& r0, int& rv) {
-    const long long gu = lo + (u < nur ? u : 0);
-    const int g = static_cast<int>(gu / upg);
+    const unsigned gu = static_cast<unsigned>(lo) + static_cast<unsigned>(u < nur ? u : 0);
+    const int g = static_cast<int>(gu / static_cast<unsigned>(upg));
     group_at(p, mt, U, g, G);
     G.e = uni(G.e);
     G.shared = uni(G.shared);
-    r0 = static_cast<int>(gu - static_cast<long long>(g) * upg) * R;
+    r0 = static_cast<int>(gu - static_cast<unsigned>(g) * static_cast<unsigned>(upg)) * R;
     const int valid = G.shared || (G.e >= 0 && G.e < p.E);
     rv = (u < nur && valid) ? min(R, rows - r0) : 0;
   };
@@ -1158,8 +1165,8 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     }
     mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, lane, xs, boff, tga, bm, sm, acc);
     if (kc == nchunks - 1)
-      finish_unit_mf<WT, TC, R, NMAT, SPC, COH>(p, nt, tga, r0, rv, rows, lane, rt.hrow[j],
-                                                rt.yrow[j], acc, yb, ys);
+      finish_unit_mf<WT, TC, R, NMAT, SPC, COH, COH>(p, nt, tga, r0, rv, rows, lane, rt.hrow[j],
+                                                     rt.yrow[j], acc, yb, ys);
   };
   auto take = [&]() {
     int v = 0;
