@@ -616,6 +616,34 @@ __device__ __forceinline__ void load_chunk(
   }
 }
 
+// Matrix-core chunk loads from a unit's precomputed bases: wrow[m] = the
+// unit's first row of matrix m, sblk[m] = the scales of its 128-row block
+// (the per-chunk address math then stays 32-bit)
+template <int WT, int TC, int R, int NMAT, int SPC>
+__device__ __forceinline__ void load_chunk_mf(const uint8_t* const (&wrow)[NMAT],
+                                              const float* const (&sblk)[NMAT], unsigned row_bytes,
+                                              int rv, int kc, int Kdim, int lane,
+                                              const uint8_t* zeros, u32x4 (&buf)[NMAT][SPC][1],
+                                              float (&sc)[NMAT][SPC]) {
+  using C = StreamCfg<WT, TC, R, NMAT, SPC>;
+  using T = typename C::T;
+  const int i = lane & 3, b = lane >> 2;
+  const bool rok = i < rv;
+  const unsigned roff = static_cast<unsigned>(i) * row_bytes;
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+      const int k = kc * C::CH + s * C::STEP + b * T::VEC;
+      const bool ok = rok && k < Kdim;
+      const uint8_t* a = ok ? wrow[m] + (roff + static_cast<unsigned>(k) * T::EB) : zeros;
+      buf[m][s][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+      if (WT == WT_FP8)
+        sc[m][s] = *(ok ? sblk[m] + (k >> 7) : reinterpret_cast<const float*>(zeros));
+    }
+  }
+}
+
 template <int WT, int TC, int R, int NMAT, int SPC, int NT>
 __device__ __forceinline__ void mul_chunk_nt(int kc, int Kpad, int lane, const uint8_t* xs,
                                              const u32x4 (&buf)[NMAT][SPC][StreamCfg<WT, TC, R, NMAT, SPC>::LR],
@@ -1155,14 +1183,41 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
   int j, r0, rv, nt, tga, boff[TG], ys = 0;
   float* yb = nullptr;
   unit_tab(u, j, r0, rv, nt, tga, boff, yb, ys);
+  // the bases of the unit whose chunks are loaded next, recomputed when it
+  // changes: the 64-bit address products stay out of the per-chunk code,
+  // whose temporaries otherwise took registers of loads in flight (and the
+  // compiler then waited for every load before reusing them)
+  const size_t row_bytes = static_cast<size_t>(Kdim) * C::T::EB;
+  const size_t mat = static_cast<size_t>(rows) * row_bytes;
+  const int kb = Kdim / 128;
+  int nb_u = -1, nb_rv = 0;
+  const uint8_t* nb_w[NMAT];
+  const float* nb_s[NMAT];
+  auto unit_base = [&](int c) {
+    Group G;
+    int r0;
+    unit_group(c, G, r0, nb_rv);
+    const int e = nb_rv > 0 ? G.e : 0;
+    const int rr = nb_rv > 0 ? r0 : 0;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      nb_w[m] = (NMAT == 1 ? wptr<2>(p, G.shared)
+                           : (m == 0 ? wptr<0>(p, G.shared) : wptr<1>(p, G.shared))) +
+                static_cast<size_t>(e) * mat + static_cast<size_t>(rr) * row_bytes;
+      if (WT == WT_FP8)
+        nb_s[m] = (NMAT == 1 ? sptr<2>(p, G.shared)
+                             : (m == 0 ? sptr<0>(p, G.shared) : sptr<1>(p, G.shared))) +
+                  (static_cast<size_t>(e) * (rows / 128) + rr / 128) * kb;
+      else
+        nb_s[m] = nullptr;
+    }
+    nb_u = c;
+  };
   auto half = [&](int un, int kn, u32x4 (&bl)[NMAT][SPC][1], float (&sl)[NMAT][SPC],
                   const u32x4 (&bm)[NMAT][SPC][1], const float (&sm)[NMAT][SPC]) {
-    {
-      Group G;
-      int q0, qv;
-      unit_group(un, G, q0, qv);
-      load_chunk<WT, TC, R, NMAT, SPC>(p, G, q0, qv, kn, rows, Kdim, lane, bl, sl);
-    }
+    if (un != nb_u) unit_base(un);
+    load_chunk_mf<WT, TC, R, NMAT, SPC>(nb_w, nb_s, static_cast<unsigned>(row_bytes), nb_rv, kn,
+                                        Kdim, lane, p.zeros, bl, sl);
     mul_chunk_mf<WT, TC, R, NMAT, SPC>(kc, lane, xs, boff, tga, bm, sm, acc);
     if (kc == nchunks - 1)
       finish_unit_mf<WT, TC, R, NMAT, SPC, COH, COH>(p, nt, tga, r0, rv, rows, lane, rt.hrow[j],
