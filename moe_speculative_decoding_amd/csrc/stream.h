@@ -1029,44 +1029,6 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     if (ybuf == nullptr) return false;
   }
 
-  // the range table (the LDS the previous phase used is free: its last
-  // barrier has passed)
-  if (static_cast<int>(threadIdx.x) < ng) {
-    const int j = threadIdx.x;
-    Group G;
-    group_at(p, mt, U, g0 + j, G);
-    const long long gs = static_cast<long long>(g0 + j) * upg;
-    rt.ustart[j] = static_cast<int>((gs > lo ? gs : lo) - lo);
-    rt.cnt[j] = G.cnt;
-    int r = 0, yo = 0;  // rows of the groups before j, and their outputs
-    for (int i = 0; i < j; ++i) {
-      Group Gi;
-      group_at(p, mt, U, g0 + i, Gi);
-      r += Gi.cnt;
-      int ylo, ylen;
-      out_rows(i, ylo, ylen);
-      yo += Gi.cnt * ylen;
-    }
-    rt.row0[j] = r;
-    int ylo, ylen;
-    out_rows(j, ylo, ylen);
-    rt.ylo[j] = ylo;
-    rt.ylen[j] = ylen;
-    rt.yoff[j] = yo;
-    if (j == ng - 1) rt.ustart[ng] = static_cast<int>(hi - lo);
-  }
-  for (int i = threadIdx.x; i < ng * 32; i += kStreamThreads) {
-    const int j = i >> 5, t = i & 31;
-    Group G;
-    group_at(p, mt, U, g0 + j, G);
-    int xrow = 0, hrow = 0;
-    float* yrow = nullptr;
-    if (t < G.cnt) token_of(p, mt, G, t, xrow, hrow, yrow);
-    rt.xrow[j][t] = xrow;
-    rt.hrow[j][t] = hrow;
-    rt.yrow[j][t] = yrow;
-  }
-
   const int nur = static_cast<int>(hi - lo);
   u32x4 b0[NMAT][SPC][1], b1[NMAT][SPC][1];
   float s0[NMAT][SPC], s1[NMAT][SPC];
@@ -1085,6 +1047,64 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     const int valid = G.shared || (G.e >= 0 && G.e < p.E);
     rv = (u < nur && valid) ? min(R, rows - r0) : 0;
   };
+  auto first_chunk = [&]() {
+    Group G;
+    int r0, rv;
+    unit_group(wave, G, r0, rv);
+    load_chunk<WT, TC, R, NMAT, SPC>(p, G, r0, rv, 0, rows, Kdim, lane, b0, s0);
+  };
+  // DOWN: the first weight chunk goes out before the range table is built,
+  // so the table is built while it is in flight (and while the UP owners of
+  // the range's groups finish)
+  if (!UP) first_chunk();
+
+  // the range table (the LDS the previous phase used is free: its last
+  // barrier has passed)
+  // (lane j of wavefront 0 takes group j; the staged rows and the buffered
+  // outputs of the groups before j are exclusive prefix sums across lanes)
+  if (static_cast<int>(threadIdx.x) < kWave) {
+    const int j = threadIdx.x;
+    int c = 0, yl = 0;
+    if (j < ng) {
+      Group G;
+      group_at(p, mt, U, g0 + j, G);
+      const long long gs = static_cast<long long>(g0 + j) * upg;
+      rt.ustart[j] = static_cast<int>((gs > lo ? gs : lo) - lo);
+      rt.cnt[j] = G.cnt;
+      int ylo, ylen;
+      out_rows(j, ylo, ylen);
+      rt.ylo[j] = ylo;
+      rt.ylen[j] = ylen;
+      c = G.cnt;
+      yl = G.cnt * ylen;
+      if (j == ng - 1) rt.ustart[ng] = static_cast<int>(hi - lo);
+    }
+    int r = c, yo = yl;  // inclusive sums over lanes 0..j (ng <= kRangeGroups = 8)
+#pragma unroll
+    for (int o = 1; o < kRangeGroups; o <<= 1) {
+      const int a = __shfl_up(r, o), b = __shfl_up(yo, o);
+      if (j >= o) {
+        r += a;
+        yo += b;
+      }
+    }
+    if (j < ng) {
+      rt.row0[j] = r - c;
+      rt.yoff[j] = yo - yl;
+    }
+  }
+  for (int i = threadIdx.x; i < ng * 32; i += kStreamThreads) {
+    const int j = i >> 5, t = i & 31;
+    Group G;
+    group_at(p, mt, U, g0 + j, G);
+    int xrow = 0, hrow = 0;
+    float* yrow = nullptr;
+    if (t < G.cnt) token_of(p, mt, G, t, xrow, hrow, yrow);
+    rt.xrow[j][t] = xrow;
+    rt.hrow[j][t] = hrow;
+    rt.yrow[j][t] = yrow;
+  }
+
   // the staged table: rows of x (UP, bf16: token rows when xtab, else each
   // group's tokens in turn) or each group's rows of H (DOWN: f32 coherent
   // loads rounded to bf16 in one launch, bf16 otherwise); zero beyond Kdim.
@@ -1122,12 +1142,6 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
     }
     if (v < nv) st16(xs + static_cast<size_t>(v) * 16, fetch(v));
   };
-  auto first_chunk = [&]() {
-    Group G;
-    int r0, rv;
-    unit_group(wave, G, r0, rv);
-    load_chunk<WT, TC, R, NMAT, SPC>(p, G, r0, rv, 0, rows, Kdim, lane, b0, s0);
-  };
   if (UP) {
     // the table (written above) is read by the staging: publish it; the x
     // rows are loaded before the first weight chunk, so their LDS stores do
@@ -1144,8 +1158,8 @@ __device__ __forceinline__ bool run_range_mf(const FfnParams& p, const Meta& mt,
       }
     }
   } else {
-    // DOWN: the first chunk is in flight during the wait for the UP flags
-    first_chunk();
+    // DOWN: the first chunk (issued above) is in flight during the wait for
+    // the UP flags
     if (COH)
       for (int j = 0; j < ng; ++j) wait_group_ready(sy, g0 + j);
     __syncthreads();
