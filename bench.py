@@ -55,8 +55,9 @@ def parse():
                     help="DeepSeek-V3-shaped layers of weights (11.3 GB each)")
     ap.add_argument("--olmoe-layers", type=int, default=8)
     ap.add_argument("--reps", type=int, default=20, help="graph replays per point timing")
-    ap.add_argument("--cpu-experts", type=int, default=12,
-                    help="union experts per pass in the CPU baseline's sample")
+    ap.add_argument("--cpu-experts", type=int, default=64,
+                    help="union experts per pass in the CPU baseline's sample (64: the "
+                         "whole union of every pass of up to 8 tokens)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the OLMoE, Qwen3, DeepSeek-V2-Lite and tree points and the "
@@ -264,10 +265,11 @@ def fits(points, ns, b_e, K, S):
 def cpu_baseline(cfg, n_experts):
     """The oracle as it stands on a bounded sample of the headline workload:
     the passes n = 1 and n = 8 (independent routing, layer 0), each limited to
-    its first `n_experts` union experts with every slot routed to them (route,
-    union, the deduplicating FFN of those experts, combine; weight decode
-    included, generation excluded).  Once on one thread, once on every host
-    core (the sample's experts split over a thread pool, one oracle call each)."""
+    its first `n_experts` union experts with every slot routed to them (by
+    default the whole union: route, union, the deduplicating FFN of those
+    experts, combine; weight decode included, generation excluded).  Once on
+    one thread, once on every host core (the sample's experts split over a
+    thread pool, one oracle call each)."""
     from concurrent.futures import ThreadPoolExecutor
 
     from threadpoolctl import threadpool_info, threadpool_limits
@@ -282,36 +284,41 @@ def cpu_baseline(cfg, n_experts):
         ids, _ = oracle.route_topk(case.logits, cfg.K)
         un = oracle.build_union(ids, cfg.E)
         m = min(int(un["U"]), n_experts)
-        for u in range(m):
-            case.expert(int(un["union_ids"][u]))  # generate before the clock starts
-        samples.append((n, case, m))
+        # generate the weights before the clock starts (numpy releases the GIL)
+        gen = [int(e) for e in un["union_ids"][:m]] + [cfg.E + s for s in range(cfg.S)]
+        with ThreadPoolExecutor(cores) as ex:
+            list(ex.map(case.expert, gen))
+        samples.append((n, case, m, int(un["U"])))
 
     def run(case, m, threads):
         t0 = time.perf_counter()
         ids, gates = oracle.route_topk(case.logits, cfg.K)
         un = oracle.build_union(ids, cfg.E)
 
-        def part(u0, u1):
+        def part(job):
+            u0, u1, S = job  # union experts [u0, u1) and the first S shared experts
             sub = {"U": u1 - u0, "union_ids": un["union_ids"][u0:u1],
                    "offsets": un["offsets"][u0:u1 + 1], "perm": un["perm"]}
-            return oracle.ffn_dedup(case.x, ids, sub, case.expert, case.shared, cfg.S,
+            return oracle.ffn_dedup(case.x, ids, sub, case.expert, case.shared, S,
                                     cfg.w_dtype, cfg.x_dtype, cfg.d, cfg.f)
 
         if threads == 1:
-            y, _, read = part(0, m)
+            y, ysh, read = part((0, m, cfg.S))
         else:
+            jobs = [(u, u + 1, 0) for u in range(m)] + [(0, 0, cfg.S)]
             with ThreadPoolExecutor(threads) as ex:
-                parts = list(ex.map(lambda u: part(u, u + 1), range(m)))
+                parts = list(ex.map(part, jobs))
             y = sum(p[0] for p in parts)  # each part fills its own slots' rows
+            ysh = parts[-1][1]
             read = sum(p[2] for p in parts)
-        oracle.combine(y, gates, None)
+        oracle.combine(y, gates, ysh)
         return time.perf_counter() - t0, read
 
     res = {}
     for threads in (1, cores):
         tot_b, tot_t, per = 0, 0.0, {}
         with threadpool_limits(limits=1):
-            for n, case, m in samples:
+            for n, case, m, _ in samples:
                 t, read = run(case, m, threads)
                 tot_b += read
                 tot_t += t
@@ -325,10 +332,15 @@ def cpu_baseline(cfg, n_experts):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
+    whole = all(m == U for _, _, m, U in samples)
+    scope = ("each pass whole (all %s union experts%s)"
+             % ("/".join(str(U) for _, _, _, U in samples),
+                " + %d shared" % cfg.S if cfg.S else "") if whole else
+             "each limited to its first %d union experts and every slot routed to them"
+             % n_experts)
     sample = ("float64 numpy oracle (route, union, deduplicating FFN incl. fp8 weight decode, "
-              "combine) on the %s layer, independent routing, passes n=1 and n=8, each limited to "
-              "its first %d union experts and every slot routed to them; GB/s on the union bytes "
-              "of the sampled experts" % (cfg.name, n_experts))
+              "combine) on the %s layer, layer 0, independent routing, passes n=1 and n=8, %s; "
+              "GB/s on the union bytes of the sampled experts" % (cfg.name, scope))
     return {"value": res[cores]["value"], "unit": "GB/s", "cores": cores, "kind": "oracle",
             "cpu": model, "blas": ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()})),
             "sample": sample + "; %d threads (one oracle "
