@@ -55,12 +55,16 @@ def _expert_to_host(w, e, cfg):
     (DSV2LITE, 8, "markov:0.5", False, (2, 6), "dedup"),
     (DSV2LITE, 16, "markov:0.5", True, (0, 9, 15), "dedup"),
     (DSV3, 1, "iid", False, (0,), "dedup"),
+    (DSV3, 2, "iid", False, (0, 1), "dedup"),         # the two-token tile
+    (DSV3, 3, "markov:0.5", False, (0, 2), "dedup"),  # the four-token tile, one row short
     (DSV3, 4, "iid", False, (1, 3), "dedup"),
+    (DSV3, 6, "iid", False, (5,), "dedup"),
     (DSV3, 8, "iid", False, (0, 7), "dedup"),
     (DSV3, 8, "markov:0.5", False, (4,), "dedup"),
     (DSV3, 32, "markov:0.5", True, (0, 17, 31), "dedup"),
     (QWEN3, 8, "logits_ar1", False, (3,), "perslot"),
     (DSV2LITE, 16, "markov:0.5", True, (4, 12), "perslot"),
+    (DSV3, 2, "markov:0.5", False, (1,), "perslot"),
     (DSV3, 8, "iid", False, (2,), "perslot"),
     (DSV3, 32, "markov:0.5", True, (5, 26), "perslot"),
 ])
