@@ -262,45 +262,35 @@ def fits(points, ns, b_e, K, S):
 
 
 # ------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg, n_experts):
-    """The oracle as it stands on a bounded sample of the headline workload:
-    the passes n = 1 and n = 8 (independent routing, layer 0), each limited to
-    its first `n_experts` union experts with every slot routed to them (by
-    default the whole union: route, union, the deduplicating FFN of those
-    experts, combine; weight decode included, generation excluded).  Once on
-    one thread, once on every host core (the sample's experts split over a
-    thread pool, one oracle call each)."""
+def _oracle_pass(cfg, case, mode, threads, n_experts):
+    """One verify op of the oracle as it stands: route, union, the FFN of
+    `mode` (weight decode included), combine.  On several threads the FFN's
+    independent parts go to a pool, one oracle call each: a union expert
+    (dedup), a slot (per-slot), the shared experts of the pass (dedup) or of
+    a token (per-slot); the rows each call produced are copied into place.
+    The deduplicating pass may be capped at its first `n_experts` union
+    experts (every slot routed to them).  Returns (seconds, bytes read,
+    experts evaluated)."""
     from concurrent.futures import ThreadPoolExecutor
 
-    from threadpoolctl import threadpool_info, threadpool_limits
+    import numpy as np
 
     import oracle
-    from synth import make_case
 
-    cores = len(os.sched_getaffinity(0))
-    samples = []
-    for n in (1, 8):
-        case = make_case(cfg, n, "iid", seed=0, window=0, layer=0)
-        ids, _ = oracle.route_topk(case.logits, cfg.K)
-        un = oracle.build_union(ids, cfg.E)
+    t0 = time.perf_counter()
+    ids, gates = oracle.route_topk(case.logits, cfg.K)
+    un = oracle.build_union(ids, cfg.E)
+    n = ids.shape[0]
+    ffn = (cfg.w_dtype, cfg.x_dtype, cfg.d, cfg.f)
+    if mode == "dedup":
         m = min(int(un["U"]), n_experts)
-        # generate the weights before the clock starts (numpy releases the GIL)
-        gen = [int(e) for e in un["union_ids"][:m]] + [cfg.E + s for s in range(cfg.S)]
-        with ThreadPoolExecutor(cores) as ex:
-            list(ex.map(case.expert, gen))
-        samples.append((n, case, m, int(un["U"])))
+        evals = m + cfg.S
 
-    def run(case, m, threads):
-        t0 = time.perf_counter()
-        ids, gates = oracle.route_topk(case.logits, cfg.K)
-        un = oracle.build_union(ids, cfg.E)
-
-        def part(job):
-            u0, u1, S = job  # union experts [u0, u1) and the first S shared experts
+        def part(job):  # union experts [u0, u1) and the first S shared experts
+            u0, u1, S = job
             sub = {"U": u1 - u0, "union_ids": un["union_ids"][u0:u1],
                    "offsets": un["offsets"][u0:u1 + 1], "perm": un["perm"]}
-            return oracle.ffn_dedup(case.x, ids, sub, case.expert, case.shared, S,
-                                    cfg.w_dtype, cfg.x_dtype, cfg.d, cfg.f)
+            return oracle.ffn_dedup(case.x, ids, sub, case.expert, case.shared, S, *ffn)
 
         if threads == 1:
             y, ysh, read = part((0, m, cfg.S))
@@ -308,45 +298,137 @@ def cpu_baseline(cfg, n_experts):
             jobs = [(u, u + 1, 0) for u in range(m)] + [(0, 0, cfg.S)]
             with ThreadPoolExecutor(threads) as ex:
                 parts = list(ex.map(part, jobs))
-            y = sum(p[0] for p in parts)  # each part fills its own slots' rows
+            y = np.zeros((n, cfg.K, cfg.d))
+            for (u, _, _), (yp, _, _) in zip(jobs[:m], parts):
+                for sl in un["perm"][un["offsets"][u]:un["offsets"][u + 1]]:
+                    t, k = divmod(int(sl), cfg.K)
+                    y[t, k] = yp[t, k]
             ysh = parts[-1][1]
             read = sum(p[2] for p in parts)
-        oracle.combine(y, gates, ysh)
-        return time.perf_counter() - t0, read
+    else:
+        evals = n * (cfg.K + cfg.S)
+        if threads == 1:
+            y, ysh, read = oracle.ffn_perslot(case.x, ids, case.expert, case.shared, cfg.S, *ffn)
+        else:
+            def part(job):  # slot (t, k), or the shared experts of token t (k = -1)
+                t, k = job
+                if k >= 0:
+                    return oracle.ffn_perslot(case.x[t:t + 1], ids[t:t + 1, k:k + 1],
+                                              case.expert, case.shared, 0, *ffn)
+                return oracle.ffn_perslot(case.x[t:t + 1], ids[t:t + 1, :0], case.expert,
+                                          case.shared, cfg.S, *ffn)
 
+            jobs = [(t, k) for t in range(n) for k in range(cfg.K)] + \
+                [(t, -1) for t in range(n) if cfg.S]
+            with ThreadPoolExecutor(threads) as ex:
+                parts = list(ex.map(part, jobs))
+            y = np.zeros((n, cfg.K, cfg.d))
+            ysh = np.zeros((n, cfg.S, cfg.d))
+            for (t, k), (yp, yshp, _) in zip(jobs, parts):
+                if k >= 0:
+                    y[t, k] = yp[0, 0]
+                else:
+                    ysh[t] = yshp[0]
+            read = sum(p[2] for p in parts)
+    oracle.combine(y, gates, ysh if cfg.S else None)
+    return time.perf_counter() - t0, read, evals
+
+
+def _oracle_cases(cfg, ns, routing, cores):
+    """The sampled passes (layer 0, window 0, seed 0) with every weight they
+    read generated beforehand, outside the clock (numpy releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from synth import make_case
+
+    cases = []
+    for n in ns:
+        case = make_case(cfg, n, routing, seed=0, window=0, layer=0)
+        ids, _ = oracle.route_topk(case.logits, cfg.K)
+        un = oracle.build_union(ids, cfg.E)
+        gen = [int(e) for e in un["union_ids"]] + [cfg.E + s for s in range(cfg.S)]
+        with ThreadPoolExecutor(cores) as ex:
+            list(ex.map(case.expert, gen))
+        cases.append((n, case, int(un["U"])))
+    return cases
+
+
+def _oracle_leg(cfg, cases, mode, threads, n_experts):
+    tot_b, tot_t, per = 0, 0.0, {}
+    for n, case, _ in cases:
+        t, read, evals = _oracle_pass(cfg, case, mode, threads, n_experts)
+        tot_b += read
+        tot_t += t
+        per["n=%d" % n] = {"experts": evals, "us_op": round(t * 1e6, 1),
+                           "GBs": round(read / t / 1e9, 3)}
+    return {"value": round(tot_b / tot_t / 1e9, 3), "s": round(tot_t, 2), "per_n": per}
+
+
+def cpu_baseline(cfg, n_experts):
+    """The oracle as it stands, timed on the host cores on one thread and on
+    every core (BLAS one thread per call), with the core count:
+
+    - the headline value: the deduplicating op on a bounded sample of the
+      headline workload, the passes n = 1 and n = 8 (independent routing,
+      layer 0), each capped at its first `n_experts` union experts (by
+      default the whole union), GB/s on the union bytes read;
+    - `perslot`: the per-slot op on the same passes, GB/s on requested bytes;
+    - `olmoe`: the OLMoE-shaped bf16 layer at n = 1..8 (Markov p = 0.5), both
+      ops, µs per op and GB/s.
+    Weight generation is outside the clock; weight decode is inside."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from synth.configs import OLMOE
+
+    cores = len(os.sched_getaffinity(0))
+    head = _oracle_cases(cfg, (1, 8), "iid", cores)
+    olm = _oracle_cases(OLMOE, range(1, 9), "markov:0.5", cores)
     res = {}
-    for threads in (1, cores):
-        tot_b, tot_t, per = 0, 0.0, {}
-        with threadpool_limits(limits=1):
-            for n, case, m, _ in samples:
-                t, read = run(case, m, threads)
-                tot_b += read
-                tot_t += t
-                per["n=%d" % n] = {"experts": m, "s": round(t, 2),
-                                   "GBs_union": round(read / t / 1e9, 3)}
-        res[threads] = {"value": round(tot_b / tot_t / 1e9, 3), "s": round(tot_t, 2), "per_n": per}
-        log("cpu oracle, %d thread(s): %s" % (threads, json.dumps(res[threads])))
+    with threadpool_limits(limits=1):
+        for threads in (1, cores):
+            res[("dedup", threads)] = _oracle_leg(cfg, head, "dedup", threads, n_experts)
+            res[("perslot", threads)] = _oracle_leg(cfg, head, "perslot", threads, n_experts)
+            res[("olmoe dedup", threads)] = _oracle_leg(OLMOE, olm, "dedup", threads, 64)
+            res[("olmoe perslot", threads)] = _oracle_leg(OLMOE, olm, "perslot", threads, 64)
+    for (leg, threads), r in res.items():
+        log("cpu oracle, %s, %d thread(s): %s" % (leg, threads, json.dumps(r)))
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    whole = all(m == U for _, _, m, U in samples)
+    whole = all(min(U, n_experts) == U for _, _, U in head)
     scope = ("each pass whole (all %s union experts%s)"
-             % ("/".join(str(U) for _, _, _, U in samples),
+             % ("/".join(str(U) for _, _, U in head),
                 " + %d shared" % cfg.S if cfg.S else "") if whole else
              "each limited to its first %d union experts and every slot routed to them"
              % n_experts)
     sample = ("float64 numpy oracle (route, union, deduplicating FFN incl. fp8 weight decode, "
               "combine) on the %s layer, layer 0, independent routing, passes n=1 and n=8, %s; "
-              "GB/s on the union bytes of the sampled experts" % (cfg.name, scope))
-    return {"value": res[cores]["value"], "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "cpu": model, "blas": ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()})),
-            "sample": sample + "; %d threads (one oracle "
-            "call per sampled expert), BLAS one thread each" % cores,
-            "per_n": res[cores]["per_n"],
-            "single_thread": {"value": res[1]["value"], "cores": 1, "per_n": res[1]["per_n"]}}
+              "GB/s on the union bytes read; %d threads (one oracle call per union expert), "
+              "BLAS one thread each" % (cfg.name, scope, cores))
+
+    def both(leg):
+        return {"value": res[(leg, cores)]["value"], "cores": cores,
+                "per_n": res[(leg, cores)]["per_n"],
+                "single_thread": {"value": res[(leg, 1)]["value"], "cores": 1,
+                                  "per_n": res[(leg, 1)]["per_n"]}}
+
+    out = {"value": res[("dedup", cores)]["value"], "unit": "GB/s", "cores": cores,
+           "kind": "oracle", "cpu": model,
+           "blas": ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()})),
+           "sample": sample, "per_n": res[("dedup", cores)]["per_n"],
+           "single_thread": {"value": res[("dedup", 1)]["value"], "cores": 1,
+                             "per_n": res[("dedup", 1)]["per_n"]},
+           "perslot": dict(both("perslot"), unit="GB/s on requested bytes",
+                           sample="the same passes, per-slot op (one oracle call per slot)"),
+           "olmoe": {"workload": "OLMoE-shaped bf16 layer, Markov p=0.5, layer 0, n=1..8",
+                     "dedup": both("olmoe dedup"), "perslot": both("olmoe perslot")},
+           "cpu_seconds": round(sum(r["s"] * (1 if th == 1 else cores)
+                                    for (_, th), r in res.items()), 1)}
+    return out
 
 
 # ------------------------------------------------------------ other shapes
