@@ -19,6 +19,11 @@
     python -m moe_speculative_decoding_amd.profiling valu PMC_DIR MANIFEST
         VALUBusy, VALU and MFMA instruction counts per pass from a `--pmc` run of
         `bench.py --counters MANIFEST`.
+
+    python -m moe_speculative_decoding_amd.profiling counters PMC_DIR MANIFEST NAME [NAME ...]
+        the mean of each named counter per pass (mode, routing, n) from a `--pmc`
+        run of `bench.py --counters MANIFEST` (values as rocprofv3 reports them,
+        summed over the counter's instances).
 """
 from __future__ import annotations
 
@@ -124,11 +129,10 @@ def traffic(fetch_dir: str, write_dir: str, manifest_path: str) -> dict:
     return out
 
 
-def valu(d: str, manifest_path: str) -> dict:
-    """VALU activity per one-launch pass from a `--pmc VALUBusy SQ_INSTS_VALU
-    SQ_INSTS_MFMA` run of `bench.py --counters` (VALUBusy: the share of the
-    kernel's GPU time in which vector ALU instructions are processed, the
-    vendor's derived counter)."""
+def counter_means(d: str, manifest_path: str, names) -> dict:
+    """Mean per pass (mode, routing, n) of each named counter, from a `--pmc`
+    run of `bench.py --counters`: the manifest's launches are the run's last
+    dispatches of its kernel, in order."""
     with open(manifest_path) as fh:
         man = json.load(fh)
     kname = man.get("kernel", "layer_kernel")
@@ -139,14 +143,22 @@ def valu(d: str, manifest_path: str) -> dict:
         k = int(r["Dispatch_Id"])
         vals.setdefault(k, defaultdict(float))[r["Counter_Name"]] += float(r["Counter_Value"])
     ids = sorted(vals)[-len(man["launches"]):]
+    if len(ids) < len(man["launches"]):
+        raise ValueError("expected %d %s dispatches, found %d"
+                         % (len(man["launches"]), kname, len(ids)))
     groups = defaultdict(list)
     for k, l in zip(ids, man["launches"]):
         groups["%s %s n=%d" % (l["mode"], l["routing"], l["n"])].append(vals[k])
-    out = {}
-    for key, vs in groups.items():
-        out[key] = {c: sum(v.get(c, 0.0) for v in vs) / len(vs)
-                    for c in ("VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_MFMA")}
-    return out
+    return {key: {c: sum(v.get(c, 0.0) for v in vs) / len(vs) for c in names}
+            for key, vs in groups.items()}
+
+
+def valu(d: str, manifest_path: str) -> dict:
+    """VALU activity per one-launch pass from a `--pmc VALUBusy SQ_INSTS_VALU
+    SQ_INSTS_MFMA` run of `bench.py --counters` (VALUBusy: the share of the
+    kernel's GPU time in which vector ALU instructions are processed, the
+    vendor's derived counter)."""
+    return counter_means(d, manifest_path, ("VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"))
 
 
 def step_stats(trace_dir: str, manifest_path: str) -> dict:
@@ -212,6 +224,8 @@ def main(argv):
             with open(argv[5], "w") as fh:
                 json.dump(rec, fh, indent=1)
         print(json.dumps(rec, indent=1))
+    elif len(argv) >= 4 and argv[0] == "counters":
+        print(json.dumps(counter_means(argv[1], argv[2], argv[3:]), indent=1))
     elif len(argv) >= 2 and argv[0] == "stats":
         print(stats(argv[1]))
     else:
