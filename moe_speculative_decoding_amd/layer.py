@@ -1,7 +1,10 @@
 """Device buffers of one MoE layer and the chain of entry points of one verify pass.
 
 Only allocation (torch, on the GPU) and calls through the C ABI happen here;
-every step of the pass runs in the HIP library.
+every step of the pass runs in the HIP library.  The calls are asynchronous:
+an argument error raises at once, but what the device detects (expert ids out
+of range, a hand-over wait that gave up) lands in the workspace's error word,
+which `_lib.moe_get_error(buf.ws)` reads after synchronising.
 """
 from __future__ import annotations
 
